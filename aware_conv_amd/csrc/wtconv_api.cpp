@@ -1,0 +1,170 @@
+// C-ABI front end of the fused WTConv library: argument checks (all of them
+// before anything is enqueued), workspace sizing, dispatch to the kernels.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "wtconv.h"
+#include "wtconv_internal.h"
+
+namespace {
+
+using wtc::Grads;
+using wtc::Params;
+
+size_t elem_size(int dtype) { return dtype == WTCONV_F32 ? 4 : 2; }
+
+int check_shape(const wtconv_shape* s) {
+    if (!s) return WTCONV_ERR_NULL;
+    if (s->B < 0 || s->C < 0 || s->H < 0 || s->W < 0) return WTCONV_ERR_SHAPE;
+    if (s->L < 1 || s->L > WTCONV_MAX_LEVELS) return WTCONV_ERR_LEVELS;
+    if (s->k < 1 || s->k > 7 || (s->k % 2) == 0) return WTCONV_ERR_KERNEL;
+    if (s->dtype != WTCONV_F32 && s->dtype != WTCONV_F16) return WTCONV_ERR_DTYPE;
+    const int m = 1 << s->L;
+    if ((s->H % m) != 0 || (s->W % m) != 0) return WTCONV_ERR_SHAPE;
+    // element counts must fit the kernels' 64-bit offsets and 32-bit grids
+    const unsigned long long n = (unsigned long long)s->B * (unsigned long long)s->C *
+                                 (unsigned long long)s->H * (unsigned long long)s->W;
+    if (s->H > 0 && s->W > 0 && n / ((unsigned long long)s->H * s->W) !=
+                                    (unsigned long long)s->B * s->C)
+        return WTCONV_ERR_SHAPE;
+    if (n > (1ULL << 40)) return WTCONV_ERR_SHAPE;
+    return WTCONV_OK;
+}
+
+bool empty_planes(const wtconv_shape* s) { return s->H == 0 || s->W == 0; }
+bool empty_act(const wtconv_shape* s) { return s->B == 0 || s->C == 0 || empty_planes(s); }
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+size_t act_bytes(const wtconv_shape* s) {
+    return (size_t)s->B * s->C * s->H * s->W * elem_size(s->dtype);
+}
+
+bool overlap(const void* a, const void* b, size_t n) {
+    const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+    return n > 0 && x < y + n && y < x + n;
+}
+
+int check_params(const wtconv_shape* s, const void* w_base, const void* b_base,
+                 const void* s_base, const void* w_wav, const void* s_wav) {
+    if (s->C == 0) return WTCONV_OK;
+    if (!w_base || !s_base || !w_wav || !s_wav) return WTCONV_ERR_NULL;
+    if (b_base == nullptr) return WTCONV_ERR_NULL;
+    const size_t e = elem_size(s->dtype);
+    if (!aligned(w_base, e) || !aligned(b_base, e) || !aligned(s_base, e) ||
+        !aligned(w_wav, e) || !aligned(s_wav, e))
+        return WTCONV_ERR_ALIGN;
+    return WTCONV_OK;
+}
+
+// The one kernel family of this build: whole planes staged in LDS.
+int check_supported(const wtconv_shape* s) {
+    if (empty_act(s)) return WTCONV_OK;
+    return wtc::plane_supported(*s) ? WTCONV_OK : WTCONV_ERR_UNSUPPORTED;
+}
+
+size_t workspace_bytes(const wtconv_shape* s) {
+    if (empty_act(s)) return 0;
+    return wtc::plane_workspace_bytes(*s);
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? WTCONV_OK : WTCONV_ERR_HIP; }
+
+// Shared by the forward and the input gradient (flip = true).
+int apply(const wtconv_shape* s, const void* in, const void* w_base, const void* b_base,
+          const void* s_base, const void* w_wav, const void* s_wav, void* out,
+          void* workspace, size_t ws_bytes, void* stream, bool flip) {
+    int rc = check_shape(s);
+    if (rc) return rc;
+    rc = check_params(s, w_base, b_base, s_base, w_wav, s_wav);
+    if (rc) return rc;
+    if (empty_act(s)) return WTCONV_OK;
+    if (!in || !out) return WTCONV_ERR_NULL;
+    if (!aligned(in, 16) || !aligned(out, 16)) return WTCONV_ERR_ALIGN;
+    if (overlap(in, out, act_bytes(s))) return WTCONV_ERR_ALIAS;
+    rc = check_supported(s);
+    if (rc) return rc;
+    (void)workspace;  // the forward and the input gradient need no workspace
+    (void)ws_bytes;
+    Params p{w_base, b_base, s_base, w_wav, s_wav};
+    return hip_status(wtc::plane_apply(*s, in, p, out, flip, static_cast<hipStream_t>(stream)));
+}
+
+}  // namespace
+
+extern "C" {
+
+int wtconv_workspace_size(const wtconv_shape* s, size_t* bytes) {
+    int rc = check_shape(s);
+    if (rc) return rc;
+    if (!bytes) return WTCONV_ERR_NULL;
+    rc = check_supported(s);
+    if (rc) return rc;
+    *bytes = workspace_bytes(s);
+    return WTCONV_OK;
+}
+
+int wtconv_fwd(const wtconv_shape* s, const void* x, const void* w_base, const void* b_base,
+               const void* s_base, const void* w_wav, const void* s_wav, void* y,
+               void* workspace, size_t ws_bytes, void* stream) {
+    return apply(s, x, w_base, b_base, s_base, w_wav, s_wav, y, workspace, ws_bytes, stream,
+                 false);
+}
+
+int wtconv_bwd_input(const wtconv_shape* s, const void* dy, const void* w_base,
+                     const void* s_base, const void* w_wav, const void* s_wav, void* dx,
+                     void* workspace, size_t ws_bytes, void* stream) {
+    // the input gradient has no bias term; pass a non-null stand-in that is
+    // never read so the shared checks apply unchanged
+    return apply(s, dy, w_base, w_base, s_base, w_wav, s_wav, dx, workspace, ws_bytes, stream,
+                 true);
+}
+
+int wtconv_bwd_weight(const wtconv_shape* s, const void* x, const void* dy, const void* w_base,
+                      const void* b_base, const void* s_base, const void* w_wav,
+                      const void* s_wav, void* dw_base, void* db_base, void* ds_base,
+                      void* dw_wav, void* ds_wav, void* workspace, size_t ws_bytes,
+                      void* stream) {
+    int rc = check_shape(s);
+    if (rc) return rc;
+    rc = check_params(s, w_base, b_base, s_base, w_wav, s_wav);
+    if (rc) return rc;
+    if (s->C == 0) return WTCONV_OK;
+    if (!dw_base || !db_base || !ds_base || !dw_wav || !ds_wav) return WTCONV_ERR_NULL;
+    const size_t e = elem_size(s->dtype);
+    if (!aligned(dw_base, e) || !aligned(db_base, e) || !aligned(ds_base, e) ||
+        !aligned(dw_wav, e) || !aligned(ds_wav, e))
+        return WTCONV_ERR_ALIGN;
+    Params p{w_base, b_base, s_base, w_wav, s_wav};
+    Grads g{dw_base, db_base, ds_base, dw_wav, ds_wav};
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (empty_act(s)) return hip_status(wtc::zero_grads(*s, p, g, st));
+    if (!x || !dy) return WTCONV_ERR_NULL;
+    if (!aligned(x, 16) || !aligned(dy, 16)) return WTCONV_ERR_ALIGN;
+    rc = check_supported(s);
+    if (rc) return rc;
+    const size_t need = workspace_bytes(s);
+    if (ws_bytes < need) return WTCONV_ERR_WORKSPACE;
+    if (need > 0 && !workspace) return WTCONV_ERR_NULL;
+    if (need > 0 && !aligned(workspace, 16)) return WTCONV_ERR_ALIGN;
+    return hip_status(wtc::plane_bwd_weight(*s, x, dy, p, g, workspace, st));
+}
+
+const char* wtconv_strerror(int code) {
+    switch (code) {
+        case WTCONV_OK: return "ok";
+        case WTCONV_ERR_NULL: return "a required pointer is NULL";
+        case WTCONV_ERR_SHAPE: return "invalid shape (negative dimension, H or W not a multiple of 2^L, or too large)";
+        case WTCONV_ERR_KERNEL: return "kernel size must be odd and between 1 and 7";
+        case WTCONV_ERR_LEVELS: return "levels must be between 1 and WTCONV_MAX_LEVELS";
+        case WTCONV_ERR_DTYPE: return "unknown dtype";
+        case WTCONV_ERR_ALIGN: return "misaligned pointer (activations and workspace need 16 bytes)";
+        case WTCONV_ERR_WORKSPACE: return "workspace smaller than wtconv_workspace_size()";
+        case WTCONV_ERR_UNSUPPORTED: return "no kernel for this shape in this build";
+        case WTCONV_ERR_ALIAS: return "an output overlaps an input";
+        case WTCONV_ERR_HIP: return "a HIP kernel launch failed";
+        default: return "unknown error code";
+    }
+}
+
+}  // extern "C"

@@ -1,0 +1,46 @@
+// Internal interface between the C-ABI front end (wtconv_api.cpp) and the
+// kernel translation units.  Not installed; not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+
+#include "wtconv.h"
+
+namespace wtc {
+
+// Raw (unfolded) parameter pointers, all in the layer's storage dtype.
+struct Params {
+    const void* w_base;  // [C][k][k]
+    const void* b_base;  // [C]   (may be NULL for the input gradient)
+    const void* s_base;  // [C]
+    const void* w_wav;   // [L][C][4][k][k]
+    const void* s_wav;   // [L][C][4]
+};
+
+struct Grads {
+    void* dw_base;
+    void* db_base;
+    void* ds_base;
+    void* dw_wav;
+    void* ds_wav;
+};
+
+// Whole-plane path: every (b, c) plane is staged in LDS in one piece.
+// Returns true if this build holds kernels for the shape.
+bool plane_supported(const wtconv_shape& s);
+// Workspace bytes the whole-plane weight-gradient kernels need.
+size_t plane_workspace_bytes(const wtconv_shape& s);
+// flip = false: forward (y = op(x)); flip = true: input gradient
+// (dx = op^T(dy): 180-degree rotated kernels, no bias).
+hipError_t plane_apply(const wtconv_shape& s, const void* in,
+                       const Params& p, void* out, bool flip,
+                       hipStream_t stream);
+hipError_t plane_bwd_weight(const wtconv_shape& s, const void* x,
+                            const void* dy, const Params& p, const Grads& g,
+                            void* workspace, hipStream_t stream);
+// Zero parameter gradients (empty batch or empty planes).
+hipError_t zero_grads(const wtconv_shape& s, const Params& p, const Grads& g,
+                      hipStream_t stream);
+
+}  // namespace wtc

@@ -1,0 +1,118 @@
+"""The C-ABI library loads, exports every declared entry point, and rejects
+bad arguments with the documented codes before any device call.
+
+Runs on the CPU: every call here fails validation, which happens before the
+library touches HIP, so no GPU is needed.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def lb():
+    from aware_conv_amd import _lib
+    return _lib
+
+
+def declared_functions():
+    src = open(os.path.join(ROOT, "include", "wtconv.h")).read()
+    return sorted(set(re.findall(r"^\s*(?:int|const char\*)\s+(wtconv_\w+)\s*\(", src, re.M)))
+
+
+def test_exports_every_declared_symbol(lb):
+    names = declared_functions()
+    assert set(names) == set(lb.EXPORTED)
+    for n in names:
+        assert getattr(lb.lib, n) is not None  # dlsym succeeds
+
+
+def test_header_error_codes_match_binding(lb):
+    src = open(os.path.join(ROOT, "include", "wtconv.h")).read()
+    codes = dict((n, int(v)) for n, v in re.findall(r"#define (WTCONV_\w+) \((-?\d+)\)", src))
+    assert codes["WTCONV_ERR_UNSUPPORTED"] == -8
+    for n, v in codes.items():
+        assert lb.wtconv_strerror(v) not in ("", "unknown error code"), n
+    assert lb.wtconv_strerror(12345) == "unknown error code"
+
+
+FAKE = ctypes.c_void_p(0x100000)      # 16-byte aligned, never dereferenced
+FAKE2 = ctypes.c_void_p(0x200000)
+MIS = ctypes.c_void_p(0x100004)        # 4-byte aligned only
+
+
+# Every call below must fail validation: a call that passed would enqueue a
+# kernel on fake pointers.
+def fwd(lb, shape, x=FAKE, y=FAKE2, params=FAKE, ws=None, nws=0):
+    return lb.lib.wtconv_fwd(ctypes.byref(shape) if shape is not None else None,
+                            x, params, params, params, params, params, y, ws, nws, None)
+
+
+def good(lb, **kw):
+    d = dict(B=2, C=8, H=56, W=56, L=2, k=5, dtype=lb.WTCONV_F32)
+    d.update(kw)
+    return lb.Shape(d["B"], d["C"], d["H"], d["W"], d["L"], d["k"], d["dtype"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(B=-1), -2), (dict(H=-56), -2), (dict(H=54), -2), (dict(W=58), -2),
+    (dict(L=0), -4), (dict(L=7), -4), (dict(k=4), -3), (dict(k=9), -3), (dict(k=0), -3),
+    (dict(dtype=2), -5),
+])
+def test_shape_errors(lb, kw, code):
+    assert fwd(lb, good(lb, **kw)) == code
+
+
+def test_null_and_alignment_errors(lb):
+    s = good(lb)
+    assert fwd(lb, None) == -1
+    assert fwd(lb, s, x=None) == -1
+    assert fwd(lb, s, params=None) == -1
+    assert fwd(lb, s, x=MIS) == -6
+    assert fwd(lb, s, y=MIS) == -6
+    assert fwd(lb, s, params=ctypes.c_void_p(0x100001)) == -6
+    assert fwd(lb, s, y=FAKE) == -9  # y aliases x
+
+
+def test_bwd_input_checks(lb):
+    s = good(lb)
+    f = lb.lib.wtconv_bwd_input
+    assert f(ctypes.byref(s), None, FAKE, FAKE, FAKE, FAKE, FAKE2, None, 0, None) == -1
+    assert f(ctypes.byref(s), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, 0, None) == -9
+    assert f(ctypes.byref(good(lb, k=2)), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE2, None, 0, None) == -3
+
+
+def test_bwd_weight_workspace_checks(lb):
+    s = good(lb)
+    need = lb.wtconv_workspace_size(s)
+    assert need > 0
+    f = lb.lib.wtconv_bwd_weight
+    args = [ctypes.byref(s), FAKE, FAKE2] + [FAKE] * 5 + [FAKE2] * 5
+    assert f(*args, FAKE, need - 1, None) == -7
+    assert f(*args, None, need, None) == -1
+    assert f(*args, MIS, need, None) == -6
+    bad = [ctypes.byref(s), FAKE, FAKE2] + [FAKE] * 5 + [FAKE2] * 4 + [None]
+    assert f(*bad, FAKE, need, None) == -1
+
+
+def test_workspace_size_queries(lb):
+    n = ctypes.c_size_t(7)
+    assert lb.lib.wtconv_workspace_size(ctypes.byref(good(lb, H=48, W=48)), ctypes.byref(n)) == -8
+    assert n.value == 7  # untouched on error
+    assert lb.lib.wtconv_workspace_size(ctypes.byref(good(lb)), None) == -1
+    assert lb.wtconv_workspace_size(good(lb, B=0)) == 0
+    # grows with the batch, fixed per shape
+    assert lb.wtconv_workspace_size(good(lb, B=64)) >= lb.wtconv_workspace_size(good(lb, B=2))
+    assert lb.wtconv_workspace_size(good(lb, B=64)) == lb.wtconv_workspace_size(good(lb, B=64))
+
+
+def test_empty_tensors_need_no_pointers(lb):
+    # B = 0: nothing to compute, nothing dereferenced, no launch
+    s = good(lb, B=0)
+    assert fwd(lb, s, x=None, y=None) == 0
+    s = good(lb, C=0)
+    assert fwd(lb, s, x=None, y=None, params=None) == 0

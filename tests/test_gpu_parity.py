@@ -1,0 +1,177 @@
+"""HIP path against the fp64 oracle, element by element, through the C ABI.
+
+Error metric per output tensor: max_i |gpu_i - oracle_i| / max_i |oracle_i|
+(an absolute bound where the oracle is identically zero).  Bars: 1e-5 for
+fp32, 2e-2 for fp16 storage with fp32 accumulation.  For fp16 the oracle gets
+the same fp16-rounded inputs, upcast to fp64.
+
+The named workloads are run at their full sizes, in the launch configuration
+the benchmark uses, and compared with the oracle on every element.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import wtconv_inputs as wi
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"f32": 1e-5, "f16": 2e-2}
+NAMES = ("y", "dx", "dw_base", "db_base", "ds_base", "dw_wav", "ds_wav")
+
+
+def lib():
+    from aware_conv_amd import _lib
+    return _lib
+
+
+def gpu_run(d, dev="cuda"):
+    L = lib()
+    t = {k: v.to(dev) for k, v in d.items()}
+    y = L.wtconv_fwd(t["x"], t["w_base"], t["b_base"], t["s_base"], t["w_wav"], t["s_wav"])
+    dx = L.wtconv_bwd_input(t["dy"], t["w_base"], t["s_base"], t["w_wav"], t["s_wav"])
+    g = L.wtconv_bwd_weight(t["x"], t["dy"], t["w_base"], t["b_base"], t["s_base"],
+                            t["w_wav"], t["s_wav"])
+    torch.cuda.synchronize()
+    out = {"y": y, "dx": dx}
+    out.update(g)
+    return {k: v.double().cpu().numpy() for k, v in out.items()}
+
+
+def oracle_run(d):
+    a = {k: v.double().numpy() for k, v in d.items()}
+    p = [a[n] for n in ("w_base", "b_base", "s_base", "w_wav", "s_wav")]
+    out = {"y": oracle.fwd(a["x"], *p)}
+    g = oracle.bwd(a["x"], a["dy"], *p)
+    out.update(g)
+    return out
+
+
+def rel_err(g, o):
+    g = g.reshape(o.shape)
+    m = np.abs(o).max() if o.size else 0.0
+    e = np.abs(g - o).max() if o.size else 0.0
+    return e / m if m > 0 else e
+
+
+def assert_parity(d, dtype, label, names=NAMES):
+    g = gpu_run(d)
+    o = oracle_run(d)
+    errs = {n: rel_err(g[n], o[n]) for n in names}
+    print("\n%s: %s" % (label, " ".join("%s=%.2e" % kv for kv in errs.items())), flush=True)
+    for n in names:
+        assert np.all(np.isfinite(g[n])), (label, n)
+        assert errs[n] <= TOL[dtype], (label, n, errs[n])
+
+
+@pytest.mark.parametrize("name", ["tiny", "stage1", "stage2", "stage3", "stage1_f16"])
+def test_named_workload_full_size(name):
+    wl = wi.WORKLOADS[name]
+    print("\ncase %s %s" % (name, wl), flush=True)
+    assert_parity(wi.workload_inputs(wl), wl.dtype, name)
+
+
+@pytest.mark.parametrize("name", ["stage1", "stage1_f16"])
+def test_wavelet_path_alone(name):
+    """beta = 0 leaves only the wavelet path, so its (small) contribution is
+    checked at full tolerance instead of hiding under the base conv."""
+    wl = wi.WORKLOADS[name]
+    d = wi.make_inputs(8, wl.C, wl.H, wl.W, wl.L, wl.k, wl.dtype, seed=3, s_base=0.0)
+    assert_parity(d, wl.dtype, name + "-wavelet-only", names=("y", "dx", "dw_wav", "ds_wav", "ds_base"))
+
+
+SMALL = [  # k, L, H, W: every small variant the library carries
+    (1, 1, 8, 8), (3, 1, 8, 8), (3, 2, 16, 16), (3, 3, 16, 16), (5, 3, 16, 16),
+    (7, 2, 16, 16), (7, 1, 14, 14), (3, 2, 16, 32), (5, 4, 32, 32), (3, 5, 32, 32),
+    (5, 6, 64, 64), (5, 2, 32, 32), (5, 2, 28, 28), (5, 1, 14, 14), (5, 2, 56, 56),
+]
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f16"])
+@pytest.mark.parametrize("k,L,H,W", SMALL)
+def test_small_shapes_ragged_batch(k, L, H, W, dtype):
+    """Ragged batch (not a multiple of the planes per workgroup), odd channel
+    count and per-channel random scales, so every index of the fold and of
+    the gradient reduction is exercised."""
+    B, C = 3, 5
+    d = wi.make_inputs(B, C, H, W, L, k, dtype, seed=k * 100 + L * 10 + H)
+    g = torch.Generator().manual_seed(7)
+    td = d["x"].dtype
+    d["s_base"] = (1 + 0.5 * torch.randn(C, generator=g)).to(td)
+    d["s_wav"] = (0.1 + 0.5 * torch.randn(L, C, 4, generator=g)).to(td)
+    d["b_base"] = (0.5 * torch.randn(C, generator=g)).to(td)
+    assert_parity(d, dtype, "k%d L%d %dx%d %s" % (k, L, H, W, dtype))
+
+
+def test_single_image_single_channel():
+    d = wi.make_inputs(1, 1, 56, 56, 2, 5, "f32", seed=5)
+    assert_parity(d, "f32", "B1C1")
+
+
+def test_outputs_fully_written_and_deterministic():
+    """NaN-poisoned outputs are fully overwritten, and repeated calls give
+    the same bits (fixed reduction order, no float atomics)."""
+    L = lib()
+    d = {k: v.cuda() for k, v in wi.make_inputs(5, 7, 28, 28, 2, 5, "f32", seed=9).items()}
+    p = [d[n] for n in ("w_base", "b_base", "s_base", "w_wav", "s_wav")]
+    y = torch.full_like(d["x"], float("nan"))
+    L.wtconv_fwd(d["x"], *p, y=y)
+    dx = torch.full_like(d["x"], float("nan"))
+    L.wtconv_bwd_input(d["dy"], p[0], p[2], p[3], p[4], dx=dx)
+    gr = {n: torch.full_like(t, float("nan")) for n, t in
+          zip(L.GRAD_NAMES, (p[0], p[1], p[2], p[3], p[4]))}
+    L.wtconv_bwd_weight(d["x"], d["dy"], *p, grads=gr)
+    torch.cuda.synchronize()
+    for t in [y, dx] + list(gr.values()):
+        assert torch.isfinite(t).all()
+    y2 = L.wtconv_fwd(d["x"], *p)
+    g2 = L.wtconv_bwd_weight(d["x"], d["dy"], *p)
+    torch.cuda.synchronize()
+    assert torch.equal(y, y2)
+    for n in L.GRAD_NAMES:
+        assert torch.equal(gr[n], g2[n])
+
+
+def test_input_gradient_is_rotated_forward():
+    """On the GPU too: bwd_input(dy) == fwd(dy) with 180-degree rotated
+    kernels and zero bias."""
+    L = lib()
+    d = {k: v.cuda() for k, v in wi.make_inputs(4, 6, 56, 56, 2, 5, "f32", seed=2).items()}
+    dx = L.wtconv_bwd_input(d["dy"], d["w_base"], d["s_base"], d["w_wav"], d["s_wav"])
+    y = L.wtconv_fwd(d["dy"], d["w_base"].flip(-1, -2).contiguous(), torch.zeros_like(d["b_base"]),
+                     d["s_base"], d["w_wav"].flip(-1, -2).contiguous(), d["s_wav"])
+    torch.cuda.synchronize()
+    assert (dx - y).abs().max().item() <= 1e-6 * y.abs().max().item()
+
+
+def test_empty_batch():
+    L = lib()
+    d = {k: v.cuda() for k, v in wi.make_inputs(0, 4, 16, 16, 2, 3, "f32").items()}
+    p = [d[n] for n in ("w_base", "b_base", "s_base", "w_wav", "s_wav")]
+    y = L.wtconv_fwd(d["x"], *p)
+    g = {n: torch.full_like(t, 3.0) for n, t in zip(L.GRAD_NAMES, p)}
+    L.wtconv_bwd_weight(d["x"], d["dy"], *p, grads=g)
+    torch.cuda.synchronize()
+    assert y.shape == d["x"].shape
+    for n in L.GRAD_NAMES:
+        assert torch.count_nonzero(g[n]) == 0
+
+
+def test_autograd_module_matches_oracle():
+    from aware_conv_amd import WTConv2d
+    torch.manual_seed(0)
+    m = WTConv2d(8, kernel_size=5, levels=2).cuda()
+    x = torch.randn(2, 8, 32, 32, device="cuda", requires_grad=True)
+    dy = torch.randn(2, 8, 32, 32, device="cuda")
+    y = m(x)
+    y.backward(dy)
+    torch.cuda.synchronize()
+    p = [getattr(m, n).detach().double().cpu().numpy() for n in ("w_base", "b_base", "s_base", "w_wav", "s_wav")]
+    xo = x.detach().double().cpu().numpy()
+    yo = oracle.fwd(xo, *p)
+    go = oracle.bwd(xo, dy.double().cpu().numpy(), *p)
+    assert rel_err(y.detach().double().cpu().numpy(), yo) < 1e-5
+    assert rel_err(x.grad.double().cpu().numpy(), go["dx"]) < 1e-5
+    assert rel_err(m.w_wav.grad.double().cpu().numpy(), go["dw_wav"]) < 1e-5
+    assert rel_err(m.s_base.grad.double().cpu().numpy(), go["ds_base"]) < 1e-5
