@@ -1,0 +1,217 @@
+"""Throughput of the fused WTConv training step on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload stage1]
+
+A step is one pass of the whole hot path over one batch: wtconv_fwd,
+wtconv_bwd_input and wtconv_bwd_weight on synthetic inputs already resident in
+device memory.  W untimed steps, then exactly K timed steps bracketed by
+device synchronisation; value = images per second over the K steps.  Each
+step reads its own set of buffers, rotating over enough sets that no step
+finds the previous step's tensors in the 256 MB last-level cache.
+
+Also reported, on the same JSON line:
+  roofline     the dominant kernel (longest average launch, timed live with
+               HIP events on the stream it is launched on) against the
+               roof that bounds it: algorithmic FLOPs over the fp32 vector
+               peak without packed FP32 (the kernels are built with packed
+               FP32 selection off), with its HBM bandwidth fraction alongside;
+               traffic = HBM bytes per launch from the committed rocprofv3
+               counter summary when it was taken on the current kernel source,
+               else null
+  cpu_baseline the fp64 oracle (test infrastructure, timed as it stands) on
+               the host cores, on the same workload, about ten seconds of work
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_FP32_VALU_TFLOPS = 78.6    # 256 CU * 4 SIMD * 16 lanes * 2 FLOP * 2.4 GHz, no packed FP32
+PEAK_FP32_PACKED_TFLOPS = 157.3  # the same with packed FP32 (not used by these kernels)
+PEAK_HBM_GBS = 8000.0
+KERNEL_SOURCE = os.path.join(ROOT, "aware_conv_amd", "csrc", "wtconv_plane.hip")
+TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "traffic_{workload}.json")
+
+
+def conv_flops_per_pixel(L, k):
+    """Algorithmic FLOPs per input pixel of one pass: 2 k^2 for the base conv
+    plus 4 subbands of 2 k^2 on a grid 4^l times smaller at each level l."""
+    return 2.0 * k * k * (1.0 + sum(4.0 * 4.0 ** (-l) for l in range(1, L + 1)))
+
+
+def io_model_reference(L):
+    """Elements moved through device memory per input element by the unfused
+    reference forward: 7 for the base path and the final add, 10.75 per level
+    on a grid 4^(l-1) times smaller (see the design doc for the op-by-op count)."""
+    return 7.0 + 10.75 * sum(4.0 ** (-j) for j in range(L))
+
+
+def source_hash():
+    with open(KERNEL_SOURCE, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def cpu_baseline(wl, min_seconds=10.0):
+    import numpy as np
+
+    import oracle
+    import wtconv_inputs as wi
+    d = wi.workload_inputs(wl)
+    a = {k: v.double().numpy() for k, v in d.items()}
+    p = [a[n] for n in ("w_base", "b_base", "s_base", "w_wav", "s_wav")]
+    # bounded sample: whole batches until min_seconds of work, at least one
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        oracle.fwd(a["x"], *p)
+        oracle.bwd(a["x"], a["dy"], *p)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= min_seconds:
+            break
+    del np
+    return {"value": round(reps * wl.B / el, 3), "unit": "images/s", "cores": oracle.num_threads(),
+            "kind": "oracle",
+            "sample": "%d full %s batch(es) of %d images (fwd + bwd), fp64, %.1f s" % (reps, wl.name, wl.B, el)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="stage1")
+    ap.add_argument("--sets", type=int, default=0, help="buffer sets to rotate (0 = auto)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="also run a plain device copy of the step's input size "
+                         "(calibrates rocprofv3 byte counters)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path "
+              "(--gpus %d requested)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import wtconv_inputs as wi
+    from aware_conv_amd import _lib as L
+
+    wl = wi.WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    esz = 4 if wl.dtype == "f32" else 2
+    act_bytes = wl.N * esz
+    nsets = args.sets or max(1, min(8, int((1.2e9 + 4 * act_bytes - 1) // (4 * act_bytes))))
+    host = wi.workload_inputs(wl)
+    sets = []
+    for i in range(nsets):
+        t = {k: v.to(dev) for k, v in host.items()}
+        if i:
+            t["x"] = t["x"].roll(i, dims=0).contiguous()
+            t["dy"] = t["dy"].roll(i, dims=0).contiguous()
+        t["y"] = torch.empty_like(t["x"])
+        t["dx"] = torch.empty_like(t["x"])
+        t["g"] = {n: torch.empty_like(t[s]) for n, s in
+                  zip(L.GRAD_NAMES, ("w_base", "b_base", "s_base", "w_wav", "s_wav"))}
+        sets.append(t)
+    shape = L.shape_of(sets[0]["x"], sets[0]["w_wav"])
+    ws = torch.empty(max(16, L.wtconv_workspace_size(shape)), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step(t, ev=None):
+        p = (t["w_base"], t["b_base"], t["s_base"], t["w_wav"], t["s_wav"])
+        if ev is not None:
+            ev[0].record(stream)
+        L.wtconv_fwd(t["x"], *p, y=t["y"], workspace=ws, stream=stream)
+        if ev is not None:
+            ev[1].record(stream)
+        L.wtconv_bwd_input(t["dy"], p[0], p[2], p[3], p[4], dx=t["dx"], workspace=ws, stream=stream)
+        if ev is not None:
+            ev[2].record(stream)
+        L.wtconv_bwd_weight(t["x"], t["dy"], *p, grads=t["g"], workspace=ws, stream=stream)
+        if ev is not None:
+            ev[3].record(stream)
+
+    for i in range(args.warmup):
+        step(sets[i % nsets])
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(sets[i % nsets], evs[i])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    per = {"wtconv_fwd": [], "wtconv_bwd_input": [], "wtconv_bwd_weight": []}
+    for e in evs:
+        per["wtconv_fwd"].append(e[0].elapsed_time(e[1]))
+        per["wtconv_bwd_input"].append(e[1].elapsed_time(e[2]))
+        per["wtconv_bwd_weight"].append(e[2].elapsed_time(e[3]))
+    avg_ms = {k: sum(v) / len(v) for k, v in per.items()}
+
+    if args.copy_probe:
+        src = sets[0]["x"]
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+
+    ms_step = elapsed * 1e3 / args.steps
+    value = wl.B * args.steps / elapsed
+    flops_pass = wl.N * conv_flops_per_pixel(wl.L, wl.k)
+    algo_bytes = {"wtconv_fwd": 2 * act_bytes, "wtconv_bwd_input": 2 * act_bytes,
+                  "wtconv_bwd_weight": 2 * act_bytes}
+    dom = max(avg_ms, key=avg_ms.get)
+    dur_s = avg_ms[dom] * 1e-3
+    achieved_tf = flops_pass / dur_s / 1e12
+    traffic = None
+    tpath = TRAFFIC_SUMMARY.format(workload=wl.name)
+    if os.path.exists(tpath):
+        with open(tpath) as f:
+            tr = json.load(f)
+        if tr.get("source_sha256_16") == source_hash() and dom in tr.get("bytes_per_launch", {}):
+            traffic = tr["bytes_per_launch"][dom]
+    step_bytes = 6 * act_bytes
+    rec = {
+        "metric": "fused WTConv fwd+bwd images/s and effective HBM GB/s (% of peak), 1xMI355X",
+        "value": round(value, 1),
+        "unit": "images/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32" if wl.dtype == "f32" else "f16 storage, f32 accumulate",
+        "data": "synthetic (seeded N(0,1) activations, N(0,0.02^2) filters)",
+        "config": {"workload": wl.name, "B": wl.B, "C": wl.C, "H": wl.H, "W": wl.W,
+                   "levels": wl.L, "k": wl.k, "buffer_sets": nsets},
+        "effective_hbm_gbs": round(step_bytes / (elapsed / args.steps) / 1e9, 1),
+        "effective_hbm_frac": round(step_bytes / (elapsed / args.steps) / 1e9 / PEAK_HBM_GBS, 4),
+        "per_call_ms": {k: round(v, 5) for k, v in avg_ms.items()},
+        "roofline": {
+            "kernel": dom,
+            "bound": "alu",
+            "achieved": round(achieved_tf, 2),
+            "peak": PEAK_FP32_VALU_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(achieved_tf / PEAK_FP32_VALU_TFLOPS, 4),
+            "traffic": traffic,
+            "hbm_gbs": round(algo_bytes[dom] / dur_s / 1e9, 1),
+            "hbm_frac": round(algo_bytes[dom] / dur_s / 1e9 / PEAK_HBM_GBS, 4),
+            "flops_per_launch": flops_pass,
+            "algo_bytes_per_launch": algo_bytes[dom],
+        },
+    }
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline(wl)
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()
