@@ -24,6 +24,7 @@ FLAGS = [
     "-O3", "-std=c++17", "-fPIC", "--offload-arch=gfx950",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-I", INCLUDE, "-I", CSRC, "-Wall", "-Wno-unused-function",
+    "-fconstexpr-steps=200000000",
 ]
 
 

@@ -94,7 +94,7 @@ constexpr Tile plan_tile(int K, int L, int H, int W, int P, int NT, int maxqr) {
             const int n = njobs(K, L, H, W, P, R, Q);
             if (n > NT) continue;
             const double reads = double((Q + K - 1) * (R + K - 1)) / double(Q * R * K * K);
-            const double c = double(Q * R) + 0.5 * reads;
+            const double c = double(Q * R) + 0.5 * reads + ((R & 1) ? 0.0 : 0.01);
             if (c < bc) {
                 bc = c;
                 best = Tile{R, Q, n};
@@ -103,12 +103,75 @@ constexpr Tile plan_tile(int K, int L, int H, int W, int P, int NT, int maxqr) {
     return best;
 }
 
+// LDS layout of one level: row pitch, stride between the 2-D arrays of the
+// level (one per plane and subband) and the level's start offset.
+struct Layout {
+    int pitch, astride, off;
+};
+
+// Bank multiplicity of the tiles' window reads: for every 32 consecutive
+// lanes (the lanes that share an LDS cycle), the most lanes that hit one of
+// 32 four-byte banks, summed over the level's lanes.  Every read of a tile is
+// its window address plus the same constant, so window addresses decide.
+constexpr int bank_cost(int first_job, int njobs_l, int S, int NS, int NG, int R, int Q,
+                        int pitch, int astride, int off) {
+    int cost = 0;
+    const int n0 = first_job & ~31, n1 = first_job + njobs_l;
+    for (int w = n0; w < n1; w += 32) {
+        int cnt[32] = {};
+        int mx = 0;
+        for (int n = w; n < w + 32 && n < n1; ++n) {
+            if (n < first_job) continue;
+            int r = n - first_job;
+            const int strip = r % NS;
+            r /= NS;
+            const int grp = r % NG;
+            const int ps = r / NG;  // plane * S + subband
+            const int a = off + ps * astride + grp * Q * pitch + strip * R;
+            const int b = ((a % 32) + 32) % 32;
+            if (++cnt[b] > mx) mx = cnt[b];
+        }
+        cost += mx;
+    }
+    (void)S;
+    return cost;
+}
+
+// Level start, pitch and array gap, each over one period of the bank index:
+// the level starts on the bank of its first lane's tile (R times its job
+// index), then the pitch is searched with no gap, then the gap.  Least bank
+// multiplicity wins, then least LDS.
+constexpr Layout plan_layout(int first_job, int njobs_l, int S, int NS, int NG, int R, int Q,
+                             int rows, int minpitch, int base) {
+    int off = base;
+    while (((off - R * first_job) % 32 + 32) % 32 != 0) ++off;
+    int bp = minpitch, bc = 1 << 30;
+    for (int dp = 0; dp < 32; ++dp) {
+        const int c = bank_cost(first_job, njobs_l, S, NS, NG, R, Q, minpitch + dp,
+                                rows * (minpitch + dp), off);
+        if (c < bc) {
+            bc = c;
+            bp = minpitch + dp;
+        }
+    }
+    int bg = 0;
+    bc = 1 << 30;
+    for (int gap = 0; gap < 32; ++gap) {
+        const int c = bank_cost(first_job, njobs_l, S, NS, NG, R, Q, bp, rows * bp + gap, off);
+        if (c < bc) {
+            bc = c;
+            bg = gap;
+        }
+    }
+    return Layout{bp, rows * bp + bg, off};
+}
+
 // LDS geometry of a group of P planes.  Level 0 holds the input planes,
 // level l >= 1 the four subbands of each plane.  Arrays are padded to whole
-// tiles and carry a zero border of p = k/2; pitches are odd so that the lanes
-// of a wavefront, which read tiles R columns and Q rows apart, spread over
-// the LDS banks.  The weight-gradient kernel adds compact, border-free copies
-// of levels 1..L for the analysis of dy.
+// tiles and carry a zero border of p = k/2; pitches and gaps are searched so
+// that the lanes of a wavefront, each reading its own tile window, spread
+// over the LDS banks.  The weight-gradient kernel adds compact, border-free
+// copies of levels 1..L for the analysis of dy.
 template <int K_, int L_, int H_, int W_, int P_, int NT_>
 struct Geo {
     static constexpr int K = K_, L = L_, H = H_, W = W_, P = P_, NT = NT_;
@@ -128,14 +191,27 @@ struct Geo {
         return n;
     }
     __host__ __device__ static constexpr int rows(int l) { return NG(l) * Q + 2 * p; }
-    __host__ __device__ static constexpr int pitch(int l) { return (NS(l) * R + 2 * p) | 1; }
-    __host__ __device__ static constexpr int arr(int l) { return rows(l) * pitch(l); }
-    __host__ __device__ static constexpr int off(int l) {
-        int o = 0;
-        for (int m = 0; m < l; ++m) o += P * S(m) * arr(m);
-        return o;
+
+    struct Table {
+        Layout lv[L_ + 1];
+        int end;
+    };
+    static constexpr Table make_table() {
+        Table t{};
+        int base = 0;
+        for (int l = 0; l <= L; ++l) {
+            t.lv[l] = plan_layout(jstart(l), jobs(l), S(l), NS(l), NG(l), R, Q, rows(l),
+                                  NS(l) * R + 2 * p, base);
+            base = t.lv[l].off + P * S(l) * t.lv[l].astride;
+        }
+        t.end = base;
+        return t;
     }
-    static constexpr int side = off(L + 1);
+    static constexpr Table TB = make_table();
+    __host__ __device__ static constexpr int pitch(int l) { return TB.lv[l].pitch; }
+    __host__ __device__ static constexpr int arr(int l) { return TB.lv[l].astride; }
+    __host__ __device__ static constexpr int off(int l) { return TB.lv[l].off; }
+    static constexpr int side = TB.end;
     // compact dy-side arrays, levels 1..L
     __host__ __device__ static constexpr int vpitch(int l) { return NS(l) * R; }
     __host__ __device__ static constexpr int varr(int l) { return NG(l) * Q * vpitch(l); }
@@ -270,66 +346,132 @@ __device__ __forceinline__ void store_vec(T* __restrict__ dst, const float (&v)[
 // Phases
 // ---------------------------------------------------------------------------
 
-// HBM -> LDS for planes b0..b0+P-1 (zeros past B), two rows by V columns per
-// item, with the level-1 butterflies of those 2 x V pixels computed from the
-// same registers.  WRITE_X stores the pixels themselves (x side); the level-1
-// subbands go to the x side (U) or the compact dy side (V).
-template <class G, typename T, bool WRITE_X, bool VSIDE>
-__device__ __forceinline__ void load_level1(float* lds, const T* __restrict__ src, int b0,
-                                            int B, int C, int c, int tid) {
-    constexpr int V = vec_elems<T>(G::W);
+template <int BYTES>
+struct RawVec;
+template <>
+struct RawVec<16> { using type = uint4; };
+template <>
+struct RawVec<8> { using type = uint2; };
+template <>
+struct RawVec<4> { using type = uint32_t; };
+
+// One thread's share of a group's input, held as the raw bytes loaded from
+// HBM so that the loads can be issued a whole group ahead of their use.  An
+// item is ROWS rows by V columns: with four rows the level-2 butterflies are
+// computed from registers too.
+template <class G, typename T>
+struct Fetch {
+    static constexpr int V = vec_elems<T>(G::W);
     static_assert(V % 2 == 0, "even column groups");
-    constexpr int NV = G::W / V, RP = G::H / 2;
-    constexpr int ITEMS = G::P * RP * NV;
+    static constexpr int ROWS = (G::L >= 2 && V % 4 == 0) ? 4 : 2;
+    static constexpr int NV = G::W / V, RB = G::H / ROWS;
+    static constexpr int ITEMS = G::P * RB * NV, IT = cdiv(ITEMS, G::NT);
+    static constexpr int LEVELS = ROWS == 4 ? 2 : 1;  // levels computed here
+    using raw_t = typename RawVec<V * int(sizeof(T))>::type;
+    raw_t r[IT][ROWS];
+
+    // Issue the loads of planes b0..b0+P-1 (zeros past B).
+    __device__ __forceinline__ void issue(const T* __restrict__ src, int b0, int B, int C,
+                                          int c, int tid) {
 #pragma unroll
-    for (int it = 0; it < cdiv(ITEMS, G::NT); ++it) {
-        const int item = tid + it * G::NT;
-        if (ITEMS % G::NT == 0 || item < ITEMS) {
+        for (int it = 0; it < IT; ++it) {
+            const int item = tid + it * G::NT;
             const int cv = item % NV;
-            const int rp = (item / NV) % RP;
-            const int pl = item / (NV * RP);
+            const int rb = (item / NV) % RB;
+            const int pl = item / (NV * RB);
             const int b = b0 + pl;
-            float a[V], d[V];
-            if (b < B) {
-                const T* s = src + ((size_t(b) * C + c) * G::H + 2 * rp) * G::W + cv * V;
-                load_vec<T, V>(s, a);
-                load_vec<T, V>(s + G::W, d);
+            if ((ITEMS % G::NT == 0 || item < ITEMS) && b < B) {
+                const raw_t* s = reinterpret_cast<const raw_t*>(
+                    src + ((size_t(b) * C + c) * G::H + ROWS * rb) * G::W + cv * V);
+#pragma unroll
+                for (int k = 0; k < ROWS; ++k) r[it][k] = s[k * (G::W / V)];
             } else {
 #pragma unroll
-                for (int e = 0; e < V; ++e) a[e] = d[e] = 0.f;
+                for (int k = 0; k < ROWS; ++k) r[it][k] = raw_t{};
             }
-            if constexpr (WRITE_X) {
-                float* x0 = lds + G::uidx(0, pl, 0, 2 * rp, cv * V);
+        }
+    }
+
+    static __device__ __forceinline__ void unpack(const raw_t& raw, float (&v)[V]) {
+        union {
+            raw_t r;
+            T e[V];
+        } u;
+        u.r = raw;
 #pragma unroll
-                for (int e = 0; e < V; ++e) {
-                    x0[e] = a[e];
-                    x0[G::pitch(0) + e] = d[e];
+        for (int k = 0; k < V; ++k) v[k] = to_f(u.e[k]);
+    }
+
+    // (a, b; c, d) -> LL, LH, HL, HH of one 2x2 block, unnormalised.
+    static __device__ __forceinline__ void butterfly(float a, float b, float c, float d,
+                                                     float (&o)[4]) {
+        const float s0 = a + b, d0 = a - b, s1 = c + d, d1 = c - d;
+        o[0] = s0 + s1;
+        o[1] = d0 + d1;
+        o[2] = s0 - s1;
+        o[3] = d0 - d1;
+    }
+
+    template <bool VSIDE>
+    static __device__ __forceinline__ void put(float* lds, int l, int pl, int i, int j,
+                                               const float (&o)[4]) {
+        float* dst;
+        int A;
+        if constexpr (VSIDE) {
+            dst = lds + G::vidx(l, pl, 0, i, j);
+            A = l == 1 ? G::varr(1) : G::varr(2);
+        } else {
+            dst = lds + G::uidx(l, pl, 0, i, j);
+            A = l == 1 ? G::arr(1) : G::arr(G::L >= 2 ? 2 : 1);
+        }
+#pragma unroll
+        for (int s = 0; s < 4; ++s) dst[s * A] = o[s];
+    }
+
+    // Write the pixels to the level-0 array (WRITE_X) and the level-1 (and,
+    // with four-row items, level-2) butterflies to the x side or the dy side.
+    template <bool WRITE_X, bool VSIDE>
+    __device__ __forceinline__ void commit(float* lds, int tid) const {
+#pragma unroll
+        for (int it = 0; it < IT; ++it) {
+            const int item = tid + it * G::NT;
+            if (ITEMS % G::NT == 0 || item < ITEMS) {
+                const int cv = item % NV;
+                const int rb = (item / NV) % RB;
+                const int pl = item / (NV * RB);
+                float x[ROWS][V];
+#pragma unroll
+                for (int k = 0; k < ROWS; ++k) unpack(r[it][k], x[k]);
+                if constexpr (WRITE_X) {
+                    float* o = lds + G::uidx(0, pl, 0, ROWS * rb, cv * V);
+#pragma unroll
+                    for (int k = 0; k < ROWS; ++k)
+#pragma unroll
+                        for (int e = 0; e < V; ++e) o[k * G::pitch(0) + e] = x[k][e];
                 }
-            }
+                float ll[ROWS / 2][V / 2];
 #pragma unroll
-            for (int m = 0; m < V / 2; ++m) {
-                const float p0 = a[2 * m], p1 = a[2 * m + 1], q0 = d[2 * m], q1 = d[2 * m + 1];
-                const float s0 = p0 + p1, d0 = p0 - p1, s1 = q0 + q1, d1 = q0 - q1;
-                const int j = cv * (V / 2) + m;
-                if constexpr (VSIDE) {
-                    float* o = lds + G::vidx(1, pl, 0, rp, j);
-                    constexpr int A = G::varr(1);
-                    o[0] = s0 + s1;
-                    o[A] = d0 + d1;
-                    o[2 * A] = s0 - s1;
-                    o[3 * A] = d0 - d1;
-                } else {
-                    float* o = lds + G::uidx(1, pl, 0, rp, j);
-                    constexpr int A = G::arr(1);
-                    o[0] = s0 + s1;
-                    o[A] = d0 + d1;
-                    o[2 * A] = s0 - s1;
-                    o[3 * A] = d0 - d1;
+                for (int rr = 0; rr < ROWS / 2; ++rr)
+#pragma unroll
+                    for (int m = 0; m < V / 2; ++m) {
+                        float o[4];
+                        butterfly(x[2 * rr][2 * m], x[2 * rr][2 * m + 1], x[2 * rr + 1][2 * m],
+                                  x[2 * rr + 1][2 * m + 1], o);
+                        ll[rr][m] = o[0];
+                        put<VSIDE>(lds, 1, pl, (ROWS / 2) * rb + rr, cv * (V / 2) + m, o);
+                    }
+                if constexpr (ROWS == 4) {
+#pragma unroll
+                    for (int m = 0; m < V / 4; ++m) {
+                        float o[4];
+                        butterfly(ll[0][2 * m], ll[0][2 * m + 1], ll[1][2 * m], ll[1][2 * m + 1], o);
+                        put<VSIDE>(lds, 2, pl, rb, cv * (V / 4) + m, o);
+                    }
                 }
             }
         }
     }
-}
+};
 
 // Level-l analysis (l >= 2) from the raw LL of level l-1:
 // (a, b; c, d) -> LL = a+b+c+d, LH = a-b+c-d, HL = a+b-c-d, HH = a-b-c+d.
@@ -385,11 +527,11 @@ __device__ __forceinline__ int level_pitch(int lvl) {
 // acc[q][j] = sum_{u,v} w[u*K+v] * src[(q+u)*pitch + j+v].
 template <int K, int Q, int R>
 __device__ __forceinline__ void conv_tile(const float* src, int pitch, const float (&w)[K * K],
-                                          float (&acc)[Q][R]) {
+                                          float init, float (&acc)[Q][R]) {
 #pragma unroll
     for (int q = 0; q < Q; ++q)
 #pragma unroll
-        for (int j = 0; j < R; ++j) acc[q][j] = 0.f;
+        for (int j = 0; j < R; ++j) acc[q][j] = init;
 #pragma unroll
     for (int ir = 0; ir < Q + K - 1; ++ir) {
         float in[R + K - 1];
@@ -457,37 +599,82 @@ __device__ __forceinline__ void cascade_level(float* lds, int tid) {
     }
 }
 
-// y = base conv (already in the level-0 array) + bias + level-1 synthesis,
-// V output columns per item, vector store to HBM.
+// y = base conv plus bias (already in the level-0 array) + synthesis, written
+// back in place.  Each item covers two output rows (one level-1 coefficient
+// row) by V columns.  Level 2, whose coarser levels are already folded into
+// its LL, is folded into the level-1 LL here, on the fly; then each level-1
+// coefficient is expanded over its 2x2 block.
 template <class G, typename T>
-__device__ __forceinline__ void final_out(const float* lds, float bias, T* __restrict__ out,
-                                          int b0, int B, int C, int c, int tid) {
+__device__ __forceinline__ void final_to_lds(float* lds, int tid) {
     constexpr int V = vec_elems<T>(G::W);
-    constexpr int NV = G::W / V, ITEMS = G::P * G::H * NV;
+    constexpr int NV = G::W / V, RP = G::H / 2, ITEMS = G::P * RP * NV;
     constexpr int A1 = G::arr(1);
 #pragma unroll
     for (int it = 0; it < cdiv(ITEMS, G::NT); ++it) {
         const int item = tid + it * G::NT;
         if (ITEMS % G::NT == 0 || item < ITEMS) {
             const int cv = item % NV;
-            const int y = (item / NV) % G::H;
-            const int pl = item / (NV * G::H);
-            const float sy = (y & 1) ? -1.f : 1.f;
-            const float* xb = lds + G::uidx(0, pl, 0, y, cv * V);
-            const float* cs = lds + G::uidx(1, pl, 0, y >> 1, cv * (V / 2));
-            float v[V];
+            const int i = (item / NV) % RP;
+            const int pl = item / (NV * RP);
+            float* x0 = lds + G::uidx(0, pl, 0, 2 * i, cv * V);
+            const float* cs = lds + G::uidx(1, pl, 0, i, cv * (V / 2));
 #pragma unroll
             for (int m = 0; m < V / 2; ++m) {
-                const float e = fmaf(sy, cs[2 * A1 + m], cs[m]);
-                const float f = fmaf(sy, cs[3 * A1 + m], cs[A1 + m]);
-                v[2 * m] = xb[2 * m] + bias + (e + f);
-                v[2 * m + 1] = xb[2 * m + 1] + bias + (e - f);
+                float ll = cs[m];
+                if constexpr (G::L >= 2) {
+                    constexpr int A2 = G::arr(2);
+                    const int j = cv * (V / 2) + m;
+                    const float* c2 = lds + G::uidx(2, pl, 0, i >> 1, j >> 1);
+                    const float sy2 = (i & 1) ? -1.f : 1.f, sx2 = (j & 1) ? -1.f : 1.f;
+                    const float e2 = fmaf(sy2, c2[2 * A2], c2[0]);
+                    const float f2 = fmaf(sy2, c2[3 * A2], c2[A2]);
+                    ll += fmaf(sx2, f2, e2);
+                }
+                const float lh = cs[A1 + m], hl = cs[2 * A1 + m], hh = cs[3 * A1 + m];
+                const float e0 = ll + hl, f0 = lh + hh;  // row 2i   (row bit 0)
+                const float e1 = ll - hl, f1 = lh - hh;  // row 2i+1 (row bit 1)
+                x0[2 * m] += e0 + f0;
+                x0[2 * m + 1] += e0 - f0;
+                x0[G::pitch(0) + 2 * m] += e1 + f1;
+                x0[G::pitch(0) + 2 * m + 1] += e1 - f1;
             }
-            const int b = b0 + pl;
-            if (b < B) store_vec<T, V>(out + ((size_t(b) * C + c) * G::H + y) * G::W + cv * V, v);
         }
     }
 }
+
+// The finished group (y in the level-0 array) -> HBM, ROWS x V per item.
+template <class G, typename T>
+__device__ __forceinline__ void store_out(const float* lds, T* __restrict__ out, int b0, int B,
+                                          int C, int c, int tid) {
+    using F = Fetch<G, T>;
+    constexpr int V = F::V, ROWS = F::ROWS, NV = F::NV, RB = F::RB, ITEMS = F::ITEMS;
+#pragma unroll
+    for (int it = 0; it < F::IT; ++it) {
+        const int item = tid + it * G::NT;
+        if (ITEMS % G::NT == 0 || item < ITEMS) {
+            const int cv = item % NV;
+            const int rb = (item / NV) % RB;
+            const int pl = item / (NV * RB);
+            const int b = b0 + pl;
+            if (b < B) {
+                const float* x0 = lds + G::uidx(0, pl, 0, ROWS * rb, cv * V);
+                T* o = out + ((size_t(b) * C + c) * G::H + ROWS * rb) * G::W + cv * V;
+#pragma unroll
+                for (int k = 0; k < ROWS; ++k) {
+                    float v[V];
+#pragma unroll
+                    for (int e = 0; e < V; ++e) v[e] = x0[k * G::pitch(0) + e];
+                    store_vec<T, V>(o + k * G::W, v);
+                }
+            }
+        }
+    }
+}
+
+// Wait for every outstanding vector-memory operation (the group's prefetched
+// input and stores issued a group earlier).  Stores are then issued only after
+// this point, so no later wait for prefetched data has to drain fresh stores.
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 // Folded filters into LDS: [0, KK) base, then (l, s) blocks, then the bias.
 template <class G, typename T, bool FLIP>
@@ -518,75 +705,127 @@ __device__ __forceinline__ void fold_weights(float* wf, const T* __restrict__ wb
 // Kernels
 // ---------------------------------------------------------------------------
 
-// Forward (FLIP = false) or input gradient (FLIP = true) for channel
-// blockIdx.x % C over `gpw` groups of P planes starting at group
-// (blockIdx.x / C) * gpw.
+// Waves per SIMD the LDS footprint allows (NT/64 waves per workgroup spread
+// over 4 SIMDs); the register budget is sized to match.
+constexpr int waves_for_lds(size_t lds_bytes, int nt) {
+    int wg = int(163840 / (lds_bytes ? lds_bytes : 1));
+    int w = wg * (nt / 64) / 4;
+    return w < 1 ? 1 : (w > 8 ? 8 : w);
+}
+
+template <class G>
+constexpr size_t apply_lds_bytes() { return sizeof(float) * (G::side + G::NWF); }
+template <class G>
+constexpr size_t bww_lds_bytes() {
+    size_t a = sizeof(float) * (G::side + G::vside), b = sizeof(float) * G::NT * (G::KK + 1);
+    return a > b ? a : b;
+}
+
+// Forward (FLIP = false) or input gradient (FLIP = true).  The C * ceil(B/P)
+// (channel, group of P planes) pairs, channel-major, are split into gridDim.x
+// equal contiguous ranges, one per workgroup; the filters are folded again
+// whenever a workgroup's range enters a new channel.  The next group's input
+// is loaded into registers while the current one is computed, and a group's
+// output is stored at the start of the next iteration.
 template <int K, int L, int H, int W, int P, int NT, typename T, bool FLIP>
-__global__ __launch_bounds__(NT) void k_plane_apply(
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(
+    waves_for_lds(apply_lds_bytes<Geo<K, L, H, W, P, NT>>(), NT) < 4
+        ? waves_for_lds(apply_lds_bytes<Geo<K, L, H, W, P, NT>>(), NT)
+        : 4,
+    8))) void k_plane_apply(
     const T* __restrict__ in, const T* __restrict__ wb, const T* __restrict__ bb,
     const T* __restrict__ sb, const T* __restrict__ ww, const T* __restrict__ sw,
-    T* __restrict__ out, int B, int C, int gpw) {
+    T* __restrict__ out, int B, int C) {
     using G = Geo<K, L, H, W, P, NT>;
+    using F = Fetch<G, T>;
     constexpr int KK = G::KK, Q = G::Q, R = G::R;
     extern __shared__ float lds[];
     float* wf = lds + G::side;
     const int tid = threadIdx.x;
-    const int c = blockIdx.x % C;
-    const int chunk = blockIdx.x / C;
+    const int ngroups = cdiv(B, P);
+    const long total = long(C) * ngroups;
+    const int q0 = int(total * blockIdx.x / gridDim.x);
+    const int q1 = int(total * (blockIdx.x + 1) / gridDim.x);
+    F fx;
+    if (q0 < q1) fx.issue(in, (q0 % ngroups) * P, B, C, q0 / ngroups, tid);
     for (int i = tid; i < G::side; i += NT) lds[i] = 0.f;
-    fold_weights<G, T, FLIP>(wf, wb, bb, sb, ww, sw, C, c, tid);
-    __syncthreads();
 
     const Job job = decode_job<G>(tid);
     const int wsrc = job.lvl == 0 ? 0 : KK * (1 + (job.lvl - 1) * 4 + job.s);
-    float w[KK];
-#pragma unroll
-    for (int t = 0; t < KK; ++t) w[t] = wf[wsrc + t];
-    const float bias = wf[G::NWF - 1];
     const int win = window_index<G>(job);
     const int pitch = level_pitch<G>(job.lvl);
     const int hrows = by_level<G>(job.lvl, [](auto lc) { return G::hl(decltype(lc)::value); });
     const int wcols = by_level<G>(job.lvl, [](auto lc) { return G::wl(decltype(lc)::value); });
     const int nrows = min(Q, hrows - job.grp * Q);
     const int ncols = min(R, wcols - job.strip * R);
+    const bool full = nrows == Q && ncols == R;
     const int dst = win + G::p * pitch + G::p;  // tile's first output element
 
-    const int ngroups = cdiv(B, P);
-    const int g0 = chunk * gpw;
-    const int g1 = min(g0 + gpw, ngroups);
-    for (int g = g0; g < g1; ++g) {
-        const int b0 = g * P;
-        load_level1<G, T, true, false>(lds, in, b0, B, C, c, tid);
+    float w[KK];
+    float init = 0.f;
+    int cur = -1, pend_b0 = -1, pend_c = 0;
+    for (int q = q0; q < q1; ++q) {
+        const int c = q / ngroups;
+        const int b0 = (q % ngroups) * P;
+        if (c != cur) {
+            fold_weights<G, T, FLIP>(wf, wb, bb, sb, ww, sw, C, c, tid);
+            __syncthreads();
+#pragma unroll
+            for (int t = 0; t < KK; ++t) w[t] = wf[wsrc + t];
+            init = job.lvl == 0 ? wf[G::NWF - 1] : 0.f;
+            cur = c;
+        }
+        wait_vmem();
+        if (pend_b0 >= 0) {
+            store_out<G, T>(lds, out, pend_b0, B, C, pend_c, tid);
+            __syncthreads();
+        }
+        fx.template commit<true, false>(lds, tid);
         __syncthreads();
-        static_for<2, L + 1>([&](auto lc) {
+        static_for<F::LEVELS + 1, L + 1>([&](auto lc) {
             analysis_level<G, decltype(lc)::value, false>(lds, tid);
             __syncthreads();
         });
         float acc[Q][R];
-        if (job.on) conv_tile<K, Q, R>(lds + win, pitch, w, acc);
+        if (job.on) conv_tile<K, Q, R>(lds + win, pitch, w, init, acc);
+        // the next group's loads fly during write-back, synthesis and store
+        if (q + 1 < q1) fx.issue(in, ((q + 1) % ngroups) * P, B, C, (q + 1) / ngroups, tid);
         __syncthreads();
         if (job.on) {
+            if (full) {
 #pragma unroll
-            for (int q = 0; q < Q; ++q)
+                for (int qq = 0; qq < Q; ++qq)
 #pragma unroll
-                for (int j = 0; j < R; ++j)
-                    if (q < nrows && j < ncols) lds[dst + q * pitch + j] = acc[q][j];
+                    for (int j = 0; j < R; ++j) lds[dst + qq * pitch + j] = acc[qq][j];
+            } else {
+#pragma unroll
+                for (int qq = 0; qq < Q; ++qq)
+#pragma unroll
+                    for (int j = 0; j < R; ++j)
+                        if (qq < nrows && j < ncols) lds[dst + qq * pitch + j] = acc[qq][j];
+            }
         }
         __syncthreads();
-        static_for<0, L - 1>([&](auto lc) {
+        // levels L..3 fold into the LL of the level above; level 2 folds into
+        // level 1 inside final_to_lds
+        static_for<0, L - 2>([&](auto lc) {
             cascade_level<G, L - decltype(lc)::value>(lds, tid);
             __syncthreads();
         });
-        final_out<G, T>(lds, bias, out, b0, B, C, c, tid);
+        final_to_lds<G, T>(lds, tid);
+        pend_b0 = b0;
+        pend_c = c;
         __syncthreads();
     }
+    if (pend_b0 >= 0) store_out<G, T>(lds, out, pend_b0, B, C, pend_c, tid);
 }
 
 // Weight-gradient partial sums of channel blockIdx.x % C over the groups of
 // chunk blockIdx.x / C: one row of G::NPART floats per workgroup,
 // [G_b (KK), sum dy, G[l][s] (4 L KK)].
 template <int K, int L, int H, int W, int P, int NT, typename T>
-__global__ __launch_bounds__(NT) void k_plane_bww(const T* __restrict__ x,
+__global__ __launch_bounds__(NT) void k_plane_bww(
+    const T* __restrict__ x,
                                                   const T* __restrict__ dy,
                                                   float* __restrict__ part, int B, int C,
                                                   int gpw) {
@@ -596,6 +835,12 @@ __global__ __launch_bounds__(NT) void k_plane_bww(const T* __restrict__ x,
     const int tid = threadIdx.x;
     const int c = blockIdx.x % C;
     const int chunk = blockIdx.x / C;
+    const int ngroups = cdiv(B, P);
+    const int g0 = chunk * gpw;
+    const int g1 = min(g0 + gpw, ngroups);
+    Fetch<G, T> fx, fd;
+    fx.issue(x, g0 * P, B, C, c, tid);
+    fd.issue(dy, g0 * P, B, C, c, tid);
     for (int i = tid; i < G::side + G::vside; i += NT) lds[i] = 0.f;
     __syncthreads();
 
@@ -622,15 +867,16 @@ __global__ __launch_bounds__(NT) void k_plane_bww(const T* __restrict__ x,
     for (int t = 0; t < KK; ++t) acc[t] = 0.f;
     float sdy = 0.f;
 
-    const int ngroups = cdiv(B, P);
-    const int g0 = chunk * gpw;
-    const int g1 = min(g0 + gpw, ngroups);
     for (int g = g0; g < g1; ++g) {
         const int b0 = g * P;
-        load_level1<G, T, true, false>(lds, x, b0, B, C, c, tid);
-        load_level1<G, T, false, true>(lds, dy, b0, B, C, c, tid);
+        fx.template commit<true, false>(lds, tid);
+        fd.template commit<false, true>(lds, tid);
+        if (g + 1 < g1) {
+            fx.issue(x, b0 + P, B, C, c, tid);
+            fd.issue(dy, b0 + P, B, C, c, tid);
+        }
         __syncthreads();
-        static_for<2, L + 1>([&](auto lc) {
+        static_for<Fetch<G, T>::LEVELS + 1, L + 1>([&](auto lc) {
             analysis_level<G, decltype(lc)::value, false>(lds, tid);
             analysis_level<G, decltype(lc)::value, true>(lds, tid);
             __syncthreads();
@@ -757,10 +1003,8 @@ struct Variant {
 template <int K, int L, int H, int W, int P, int NT, typename T>
 Variant make_variant(int dtype) {
     using G = Geo<K, L, H, W, P, NT>;
-    const size_t la = sizeof(float) * (G::side + G::NWF);
-    size_t lb = sizeof(float) * (G::side + G::vside);
-    const size_t lr = sizeof(float) * NT * (G::KK + 1);
-    if (lb < lr) lb = lr;
+    const size_t la = apply_lds_bytes<G>();
+    const size_t lb = bww_lds_bytes<G>();
     return Variant{K, L, H, W, dtype, P, NT,
                    reinterpret_cast<const void*>(&k_plane_apply<K, L, H, W, P, NT, T, false>),
                    reinterpret_cast<const void*>(&k_plane_apply<K, L, H, W, P, NT, T, true>),
@@ -805,16 +1049,30 @@ hipError_t prepare(const void* fn, size_t lds) {
     return hipSuccess;
 }
 
-// Groups of planes per workgroup: enough workgroups to cover the chip about
-// three times, each walking a contiguous run of groups of one channel.
-int groups_per_wg(const wtconv_shape& s, int P) {
+// Workgroups that fit on the whole device at once for this kernel (compute
+// units times resident workgroups per unit), 1024 when it cannot be queried.
+int resident_wgs(const void* fn, int nt, size_t lds) {
+    int dev = 0, cus = 0, per = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, fn, nt, lds) != hipSuccess ||
+        cus <= 0 || per <= 0)
+        return 1024;
+    return cus * per;
+}
+
+// Weight gradient: chunks of the batch per channel.  At most this many, so
+// that the workspace size is a function of the shape alone.
+constexpr int kMaxChunks = 64;
+
+int bww_chunks(const wtconv_shape& s, int P, int slots) {
     const int ngroups = cdiv(s.B, P);
-    const long total = long(ngroups) * s.C;
-    const long target = 768;
-    int gpw = int((total + target - 1) / target);
-    if (gpw < 1) gpw = 1;
-    if (gpw > ngroups) gpw = ngroups > 0 ? ngroups : 1;
-    return gpw;
+    int want = slots / (s.C > 0 ? s.C : 1);
+    if (want < 1) want = 1;
+    if (want > kMaxChunks) want = kMaxChunks;
+    if (want > ngroups) want = ngroups;
+    const int gpw = cdiv(ngroups, want);
+    return cdiv(ngroups, gpw);
 }
 
 }  // namespace
@@ -824,8 +1082,8 @@ bool plane_supported(const wtconv_shape& s) { return find_variant(s) != nullptr;
 size_t plane_workspace_bytes(const wtconv_shape& s) {
     const Variant* v = find_variant(s);
     if (!v || s.B == 0 || s.C == 0) return 0;
-    const int gpw = groups_per_wg(s, v->P);
-    const int nchunk = cdiv(cdiv(s.B, v->P), gpw);
+    const int ngroups = cdiv(s.B, v->P);
+    const int nchunk = ngroups < kMaxChunks ? ngroups : kMaxChunks;
     const int KK = s.k * s.k;
     const size_t npart = size_t(KK) + 1 + size_t(4) * s.L * KK;
     return size_t(nchunk) * s.C * npart * sizeof(float);
@@ -838,16 +1096,17 @@ hipError_t plane_apply(const wtconv_shape& s, const void* in, const Params& p, v
     const void* fn = flip ? v->bwi : v->fwd;
     hipError_t e = prepare(fn, v->lds_apply);
     if (e != hipSuccess) return e;
-    int gpw = groups_per_wg(s, v->P), B = s.B, C = s.C;
-    const int nchunk = cdiv(cdiv(s.B, v->P), gpw);
+    int B = s.B, C = s.C;
+    const long total = long(cdiv(s.B, v->P)) * s.C;
+    long nwg = resident_wgs(fn, v->NT, v->lds_apply);
+    if (nwg > total) nwg = total;
     const void* bb = flip ? p.w_base : p.b_base;  // unread when flipped
     const void* wb = p.w_base;
     const void* sb = p.s_base;
     const void* ww = p.w_wav;
     const void* sw = p.s_wav;
-    void* args[] = {&in, &wb, &bb, &sb, &ww, &sw, &out, &B, &C, &gpw};
-    e = hipLaunchKernel(fn, dim3(unsigned(nchunk) * unsigned(s.C)), dim3(v->NT), args,
-                        v->lds_apply, stream);
+    void* args[] = {&in, &wb, &bb, &sb, &ww, &sw, &out, &B, &C};
+    e = hipLaunchKernel(fn, dim3(unsigned(nwg)), dim3(v->NT), args, v->lds_apply, stream);
     if (e != hipSuccess) return e;
     return hipGetLastError();
 }
@@ -873,8 +1132,8 @@ hipError_t plane_bwd_weight(const wtconv_shape& s, const void* x, const void* dy
     if (!v) return hipErrorInvalidValue;
     hipError_t e = prepare(v->bww, v->lds_bww);
     if (e != hipSuccess) return e;
-    int gpw = groups_per_wg(s, v->P), B = s.B, C = s.C;
-    const int nchunk = cdiv(cdiv(s.B, v->P), gpw);
+    const int nchunk = bww_chunks(s, v->P, resident_wgs(v->bww, v->NT, v->lds_bww));
+    int gpw = cdiv(cdiv(s.B, v->P), nchunk), B = s.B, C = s.C;
     float* part = static_cast<float*>(workspace);
     void* args[] = {&x, &dy, &part, &B, &C, &gpw};
     e = hipLaunchKernel(v->bww, dim3(unsigned(nchunk) * unsigned(s.C)), dim3(v->NT), args,
