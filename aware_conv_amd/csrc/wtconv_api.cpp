@@ -57,15 +57,18 @@ int check_params(const wtconv_shape* s, const void* w_base, const void* b_base,
     return WTCONV_OK;
 }
 
-// The one kernel family of this build: whole planes staged in LDS.
+// Two kernel families: whole planes staged in LDS (the shapes this build
+// instantiates), else output tiles of large planes plus per-plane deep levels.
+bool use_plane(const wtconv_shape* s) { return wtc::plane_supported(*s); }
+
 int check_supported(const wtconv_shape* s) {
     if (empty_act(s)) return WTCONV_OK;
-    return wtc::plane_supported(*s) ? WTCONV_OK : WTCONV_ERR_UNSUPPORTED;
+    return (use_plane(s) || wtc::tile_supported(*s)) ? WTCONV_OK : WTCONV_ERR_UNSUPPORTED;
 }
 
 size_t workspace_bytes(const wtconv_shape* s) {
     if (empty_act(s)) return 0;
-    return wtc::plane_workspace_bytes(*s);
+    return use_plane(s) ? wtc::plane_workspace_bytes(*s) : wtc::tile_workspace_bytes(*s);
 }
 
 int hip_status(hipError_t e) { return e == hipSuccess ? WTCONV_OK : WTCONV_ERR_HIP; }
@@ -84,10 +87,15 @@ int apply(const wtconv_shape* s, const void* in, const void* w_base, const void*
     if (overlap(in, out, act_bytes(s))) return WTCONV_ERR_ALIAS;
     rc = check_supported(s);
     if (rc) return rc;
-    (void)workspace;  // the forward and the input gradient need no workspace
-    (void)ws_bytes;
     Params p{w_base, b_base, s_base, w_wav, s_wav};
-    return hip_status(wtc::plane_apply(*s, in, p, out, flip, static_cast<hipStream_t>(stream)));
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (use_plane(s)) return hip_status(wtc::plane_apply(*s, in, p, out, flip, st));
+    // tiles of large planes: deeper levels go through the workspace
+    const size_t need = workspace_bytes(s);
+    if (ws_bytes < need) return WTCONV_ERR_WORKSPACE;
+    if (need > 0 && !workspace) return WTCONV_ERR_NULL;
+    if (need > 0 && !aligned(workspace, 16)) return WTCONV_ERR_ALIGN;
+    return hip_status(wtc::tile_apply(*s, in, p, out, flip, workspace, st));
 }
 
 }  // namespace
@@ -147,7 +155,8 @@ int wtconv_bwd_weight(const wtconv_shape* s, const void* x, const void* dy, cons
     if (ws_bytes < need) return WTCONV_ERR_WORKSPACE;
     if (need > 0 && !workspace) return WTCONV_ERR_NULL;
     if (need > 0 && !aligned(workspace, 16)) return WTCONV_ERR_ALIGN;
-    return hip_status(wtc::plane_bwd_weight(*s, x, dy, p, g, workspace, st));
+    if (use_plane(s)) return hip_status(wtc::plane_bwd_weight(*s, x, dy, p, g, workspace, st));
+    return hip_status(wtc::tile_bwd_weight(*s, x, dy, p, g, workspace, st));
 }
 
 const char* wtconv_strerror(int code) {

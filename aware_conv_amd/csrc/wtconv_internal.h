@@ -42,5 +42,19 @@ hipError_t plane_bwd_weight(const wtconv_shape& s, const void* x,
 // Zero parameter gradients (empty batch or empty planes).
 hipError_t zero_grads(const wtconv_shape& s, const Params& p, const Grads& g,
                       hipStream_t stream);
+// Sum `rows` fp32 partial rows per channel in order and apply the chain rule
+// through the fold (rows = 0 gives zero gradients).
+hipError_t finalize_grads(const wtconv_shape& s, const float* part, int rows, const Params& p,
+                          const Grads& g, hipStream_t stream);
+
+// Tile path for planes too large for one workgroup's LDS: base conv and up to
+// three levels per 32 x 32 output tile, deeper levels per plane.
+bool tile_supported(const wtconv_shape& s);
+size_t tile_workspace_bytes(const wtconv_shape& s);
+hipError_t tile_apply(const wtconv_shape& s, const void* in, const Params& p, void* out,
+                      bool flip, void* workspace, hipStream_t stream);
+hipError_t tile_bwd_weight(const wtconv_shape& s, const void* x, const void* dy,
+                           const Params& p, const Grads& g, void* workspace,
+                           hipStream_t stream);
 
 }  // namespace wtc

@@ -1,0 +1,19 @@
+// Tile kernels for k = 1 (instantiated in a unit of their own so the kernel
+// sizes compile in parallel).
+#include <hip/hip_fp16.h>
+
+#include "wtconv_tile_variant.h"
+
+namespace wtc {
+
+const TileVariant* tile_table_k1(int* n) {
+    static const TileVariant t[] = {
+        make_tile_variant<1, 1, float>(WTCONV_F32), make_tile_variant<1, 1, __half>(WTCONV_F16),
+        make_tile_variant<1, 2, float>(WTCONV_F32), make_tile_variant<1, 2, __half>(WTCONV_F16),
+        make_tile_variant<1, 3, float>(WTCONV_F32), make_tile_variant<1, 3, __half>(WTCONV_F16),
+    };
+    *n = int(sizeof(t) / sizeof(t[0]));
+    return t;
+}
+
+}  // namespace wtc

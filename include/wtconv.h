@@ -88,8 +88,10 @@ int wtconv_workspace_size(const wtconv_shape* s, size_t* bytes);
 /*
  * Forward: y = WTConv(x) as defined above (gist.science/pt, "Metodologia":
  * fused Haar analysis, closed-form synthesis, folded scales).  x and y are
- * [B][C][H][W]; y must not overlap x.  The workspace may be NULL when
- * wtconv_workspace_size() reported 0.
+ * [B][C][H][W]; y must not overlap x.  Planes too large for on-chip staging
+ * with more than three levels use the workspace for the deeper levels'
+ * contribution (1/64 of the input); pass wtconv_workspace_size() bytes, or
+ * NULL when it reported 0.
  */
 int wtconv_fwd(const wtconv_shape* s, const void* x, const void* w_base,
                const void* b_base, const void* s_base, const void* w_wav,
@@ -101,7 +103,8 @@ int wtconv_fwd(const wtconv_shape* s, const void* x, const void* w_base,
  * part, which is the same operator with every kernel rotated by 180 degrees
  * and no bias (the gradient the paper verifies alongside the forward,
  * gist.science/pt "Principais Contribuicoes").  dy and dx are [B][C][H][W];
- * dx must not overlap dy.  b_base is not needed.
+ * dx must not overlap dy.  b_base is not needed.  Workspace as for
+ * wtconv_fwd.
  */
 int wtconv_bwd_input(const wtconv_shape* s, const void* dy,
                      const void* w_base, const void* s_base,

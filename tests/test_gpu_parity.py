@@ -65,7 +65,7 @@ def assert_parity(d, dtype, label, names=NAMES):
         assert errs[n] <= TOL[dtype], (label, n, errs[n])
 
 
-@pytest.mark.parametrize("name", ["tiny", "stage1", "stage2", "stage3", "stage1_f16"])
+@pytest.mark.parametrize("name", ["tiny", "stage1", "stage2", "stage3", "stage1_f16", "highres"])
 def test_named_workload_full_size(name):
     wl = wi.WORKLOADS[name]
     print("\ncase %s %s" % (name, wl), flush=True)
@@ -102,6 +102,31 @@ def test_small_shapes_ragged_batch(k, L, H, W, dtype):
     d["s_wav"] = (0.1 + 0.5 * torch.randn(L, C, 4, generator=g)).to(td)
     d["b_base"] = (0.5 * torch.randn(C, generator=g)).to(td)
     assert_parity(d, dtype, "k%d L%d %dx%d %s" % (k, L, H, W, dtype))
+
+
+TILED = [  # k, L, H, W, dtype: planes handled as 32 x 32 tiles (+ deep levels)
+    (3, 3, 64, 64, "f32"),    # three levels in the tile, no deep levels
+    (5, 2, 48, 80, "f32"),    # partial edge tiles
+    (3, 2, 36, 40, "f32"),    # partial tiles, H != W
+    (1, 1, 40, 40, "f32"),    # k = 1: no halo
+    (5, 4, 96, 64, "f32"),    # one deep level
+    (7, 5, 64, 96, "f32"),    # two deep levels, k = 7
+    (5, 6, 128, 128, "f32"),  # three deep levels
+    (5, 3, 64, 64, "f16"),
+    (5, 5, 128, 96, "f16"),
+]
+
+
+@pytest.mark.parametrize("k,L,H,W,dtype", TILED)
+def test_tiled_planes(k, L, H, W, dtype):
+    B, C = 3, 5
+    d = wi.make_inputs(B, C, H, W, L, k, dtype, seed=k * 1000 + L * 100 + H + W)
+    g = torch.Generator().manual_seed(11)
+    td = d["x"].dtype
+    d["s_base"] = (1 + 0.5 * torch.randn(C, generator=g)).to(td)
+    d["s_wav"] = (0.3 + 0.5 * torch.randn(L, C, 4, generator=g)).to(td)
+    d["b_base"] = (0.5 * torch.randn(C, generator=g)).to(td)
+    assert_parity(d, dtype, "tiled k%d L%d %dx%d %s" % (k, L, H, W, dtype))
 
 
 def test_single_image_single_channel():
