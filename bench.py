@@ -34,8 +34,9 @@ sys.path.insert(0, ROOT)
 PEAK_FP32_VALU_TFLOPS = 78.6    # 256 CU * 4 SIMD * 16 lanes * 2 FLOP * 2.4 GHz, no packed FP32
 PEAK_FP32_PACKED_TFLOPS = 157.3  # the same with packed FP32 (not used by these kernels)
 PEAK_HBM_GBS = 8000.0
-KERNEL_SOURCE = os.path.join(ROOT, "aware_conv_amd", "csrc", "wtconv_plane.hip")
+KERNEL_SOURCES = os.path.join(ROOT, "aware_conv_amd", "csrc")
 TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "traffic_{workload}.json")
+COPY_PROBE_BYTES = 3 << 28  # 768 MiB: larger than any other copy of a bench run
 
 
 def conv_flops_per_pixel(L, k):
@@ -52,8 +53,66 @@ def io_model_reference(L):
 
 
 def source_hash():
-    with open(KERNEL_SOURCE, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(KERNEL_SOURCES)):
+        if name.endswith((".hip", ".h", ".cpp")):
+            with open(os.path.join(KERNEL_SOURCES, name), "rb") as f:
+                h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()[:16]
+
+
+def call_of(kernel_name):
+    """Entry point a profiled kernel belongs to, or None."""
+    n = kernel_name
+    if "k_plane_apply" in n or "k_tile_apply" in n or "k_deep_apply" in n:
+        # template argument FLIP: ..., false> forward, ..., true> input gradient
+        head = n.split("(")[0]
+        return "wtconv_bwd_input" if head.rstrip("> ").endswith("true") else "wtconv_fwd"
+    if "k_plane_bww" in n or "k_tile_bww" in n or "k_deep_bww" in n or "k_bww_final" in n:
+        return "wtconv_bwd_weight"
+    return None
+
+
+def summarize_traffic(fetch_dir, write_dir, wl, act_bytes):
+    """HBM bytes per entry-point call from two rocprofv3 --pmc runs (FETCH_SIZE,
+    WRITE_SIZE, KiB per dispatch), each scaled by what the same counter reads
+    for the plain device copy of act_bytes that --copy-probe performs."""
+    import csv
+    import glob
+    out = {}
+    for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+        rows = [r for f in files for r in csv.DictReader(open(f)) if r["Counter_Name"] == counter]
+        copies = [float(r["Counter_Value"]) for r in rows
+                  if "copyBuffer" in r["Kernel_Name"] and int(r["Grid_Size"]) > 0]
+        # the probe's three copies are the largest copies of the run
+        copies = sorted(copies)[-3:]
+        kib_copy = sum(copies) / len(copies)
+        factor = COPY_PROBE_BYTES / (kib_copy * 1024.0)
+        per_call = {}
+        count = {}
+        for r in rows:
+            c = call_of(r["Kernel_Name"])
+            if c is None:
+                continue
+            per_call[c] = per_call.get(c, 0.0) + float(r["Counter_Value"]) * 1024.0 * factor
+            if "final" not in r["Kernel_Name"] and "deep" not in r["Kernel_Name"]:
+                count[c] = count.get(c, 0) + 1
+        out[counter] = {"factor": factor, "copy_kib": kib_copy,
+                        "bytes_per_call": {c: per_call[c] / max(1, count.get(c, 1)) for c in per_call}}
+    calls = sorted(set(out["FETCH_SIZE"]["bytes_per_call"]) | set(out["WRITE_SIZE"]["bytes_per_call"]))
+    summary = {
+        "workload": wl.name,
+        "source_sha256_16": source_hash(),
+        "copy_probe_bytes": COPY_PROBE_BYTES,
+        "fetch_factor": out["FETCH_SIZE"]["factor"],
+        "write_factor": out["WRITE_SIZE"]["factor"],
+        "bytes_per_launch": {c: out["FETCH_SIZE"]["bytes_per_call"].get(c, 0.0) +
+                             out["WRITE_SIZE"]["bytes_per_call"].get(c, 0.0) for c in calls},
+        "fetch_bytes_per_launch": out["FETCH_SIZE"]["bytes_per_call"],
+        "write_bytes_per_launch": out["WRITE_SIZE"]["bytes_per_call"],
+    }
+    return summary
 
 
 def cpu_baseline(wl, min_seconds=10.0):
@@ -90,7 +149,20 @@ def main():
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a plain device copy of the step's input size "
                          "(calibrates rocprofv3 byte counters)")
+    ap.add_argument("--summarize-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="turn two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) of "
+                         "'bench.py --copy-probe' into profiles/traffic_<workload>.json")
     args = ap.parse_args()
+    if args.summarize_traffic:
+        import wtconv_inputs as wi
+        wl = wi.WORKLOADS[args.workload]
+        act = wl.N * (4 if wl.dtype == "f32" else 2)
+        summ = summarize_traffic(args.summarize_traffic[0], args.summarize_traffic[1], wl, act)
+        path = TRAFFIC_SUMMARY.format(workload=wl.name)
+        with open(path, "w") as f:
+            json.dump(summ, f, indent=1, sort_keys=True)
+        print(json.dumps(summ, indent=1, sort_keys=True))
+        return
     if args.gpus != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path "
               "(--gpus %d requested)" % args.gpus, file=sys.stderr)
@@ -154,11 +226,12 @@ def main():
     avg_ms = {k: sum(v) / len(v) for k, v in per.items()}
 
     if args.copy_probe:
-        src = sets[0]["x"]
+        src = torch.ones(COPY_PROBE_BYTES // 4, dtype=torch.float32, device=dev)
         dst = torch.empty_like(src)
         for _ in range(3):
             dst.copy_(src)
         torch.cuda.synchronize()
+        del src, dst
 
     ms_step = elapsed * 1e3 / args.steps
     value = wl.B * args.steps / elapsed
