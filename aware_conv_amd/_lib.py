@@ -41,11 +41,13 @@ lib.wtconv_bwd_input.argtypes = [_sp] + [_vp] * 6 + [_vp, ctypes.c_size_t, _vp]
 lib.wtconv_bwd_input.restype = ctypes.c_int
 lib.wtconv_bwd_weight.argtypes = [_sp] + [_vp] * 12 + [_vp, ctypes.c_size_t, _vp]
 lib.wtconv_bwd_weight.restype = ctypes.c_int
+lib.wtconv_bwd.argtypes = [_sp] + [_vp] * 13 + [_vp, ctypes.c_size_t, _vp]
+lib.wtconv_bwd.restype = ctypes.c_int
 lib.wtconv_strerror.argtypes = [ctypes.c_int]
 lib.wtconv_strerror.restype = ctypes.c_char_p
 
 EXPORTED = ("wtconv_workspace_size", "wtconv_fwd", "wtconv_bwd_input",
-            "wtconv_bwd_weight", "wtconv_strerror")
+            "wtconv_bwd_weight", "wtconv_bwd", "wtconv_strerror")
 
 
 class WTConvError(RuntimeError):
@@ -136,17 +138,37 @@ def wtconv_bwd_input(dy, w_base, s_base, w_wav, s_wav, dx=None,
 GRAD_NAMES = ("dw_base", "db_base", "ds_base", "dw_wav", "ds_wav")
 
 
+def _grads(w_base, b_base, s_base, w_wav, s_wav):
+    return {"dw_base": torch.empty_like(w_base), "db_base": torch.empty_like(b_base),
+            "ds_base": torch.empty_like(s_base), "dw_wav": torch.empty_like(w_wav),
+            "ds_wav": torch.empty_like(s_wav)}
+
+
 def wtconv_bwd_weight(x, dy, w_base, b_base, s_base, w_wav, s_wav, grads=None,
                       workspace=None, stream=None):
     """Parameter gradients; returns a dict keyed by GRAD_NAMES."""
     s = shape_of(x, w_wav)
     if grads is None:
-        grads = {"dw_base": torch.empty_like(w_base), "db_base": torch.empty_like(b_base),
-                 "ds_base": torch.empty_like(s_base), "dw_wav": torch.empty_like(w_wav),
-                 "ds_wav": torch.empty_like(s_wav)}
+        grads = _grads(w_base, b_base, s_base, w_wav, s_wav)
     ws, nws = _workspace(s, x.device, workspace)
     _check(lib.wtconv_bwd_weight(
         ctypes.byref(s), _ptr(x), _ptr(dy), _ptr(w_base), _ptr(b_base), _ptr(s_base),
         _ptr(w_wav), _ptr(s_wav), *[_ptr(grads[n]) for n in GRAD_NAMES],
         _ptr(ws), nws, _stream(stream, x.device)), "wtconv_bwd_weight")
     return grads
+
+
+def wtconv_bwd(x, dy, w_base, b_base, s_base, w_wav, s_wav, dx=None, grads=None,
+               workspace=None, stream=None):
+    """Input and parameter gradients in one call; returns (dx, grads dict)."""
+    s = shape_of(x, w_wav)
+    if dx is None:
+        dx = torch.empty_like(dy)
+    if grads is None:
+        grads = _grads(w_base, b_base, s_base, w_wav, s_wav)
+    ws, nws = _workspace(s, x.device, workspace)
+    _check(lib.wtconv_bwd(
+        ctypes.byref(s), _ptr(x), _ptr(dy), _ptr(w_base), _ptr(b_base), _ptr(s_base),
+        _ptr(w_wav), _ptr(s_wav), _ptr(dx), *[_ptr(grads[n]) for n in GRAD_NAMES],
+        _ptr(ws), nws, _stream(stream, x.device)), "wtconv_bwd")
+    return dx, grads

@@ -98,6 +98,49 @@ int apply(const wtconv_shape* s, const void* in, const void* w_base, const void*
     return hip_status(wtc::tile_apply(*s, in, p, out, flip, workspace, st));
 }
 
+// Shared by the weight gradient and the fused backward (dx != NULL).
+int backward(const wtconv_shape* s, const void* x, const void* dy, const void* w_base,
+             const void* b_base, const void* s_base, const void* w_wav, const void* s_wav,
+             void* dx, void* dw_base, void* db_base, void* ds_base, void* dw_wav,
+             void* ds_wav, void* workspace, size_t ws_bytes, void* stream, bool fused) {
+    int rc = check_shape(s);
+    if (rc) return rc;
+    rc = check_params(s, w_base, b_base, s_base, w_wav, s_wav);
+    if (rc) return rc;
+    if (s->C == 0) return WTCONV_OK;
+    if (!dw_base || !db_base || !ds_base || !dw_wav || !ds_wav) return WTCONV_ERR_NULL;
+    const size_t e = elem_size(s->dtype);
+    if (!aligned(dw_base, e) || !aligned(db_base, e) || !aligned(ds_base, e) ||
+        !aligned(dw_wav, e) || !aligned(ds_wav, e))
+        return WTCONV_ERR_ALIGN;
+    Params p{w_base, b_base, s_base, w_wav, s_wav};
+    Grads g{dw_base, db_base, ds_base, dw_wav, ds_wav};
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (empty_act(s)) return hip_status(wtc::zero_grads(*s, p, g, st));
+    if (!x || !dy || (fused && !dx)) return WTCONV_ERR_NULL;
+    if (!aligned(x, 16) || !aligned(dy, 16) || (fused && !aligned(dx, 16)))
+        return WTCONV_ERR_ALIGN;
+    if (fused && (overlap(dx, dy, act_bytes(s)) || overlap(dx, x, act_bytes(s))))
+        return WTCONV_ERR_ALIAS;
+    rc = check_supported(s);
+    if (rc) return rc;
+    const size_t need = workspace_bytes(s);
+    if (ws_bytes < need) return WTCONV_ERR_WORKSPACE;
+    if (need > 0 && !workspace) return WTCONV_ERR_NULL;
+    if (need > 0 && !aligned(workspace, 16)) return WTCONV_ERR_ALIGN;
+    if (use_plane(s)) {
+        if (fused) return hip_status(wtc::plane_bwd(*s, x, dy, p, dx, g, workspace, st));
+        return hip_status(wtc::plane_bwd_weight(*s, x, dy, p, g, workspace, st));
+    }
+    // tiles of large planes: the input gradient, then the weight gradient,
+    // one after the other on the stream (both use the workspace)
+    if (fused) {
+        const int r = hip_status(wtc::tile_apply(*s, dy, p, dx, true, workspace, st));
+        if (r) return r;
+    }
+    return hip_status(wtc::tile_bwd_weight(*s, x, dy, p, g, workspace, st));
+}
+
 }  // namespace
 
 extern "C" {
@@ -133,30 +176,16 @@ int wtconv_bwd_weight(const wtconv_shape* s, const void* x, const void* dy, cons
                       const void* s_wav, void* dw_base, void* db_base, void* ds_base,
                       void* dw_wav, void* ds_wav, void* workspace, size_t ws_bytes,
                       void* stream) {
-    int rc = check_shape(s);
-    if (rc) return rc;
-    rc = check_params(s, w_base, b_base, s_base, w_wav, s_wav);
-    if (rc) return rc;
-    if (s->C == 0) return WTCONV_OK;
-    if (!dw_base || !db_base || !ds_base || !dw_wav || !ds_wav) return WTCONV_ERR_NULL;
-    const size_t e = elem_size(s->dtype);
-    if (!aligned(dw_base, e) || !aligned(db_base, e) || !aligned(ds_base, e) ||
-        !aligned(dw_wav, e) || !aligned(ds_wav, e))
-        return WTCONV_ERR_ALIGN;
-    Params p{w_base, b_base, s_base, w_wav, s_wav};
-    Grads g{dw_base, db_base, ds_base, dw_wav, ds_wav};
-    hipStream_t st = static_cast<hipStream_t>(stream);
-    if (empty_act(s)) return hip_status(wtc::zero_grads(*s, p, g, st));
-    if (!x || !dy) return WTCONV_ERR_NULL;
-    if (!aligned(x, 16) || !aligned(dy, 16)) return WTCONV_ERR_ALIGN;
-    rc = check_supported(s);
-    if (rc) return rc;
-    const size_t need = workspace_bytes(s);
-    if (ws_bytes < need) return WTCONV_ERR_WORKSPACE;
-    if (need > 0 && !workspace) return WTCONV_ERR_NULL;
-    if (need > 0 && !aligned(workspace, 16)) return WTCONV_ERR_ALIGN;
-    if (use_plane(s)) return hip_status(wtc::plane_bwd_weight(*s, x, dy, p, g, workspace, st));
-    return hip_status(wtc::tile_bwd_weight(*s, x, dy, p, g, workspace, st));
+    return backward(s, x, dy, w_base, b_base, s_base, w_wav, s_wav, nullptr, dw_base, db_base,
+                    ds_base, dw_wav, ds_wav, workspace, ws_bytes, stream, false);
+}
+
+int wtconv_bwd(const wtconv_shape* s, const void* x, const void* dy, const void* w_base,
+               const void* b_base, const void* s_base, const void* w_wav, const void* s_wav,
+               void* dx, void* dw_base, void* db_base, void* ds_base, void* dw_wav,
+               void* ds_wav, void* workspace, size_t ws_bytes, void* stream) {
+    return backward(s, x, dy, w_base, b_base, s_base, w_wav, s_wav, dx, dw_base, db_base,
+                    ds_base, dw_wav, ds_wav, workspace, ws_bytes, stream, true);
 }
 
 const char* wtconv_strerror(int code) {

@@ -39,6 +39,9 @@ hipError_t plane_apply(const wtconv_shape& s, const void* in,
 hipError_t plane_bwd_weight(const wtconv_shape& s, const void* x,
                             const void* dy, const Params& p, const Grads& g,
                             void* workspace, hipStream_t stream);
+// Input gradient and parameter gradients in one pass over x and dy.
+hipError_t plane_bwd(const wtconv_shape& s, const void* x, const void* dy, const Params& p,
+                     void* dx, const Grads& g, void* workspace, hipStream_t stream);
 // Zero parameter gradients (empty batch or empty planes).
 hipError_t zero_grads(const wtconv_shape& s, const Params& p, const Grads& g,
                       hipStream_t stream);

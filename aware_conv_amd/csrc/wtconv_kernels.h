@@ -556,10 +556,12 @@ __device__ __forceinline__ int level_pitch(int lvl) {
     return by_level<G>(lvl, [&](auto lc) { return G::pitch(decltype(lc)::value); });
 }
 
-// acc[q][j] = sum_{u,v} w[u*K+v] * src[(q+u)*pitch + j+v].
-template <int K, int Q, int R>
+// acc[q][j] = sum_{u,v} w[u*K+v] * src[(q+u)*pitch + j+v].  With CAPTURE the
+// window's centre, the tile's own input values, is kept in ctr[q][j].
+template <int K, int Q, int R, bool CAPTURE = false>
 __device__ __forceinline__ void conv_tile(const float* src, int pitch, const float (&w)[K * K],
-                                          float init, float (&acc)[Q][R]) {
+                                          float init, float (&acc)[Q][R],
+                                          float (*ctr)[R] = nullptr) {
 #pragma unroll
     for (int q = 0; q < Q; ++q)
 #pragma unroll
@@ -570,6 +572,12 @@ __device__ __forceinline__ void conv_tile(const float* src, int pitch, const flo
         const float* row = src + ir * pitch;
 #pragma unroll
         for (int m = 0; m < R + K - 1; ++m) in[m] = row[m];
+        if constexpr (CAPTURE) {
+            constexpr int p = K / 2;
+            if (ir >= p && ir < p + Q)
+#pragma unroll
+                for (int j = 0; j < R; ++j) ctr[ir - p][j] = in[j + p];
+        }
 #pragma unroll
         for (int q = 0; q < Q; ++q) {
             const int u = ir - q;
@@ -858,6 +866,42 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(
     if (pend_b0 >= 0) store_out<G, T>(lds, out, pend_b0, B, C, pend_c, tid);
 }
 
+// Fixed-order workgroup reduction of the lanes' tap accumulators into one
+// partial row [G_b (KK), sum dy, G[l][s] (4 L KK)], zero-padded to npart
+// floats: each entry sums the lanes of its (array, subband) in lane order.
+// Overwrites LDS from `lds` on; the caller has synchronised the workgroup.
+template <class G>
+__device__ __forceinline__ void reduce_row(float* lds, const float (&acc)[G::KK], float sdy,
+                                           float* __restrict__ row, int npart, int tid) {
+    constexpr int KK = G::KK, RS = KK + 1;
+    float* red = lds;  // [NT][KK + 1]
+#pragma unroll
+    for (int t = 0; t < KK; ++t) red[tid * RS + t] = acc[t];
+    red[tid * RS + KK] = sdy;
+    __syncthreads();
+    for (int o = tid; o < npart; o += G::NT) {
+        float s = 0.f;
+        if (o <= KK) {
+            for (int t = G::jstart(0); t < G::jstart(1); ++t) s += red[t * RS + o];
+        } else if (o < G::NPART) {
+            const int r = o - KK - 1, ls = r / KK, tap = r % KK;
+            const int l = (ls >> 2) + 1, sb = ls & 3;
+            by_level<G>(l, [&](auto lc) {
+                constexpr int lv = decltype(lc)::value;
+                if constexpr (lv > 0) {
+                    constexpr int per = G::NS(lv) * G::NG(lv);
+                    for (int pl = 0; pl < G::P; ++pl) {
+                        const int t0 = G::jstart(lv) + (pl * 4 + sb) * per;
+                        for (int t = t0; t < t0 + per; ++t) s += red[t * RS + tap];
+                    }
+                }
+                return 0;
+            });
+        }
+        row[o] = s;
+    }
+}
+
 // Weight-gradient partial sums of channel blockIdx.x % C over the groups of
 // chunk blockIdx.x / C: one row of G::NPART floats per workgroup,
 // [G_b (KK), sum dy, G[l][s] (4 L KK)].
@@ -948,34 +992,134 @@ __global__ __launch_bounds__(NT) void k_plane_bww(
         __syncthreads();
     }
 
-    // fixed-order workgroup reduction: lane sums of each (array, subband)
-    float* red = lds;  // [NT][KK + 1]
-    constexpr int RS = KK + 1;
-#pragma unroll
-    for (int t = 0; t < KK; ++t) red[tid * RS + t] = acc[t];
-    red[tid * RS + KK] = sdy;
-    __syncthreads();
-    for (int o = tid; o < G::NPART; o += NT) {
-        float s = 0.f;
-        if (o <= KK) {
-            for (int t = G::jstart(0); t < G::jstart(1); ++t) s += red[t * RS + o];
-        } else {
-            const int r = o - KK - 1, ls = r / KK, tap = r % KK;
-            const int l = (ls >> 2) + 1, sb = ls & 3;
-            by_level<G>(l, [&](auto lc) {
-                constexpr int lv = decltype(lc)::value;
-                if constexpr (lv > 0) {
-                    constexpr int per = G::NS(lv) * G::NG(lv);
-                    for (int pl = 0; pl < P; ++pl) {
-                        const int t0 = G::jstart(lv) + (pl * 4 + sb) * per;
-                        for (int t = t0; t < t0 + per; ++t) s += red[t * RS + tap];
-                    }
-                }
-                return 0;
-            });
-        }
-        part[(size_t(chunk) * C + c) * G::NPART + o] = s;
+    reduce_row<G>(lds, acc, sdy, part + (size_t(chunk) * C + c) * G::NPART, G::NPART, tid);
+}
+
+// Offset of the dy side of the fused backward's LDS: a second copy of the
+// x-side layout, started on bank 0 so that both windows of a tile fall on
+// the same banks.
+template <class G>
+constexpr int bwd_dy_base() { return cdiv(G::side, 32) * 32; }
+template <class G>
+constexpr size_t bwd_lds_bytes() {
+    const size_t a = sizeof(float) * (bwd_dy_base<G>() + G::side + G::NWF);
+    const size_t b = sizeof(float) * G::NT * (G::KK + 1);
+    return a > b ? a : b;
+}
+
+// Fused backward: input gradient and weight-gradient partials of channel
+// blockIdx.x % C over the groups of chunk blockIdx.x / C, reading x and dy
+// once.  dy and x are analysed side by side in LDS; each lane reads the dy
+// window of its tile for the rotated-filter conv of the input gradient, keeps
+// the window's centre (its tile of dy, or of V^l_s) and correlates it with
+// the x window of the same tile for the weight gradient.  The input gradient
+// then goes through the same synthesis and deferred store as the forward.
+template <int K, int L, int H, int W, int P, int NT, typename T>
+__global__ __launch_bounds__(NT) void k_plane_bwd(
+    const T* __restrict__ x, const T* __restrict__ dy, const T* __restrict__ wb,
+    const T* __restrict__ sb, const T* __restrict__ ww, const T* __restrict__ sw,
+    T* __restrict__ dx, float* __restrict__ part, int B, int C, int gpw) {
+    using G = Geo<K, L, H, W, P, NT>;
+    using F = Fetch<G, T>;
+    constexpr int KK = G::KK, Q = G::Q, R = G::R, DY = bwd_dy_base<G>();
+    extern __shared__ float lds[];
+    float* ldy = lds + DY;
+    float* wf = ldy + G::side;
+    const int tid = threadIdx.x;
+    const int c = blockIdx.x % C;
+    const int chunk = blockIdx.x / C;
+    const int ngroups = cdiv(B, P);
+    const int g0 = chunk * gpw;
+    const int g1 = min(g0 + gpw, ngroups);
+    F fx, fd;
+    if (g0 < g1) {
+        fx.issue(x, g0 * P, B, C, c, tid);
+        fd.issue(dy, g0 * P, B, C, c, tid);
     }
+    for (int i = tid; i < DY + G::side; i += NT) lds[i] = 0.f;
+    fold_weights<G, T, true>(wf, wb, wb, sb, ww, sw, C, c, tid);
+    __syncthreads();
+
+    const Job job = decode_job<G>(tid);
+    const int wsrc = job.lvl == 0 ? 0 : KK * (1 + (job.lvl - 1) * 4 + job.s);
+    const int win = window_index<G>(job);
+    const int pitch = level_pitch<G>(job.lvl);
+    const int hrows = by_level<G>(job.lvl, [](auto lc) { return G::hl(decltype(lc)::value); });
+    const int wcols = by_level<G>(job.lvl, [](auto lc) { return G::wl(decltype(lc)::value); });
+    const int nrows = min(Q, hrows - job.grp * Q);
+    const int ncols = min(R, wcols - job.strip * R);
+    const bool full = nrows == Q && ncols == R;
+    const int dst = win + G::p * pitch + G::p;
+    float w[KK];
+#pragma unroll
+    for (int t = 0; t < KK; ++t) w[t] = wf[wsrc + t];
+    float gacc[KK];
+#pragma unroll
+    for (int t = 0; t < KK; ++t) gacc[t] = 0.f;
+    float sdy = 0.f;
+
+    int pend_b0 = -1;
+    for (int g = g0; g < g1; ++g) {
+        const int b0 = g * P;
+        wait_vmem();
+        if (pend_b0 >= 0) {
+            store_out<G, T>(ldy, dx, pend_b0, B, C, c, tid);
+            __syncthreads();
+        }
+        fx.template commit<true, false>(lds, tid);
+        fd.template commit<true, false>(ldy, tid);
+        __syncthreads();
+        static_for<F::LEVELS + 1, L + 1>([&](auto lc) {
+            analysis_level<G, decltype(lc)::value, false>(lds, tid);
+            analysis_level<G, decltype(lc)::value, false>(ldy, tid);
+            __syncthreads();
+        });
+        float acc[Q][R];
+        if (job.on) {
+            // outside the level's core both windows read zeros, so the
+            // centre of a partial tile needs no mask
+            float d[Q][R];
+            conv_tile<K, Q, R, true>(ldy + win, pitch, w, 0.f, acc, d);
+            if (job.lvl == 0)
+#pragma unroll
+                for (int qq = 0; qq < Q; ++qq)
+#pragma unroll
+                    for (int j = 0; j < R; ++j) sdy += d[qq][j];
+            corr_tile<K, Q, R>(d, lds + win, pitch, gacc);
+        }
+        if (g + 1 < g1) {
+            fx.issue(x, b0 + P, B, C, c, tid);
+            fd.issue(dy, b0 + P, B, C, c, tid);
+        }
+        __syncthreads();
+        if (job.on) {
+            if (full) {
+#pragma unroll
+                for (int qq = 0; qq < Q; ++qq)
+#pragma unroll
+                    for (int j = 0; j < R; ++j) ldy[dst + qq * pitch + j] = acc[qq][j];
+            } else {
+#pragma unroll
+                for (int qq = 0; qq < Q; ++qq)
+#pragma unroll
+                    for (int j = 0; j < R; ++j)
+                        if (qq < nrows && j < ncols) ldy[dst + qq * pitch + j] = acc[qq][j];
+            }
+        }
+        __syncthreads();
+        static_for<0, L - 2>([&](auto lc) {
+            cascade_level<G, L - decltype(lc)::value>(ldy, tid);
+            __syncthreads();
+        });
+        final_to_lds<G, T>(ldy, tid);
+        pend_b0 = b0;
+        __syncthreads();
+    }
+    if (pend_b0 >= 0) {
+        store_out<G, T>(ldy, dx, pend_b0, B, C, c, tid);
+        __syncthreads();
+    }
+    reduce_row<G>(lds, gacc, sdy, part + (size_t(chunk) * C + c) * G::NPART, G::NPART, tid);
 }
 
 // Sum the partial rows of every chunk in order and apply the chain rule
@@ -1258,31 +1402,7 @@ __global__ __launch_bounds__(NT) void k_tile_bww(const T* __restrict__ x,
         __syncthreads();
     }
 
-    float* red = lds;  // [NT][KK + 1]
-    constexpr int RS = KK + 1;
-#pragma unroll
-    for (int t = 0; t < KK; ++t) red[tid * RS + t] = acc[t];
-    red[tid * RS + KK] = sdy;
-    __syncthreads();
-    for (int o = tid; o < npart; o += NT) {
-        float sum = 0.f;
-        if (o <= KK) {
-            for (int t = G::jstart(0); t < G::jstart(1); ++t) sum += red[t * RS + o];
-        } else if (o < G::NPART) {
-            const int r = o - KK - 1, ls = r / KK, tap = r % KK;
-            const int l = (ls >> 2) + 1, sb = ls & 3;
-            by_level<G>(l, [&](auto lc) {
-                constexpr int lv = decltype(lc)::value;
-                if constexpr (lv > 0) {
-                    constexpr int per = G::NS(lv) * G::NG(lv);
-                    const int t0 = G::jstart(lv) + sb * per;
-                    for (int t = t0; t < t0 + per; ++t) sum += red[t * RS + tap];
-                }
-                return 0;
-            });
-        }
-        part[(size_t(chunk) * C + c) * npart + o] = sum;
-    }
+    reduce_row<G>(lds, acc, sdy, part + (size_t(chunk) * C + c) * npart, npart, tid);
 }
 }  // namespace dev
 }  // namespace wtc

@@ -11,19 +11,26 @@ struct Variant {
     const void* fwd;
     const void* bwi;
     const void* bww;
-    size_t lds_apply, lds_bww;
+    const void* bwd;  // fused backward, NULL where its LDS does not fit
+    size_t lds_apply, lds_bww, lds_bwd;
 };
+
+constexpr size_t kMaxLds = 163840;  // LDS of one gfx950 compute unit
 
 template <int K, int L, int H, int W, int P, int NT, typename T>
 Variant make_variant(int dtype) {
     using G = Geo<K, L, H, W, P, NT>;
     const size_t la = apply_lds_bytes<G>();
     const size_t lb = bww_lds_bytes<G>();
+    constexpr size_t ld = bwd_lds_bytes<G>();
+    const void* fused = nullptr;
+    if constexpr (ld <= kMaxLds)
+        fused = reinterpret_cast<const void*>(&k_plane_bwd<K, L, H, W, P, NT, T>);
     return Variant{K, L, H, W, dtype, P, NT,
                    reinterpret_cast<const void*>(&k_plane_apply<K, L, H, W, P, NT, T, false>),
                    reinterpret_cast<const void*>(&k_plane_apply<K, L, H, W, P, NT, T, true>),
                    reinterpret_cast<const void*>(&k_plane_bww<K, L, H, W, P, NT, T>),
-                   la, lb};
+                   fused, la, lb, ld};
 }
 
 // (K, L, H, W, planes per group, threads).  The ConvNeXt-T stage shapes
@@ -158,6 +165,32 @@ hipError_t plane_bwd_weight(const wtconv_shape& s, const void* x, const void* dy
     void* args[] = {&x, &dy, &part, &B, &C, &gpw};
     e = hipLaunchKernel(v->bww, dim3(unsigned(nchunk) * unsigned(s.C)), dim3(v->NT), args,
                         v->lds_bww, stream);
+    if (e == hipSuccess) e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    return finalize_grads(s, part, nchunk, p, g, stream);
+}
+
+hipError_t plane_bwd(const wtconv_shape& s, const void* x, const void* dy, const Params& p,
+                     void* dx, const Grads& g, void* workspace, hipStream_t stream) {
+    const Variant* v = find_variant(s);
+    if (!v) return hipErrorInvalidValue;
+    if (!v->bwd) {
+        hipError_t e = plane_apply(s, dy, p, dx, true, stream);
+        if (e != hipSuccess) return e;
+        return plane_bwd_weight(s, x, dy, p, g, workspace, stream);
+    }
+    hipError_t e = prepare(v->bwd, v->lds_bwd);
+    if (e != hipSuccess) return e;
+    const int nchunk = bww_chunks(s, v->P, resident_wgs(v->bwd, v->NT, v->lds_bwd));
+    int gpw = cdiv(cdiv(s.B, v->P), nchunk), B = s.B, C = s.C;
+    float* part = static_cast<float*>(workspace);
+    const void* wb = p.w_base;
+    const void* sb = p.s_base;
+    const void* ww = p.w_wav;
+    const void* sw = p.s_wav;
+    void* args[] = {&x, &dy, &wb, &sb, &ww, &sw, &dx, &part, &B, &C, &gpw};
+    e = hipLaunchKernel(v->bwd, dim3(unsigned(nchunk) * unsigned(s.C)), dim3(v->NT), args,
+                        v->lds_bwd, stream);
     if (e == hipSuccess) e = hipGetLastError();
     if (e != hipSuccess) return e;
     return finalize_grads(s, part, nchunk, p, g, stream);

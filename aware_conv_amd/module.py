@@ -5,9 +5,10 @@ from . import _lib
 
 
 class WTConvFunction(torch.autograd.Function):
-    """Forward through ``wtconv_fwd``; backward through ``wtconv_bwd_input``
-    and ``wtconv_bwd_weight``.  Only x and the parameters are saved: the
-    subband tensors are recomputed by the backward kernels."""
+    """Forward through ``wtconv_fwd``; backward through ``wtconv_bwd`` (input
+    and parameter gradients from one pass), or the one of ``wtconv_bwd_input``
+    and ``wtconv_bwd_weight`` that is needed.  Only x and the parameters are
+    saved: the subband tensors are recomputed by the backward kernels."""
 
     @staticmethod
     def forward(ctx, x, w_base, b_base, s_base, w_wav, s_wav):
@@ -19,10 +20,13 @@ class WTConvFunction(torch.autograd.Function):
         x, w_base, b_base, s_base, w_wav, s_wav = ctx.saved_tensors
         dy = dy.contiguous()
         dx = None
-        if ctx.needs_input_grad[0]:
-            dx = _lib.wtconv_bwd_input(dy, w_base, s_base, w_wav, s_wav)
         g = {n: None for n in _lib.GRAD_NAMES}
-        if any(ctx.needs_input_grad[1:]):
+        want_dx, want_g = ctx.needs_input_grad[0], any(ctx.needs_input_grad[1:])
+        if want_dx and want_g:
+            dx, g = _lib.wtconv_bwd(x, dy, w_base, b_base, s_base, w_wav, s_wav)
+        elif want_dx:
+            dx = _lib.wtconv_bwd_input(dy, w_base, s_base, w_wav, s_wav)
+        elif want_g:
             g = _lib.wtconv_bwd_weight(x, dy, w_base, b_base, s_base, w_wav, s_wav)
         return dx, g["dw_base"], g["db_base"], g["ds_base"], g["dw_wav"], g["ds_wav"]
 

@@ -1,10 +1,12 @@
 """Throughput of the fused WTConv training step on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload stage1]
+                    [--backward fused|split]
 
-A step is one pass of the whole hot path over one batch: wtconv_fwd,
-wtconv_bwd_input and wtconv_bwd_weight on synthetic inputs already resident in
-device memory.  W untimed steps, then exactly K timed steps bracketed by
+A step is one pass of the whole hot path over one batch on synthetic inputs
+already resident in device memory: wtconv_fwd, then the backward, by default
+the fused wtconv_bwd (input and parameter gradients reading x and dy once),
+with --backward split the two calls wtconv_bwd_input and wtconv_bwd_weight.  W untimed steps, then exactly K timed steps bracketed by
 device synchronisation; value = images per second over the K steps.  Each
 step reads its own set of buffers, rotating over enough sets that no step
 finds the previous step's tensors in the 256 MB last-level cache.
@@ -35,7 +37,7 @@ PEAK_FP32_VALU_TFLOPS = 78.6    # 256 CU * 4 SIMD * 16 lanes * 2 FLOP * 2.4 GHz,
 PEAK_FP32_PACKED_TFLOPS = 157.3  # the same with packed FP32 (not used by these kernels)
 PEAK_HBM_GBS = 8000.0
 KERNEL_SOURCES = os.path.join(ROOT, "aware_conv_amd", "csrc")
-TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "traffic_{workload}.json")
+TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "traffic_{workload}_{backward}.json")
 COPY_PROBE_BYTES = 3 << 28  # 768 MiB: larger than any other copy of a bench run
 
 
@@ -61,19 +63,31 @@ def source_hash():
     return h.hexdigest()[:16]
 
 
-def call_of(kernel_name):
+def call_of(kernel_name, fused):
     """Entry point a profiled kernel belongs to, or None."""
     n = kernel_name
+    c = None
     if "k_plane_apply" in n or "k_tile_apply" in n or "k_deep_apply" in n:
         # template argument FLIP: ..., false> forward, ..., true> input gradient
         head = n.split("(")[0]
-        return "wtconv_bwd_input" if head.rstrip("> ").endswith("true") else "wtconv_fwd"
-    if "k_plane_bww" in n or "k_tile_bww" in n or "k_deep_bww" in n or "k_bww_final" in n:
-        return "wtconv_bwd_weight"
-    return None
+        c = "wtconv_bwd_input" if head.rstrip("> ").endswith("true") else "wtconv_fwd"
+    elif "k_plane_bww" in n or "k_tile_bww" in n or "k_deep_bww" in n or "k_bww_final" in n:
+        c = "wtconv_bwd_weight"
+    elif "k_plane_bwd" in n:
+        c = "wtconv_bwd"
+    if fused and c in ("wtconv_bwd_input", "wtconv_bwd_weight"):
+        c = "wtconv_bwd"
+    return c
 
 
-def summarize_traffic(fetch_dir, write_dir, wl, act_bytes):
+def is_step_marker(kernel_name):
+    """The forward's main kernel: launched exactly once per step."""
+    head = kernel_name.split("(")[0]
+    return (("k_plane_apply" in head or "k_tile_apply" in head) and
+            head.rstrip("> ").endswith("false"))
+
+
+def summarize_traffic(fetch_dir, write_dir, wl, act_bytes, fused):
     """HBM bytes per entry-point call from two rocprofv3 --pmc runs (FETCH_SIZE,
     WRITE_SIZE, KiB per dispatch), each scaled by what the same counter reads
     for the plain device copy of act_bytes that --copy-probe performs."""
@@ -90,19 +104,19 @@ def summarize_traffic(fetch_dir, write_dir, wl, act_bytes):
         kib_copy = sum(copies) / len(copies)
         factor = COPY_PROBE_BYTES / (kib_copy * 1024.0)
         per_call = {}
-        count = {}
+        steps = sum(1 for r in rows if is_step_marker(r["Kernel_Name"]))
         for r in rows:
-            c = call_of(r["Kernel_Name"])
+            c = call_of(r["Kernel_Name"], fused)
             if c is None:
                 continue
             per_call[c] = per_call.get(c, 0.0) + float(r["Counter_Value"]) * 1024.0 * factor
-            if "final" not in r["Kernel_Name"] and "deep" not in r["Kernel_Name"]:
-                count[c] = count.get(c, 0) + 1
+        # every step calls each entry point once
         out[counter] = {"factor": factor, "copy_kib": kib_copy,
-                        "bytes_per_call": {c: per_call[c] / max(1, count.get(c, 1)) for c in per_call}}
+                        "bytes_per_call": {c: per_call[c] / max(1, steps) for c in per_call}}
     calls = sorted(set(out["FETCH_SIZE"]["bytes_per_call"]) | set(out["WRITE_SIZE"]["bytes_per_call"]))
     summary = {
         "workload": wl.name,
+        "backward": "fused" if fused else "split",
         "source_sha256_16": source_hash(),
         "copy_probe_bytes": COPY_PROBE_BYTES,
         "fetch_factor": out["FETCH_SIZE"]["factor"],
@@ -145,6 +159,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="stage1")
     ap.add_argument("--sets", type=int, default=0, help="buffer sets to rotate (0 = auto)")
+    ap.add_argument("--backward", choices=("fused", "split"), default="fused",
+                    help="fused: wtconv_bwd; split: wtconv_bwd_input + wtconv_bwd_weight")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a plain device copy of the step's input size "
@@ -157,8 +173,10 @@ def main():
         import wtconv_inputs as wi
         wl = wi.WORKLOADS[args.workload]
         act = wl.N * (4 if wl.dtype == "f32" else 2)
-        summ = summarize_traffic(args.summarize_traffic[0], args.summarize_traffic[1], wl, act)
-        path = TRAFFIC_SUMMARY.format(workload=wl.name)
+        fused = args.backward == "fused"
+        summ = summarize_traffic(args.summarize_traffic[0], args.summarize_traffic[1], wl, act,
+                                 fused)
+        path = TRAFFIC_SUMMARY.format(workload=wl.name, backward=args.backward)
         with open(path, "w") as f:
             json.dump(summ, f, indent=1, sort_keys=True)
         print(json.dumps(summ, indent=1, sort_keys=True))
@@ -195,34 +213,40 @@ def main():
     ws = torch.empty(max(16, L.wtconv_workspace_size(shape)), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev)
 
+    fused = args.backward == "fused"
+    calls = (["wtconv_fwd", "wtconv_bwd"] if fused else
+             ["wtconv_fwd", "wtconv_bwd_input", "wtconv_bwd_weight"])
+
     def step(t, ev=None):
         p = (t["w_base"], t["b_base"], t["s_base"], t["w_wav"], t["s_wav"])
+        run = {
+            "wtconv_fwd": lambda: L.wtconv_fwd(t["x"], *p, y=t["y"], workspace=ws, stream=stream),
+            "wtconv_bwd": lambda: L.wtconv_bwd(t["x"], t["dy"], *p, dx=t["dx"], grads=t["g"],
+                                               workspace=ws, stream=stream),
+            "wtconv_bwd_input": lambda: L.wtconv_bwd_input(t["dy"], p[0], p[2], p[3], p[4],
+                                                           dx=t["dx"], workspace=ws,
+                                                           stream=stream),
+            "wtconv_bwd_weight": lambda: L.wtconv_bwd_weight(t["x"], t["dy"], *p, grads=t["g"],
+                                                             workspace=ws, stream=stream),
+        }
+        for i, c in enumerate(calls):
+            if ev is not None:
+                ev[i].record(stream)
+            run[c]()
         if ev is not None:
-            ev[0].record(stream)
-        L.wtconv_fwd(t["x"], *p, y=t["y"], workspace=ws, stream=stream)
-        if ev is not None:
-            ev[1].record(stream)
-        L.wtconv_bwd_input(t["dy"], p[0], p[2], p[3], p[4], dx=t["dx"], workspace=ws, stream=stream)
-        if ev is not None:
-            ev[2].record(stream)
-        L.wtconv_bwd_weight(t["x"], t["dy"], *p, grads=t["g"], workspace=ws, stream=stream)
-        if ev is not None:
-            ev[3].record(stream)
+            ev[len(calls)].record(stream)
 
     for i in range(args.warmup):
         step(sets[i % nsets])
     torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(calls) + 1)]
+           for _ in range(args.steps)]
     t0 = time.perf_counter()
     for i in range(args.steps):
         step(sets[i % nsets], evs[i])
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
-    per = {"wtconv_fwd": [], "wtconv_bwd_input": [], "wtconv_bwd_weight": []}
-    for e in evs:
-        per["wtconv_fwd"].append(e[0].elapsed_time(e[1]))
-        per["wtconv_bwd_input"].append(e[1].elapsed_time(e[2]))
-        per["wtconv_bwd_weight"].append(e[2].elapsed_time(e[3]))
+    per = {c: [e[i].elapsed_time(e[i + 1]) for e in evs] for i, c in enumerate(calls)}
     avg_ms = {k: sum(v) / len(v) for k, v in per.items()}
 
     if args.copy_probe:
@@ -236,19 +260,22 @@ def main():
     ms_step = elapsed * 1e3 / args.steps
     value = wl.B * args.steps / elapsed
     flops_pass = wl.N * conv_flops_per_pixel(wl.L, wl.k)
+    # algorithmic bytes and conv passes of each call: activations read and
+    # written; the input gradient and the weight taps are one pass each
     algo_bytes = {"wtconv_fwd": 2 * act_bytes, "wtconv_bwd_input": 2 * act_bytes,
-                  "wtconv_bwd_weight": 2 * act_bytes}
+                  "wtconv_bwd_weight": 2 * act_bytes, "wtconv_bwd": 3 * act_bytes}
+    passes = {"wtconv_fwd": 1, "wtconv_bwd_input": 1, "wtconv_bwd_weight": 1, "wtconv_bwd": 2}
     dom = max(avg_ms, key=avg_ms.get)
     dur_s = avg_ms[dom] * 1e-3
-    achieved_tf = flops_pass / dur_s / 1e12
+    achieved_tf = passes[dom] * flops_pass / dur_s / 1e12
     traffic = None
-    tpath = TRAFFIC_SUMMARY.format(workload=wl.name)
+    tpath = TRAFFIC_SUMMARY.format(workload=wl.name, backward=args.backward)
     if os.path.exists(tpath):
         with open(tpath) as f:
             tr = json.load(f)
         if tr.get("source_sha256_16") == source_hash() and dom in tr.get("bytes_per_launch", {}):
             traffic = tr["bytes_per_launch"][dom]
-    step_bytes = 6 * act_bytes
+    step_bytes = sum(algo_bytes[c] for c in calls)
     rec = {
         "metric": "fused WTConv fwd+bwd images/s and effective HBM GB/s (% of peak), 1xMI355X",
         "value": round(value, 1),
@@ -263,7 +290,9 @@ def main():
         "dtype": "f32" if wl.dtype == "f32" else "f16 storage, f32 accumulate",
         "data": "synthetic (seeded N(0,1) activations, N(0,0.02^2) filters)",
         "config": {"workload": wl.name, "B": wl.B, "C": wl.C, "H": wl.H, "W": wl.W,
-                   "levels": wl.L, "k": wl.k, "buffer_sets": nsets},
+                   "levels": wl.L, "k": wl.k, "backward": args.backward,
+                   "buffer_sets": nsets},
+        "step_algo_bytes": step_bytes,
         "effective_hbm_gbs": round(step_bytes / (elapsed / args.steps) / 1e9, 1),
         "effective_hbm_frac": round(step_bytes / (elapsed / args.steps) / 1e9 / PEAK_HBM_GBS, 4),
         "per_call_ms": {k: round(v, 5) for k, v in avg_ms.items()},
@@ -277,7 +306,7 @@ def main():
             "traffic": traffic,
             "hbm_gbs": round(algo_bytes[dom] / dur_s / 1e9, 1),
             "hbm_frac": round(algo_bytes[dom] / dur_s / 1e9 / PEAK_HBM_GBS, 4),
-            "flops_per_launch": flops_pass,
+            "flops_per_launch": passes[dom] * flops_pass,
             "algo_bytes_per_launch": algo_bytes[dom],
         },
     }

@@ -80,7 +80,7 @@ typedef struct {
 
 /*
  * Bytes of device workspace the calls below need for shape `s` (the maximum
- * over wtconv_fwd, wtconv_bwd_input and wtconv_bwd_weight); 0 is possible.
+ * over every call below); 0 is possible.
  * Returns WTCONV_OK or a shape error; *bytes is set only on success.
  */
 int wtconv_workspace_size(const wtconv_shape* s, size_t* bytes);
@@ -125,6 +125,23 @@ int wtconv_bwd_weight(const wtconv_shape* s, const void* x, const void* dy,
                       const void* s_wav, void* dw_base, void* db_base,
                       void* ds_base, void* dw_wav, void* ds_wav,
                       void* workspace, size_t ws_bytes, void* stream);
+
+/*
+ * Fused backward: the results of wtconv_bwd_input and wtconv_bwd_weight from
+ * one call that reads x and dy once (the training step's backward, whose
+ * speed-up over the unfused layer gist.science/pt reports under
+ * "Resultados").  Arguments are those of the two calls, dx included: dx
+ * [B][C][H][W] must overlap neither x nor dy; the gradients are overwritten.
+ * Results equal the two separate calls up to floating-point evaluation
+ * order, and the parameter gradients are bitwise reproducible for a given
+ * shape.  Planes handled as tiles (the largest ones) run the two passes one
+ * after the other.  Needs wtconv_workspace_size() bytes of workspace.
+ */
+int wtconv_bwd(const wtconv_shape* s, const void* x, const void* dy,
+               const void* w_base, const void* b_base, const void* s_base,
+               const void* w_wav, const void* s_wav, void* dx, void* dw_base,
+               void* db_base, void* ds_base, void* dw_wav, void* ds_wav,
+               void* workspace, size_t ws_bytes, void* stream);
 
 /* Static description of an error code (never NULL). */
 const char* wtconv_strerror(int code);

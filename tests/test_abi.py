@@ -116,3 +116,24 @@ def test_empty_tensors_need_no_pointers(lb):
     assert fwd(lb, s, x=None, y=None) == 0
     s = good(lb, C=0)
     assert fwd(lb, s, x=None, y=None, params=None) == 0
+
+
+def test_fused_bwd_checks(lb):
+    s = good(lb)
+    need = lb.wtconv_workspace_size(s)
+    f = lb.lib.wtconv_bwd
+    DX = ctypes.c_void_p(0x300000)
+    GR = ctypes.c_void_p(0x400000)
+
+    def call(shape=s, x=FAKE, dy=FAKE2, dx=DX, ws=FAKE, nws=need - 1, grads=GR):
+        return f(ctypes.byref(shape), x, dy, *[FAKE] * 5, dx, *[grads] * 5, ws, nws, None)
+
+    assert call() == -7                     # workspace one byte short
+    assert call(nws=need, ws=None) == -1
+    assert call(dx=None) == -1
+    assert call(grads=None) == -1
+    assert call(dx=MIS) == -6
+    assert call(dx=FAKE) == -9              # dx aliases x
+    assert call(dx=FAKE2) == -9             # dx aliases dy
+    assert call(shape=good(lb, k=2)) == -3
+    assert call(shape=good(lb, H=6, W=6, L=1)) == -8

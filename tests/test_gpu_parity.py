@@ -6,7 +6,10 @@ fp32, 2e-2 for fp16 storage with fp32 accumulation.  For fp16 the oracle gets
 the same fp16-rounded inputs, upcast to fp64.
 
 The named workloads are run at their full sizes, in the launch configuration
-the benchmark uses, and compared with the oracle on every element.
+the benchmark uses, and compared with the oracle on every element.  Every
+case runs both backward forms: the two separate calls and the fused
+wtconv_bwd, whose input gradient must equal the separate call's bit for bit
+(same kernels' arithmetic in the same order).
 """
 import numpy as np
 import pytest
@@ -26,13 +29,16 @@ def lib():
     return _lib
 
 
-def gpu_run(d, dev="cuda"):
+def gpu_run(d, dev="cuda", fused=False):
     L = lib()
     t = {k: v.to(dev) for k, v in d.items()}
-    y = L.wtconv_fwd(t["x"], t["w_base"], t["b_base"], t["s_base"], t["w_wav"], t["s_wav"])
-    dx = L.wtconv_bwd_input(t["dy"], t["w_base"], t["s_base"], t["w_wav"], t["s_wav"])
-    g = L.wtconv_bwd_weight(t["x"], t["dy"], t["w_base"], t["b_base"], t["s_base"],
-                            t["w_wav"], t["s_wav"])
+    p = [t[n] for n in ("w_base", "b_base", "s_base", "w_wav", "s_wav")]
+    y = L.wtconv_fwd(t["x"], *p)
+    if fused:
+        dx, g = L.wtconv_bwd(t["x"], t["dy"], *p)
+    else:
+        dx = L.wtconv_bwd_input(t["dy"], p[0], p[2], p[3], p[4])
+        g = L.wtconv_bwd_weight(t["x"], t["dy"], *p)
     torch.cuda.synchronize()
     out = {"y": y, "dx": dx}
     out.update(g)
@@ -56,13 +62,18 @@ def rel_err(g, o):
 
 
 def assert_parity(d, dtype, label, names=NAMES):
-    g = gpu_run(d)
     o = oracle_run(d)
-    errs = {n: rel_err(g[n], o[n]) for n in names}
-    print("\n%s: %s" % (label, " ".join("%s=%.2e" % kv for kv in errs.items())), flush=True)
-    for n in names:
-        assert np.all(np.isfinite(g[n])), (label, n)
-        assert errs[n] <= TOL[dtype], (label, n, errs[n])
+    runs = {}
+    for fused in (False, True):
+        tag = label + (" fused" if fused else "")
+        print("\ncase %s" % tag, flush=True)
+        g = runs[fused] = gpu_run(d, fused=fused)
+        errs = {n: rel_err(g[n], o[n]) for n in names}
+        print("%s: %s" % (tag, " ".join("%s=%.2e" % kv for kv in errs.items())), flush=True)
+        for n in names:
+            assert np.all(np.isfinite(g[n])), (tag, n)
+            assert errs[n] <= TOL[dtype], (tag, n, errs[n])
+    assert np.array_equal(runs[True]["dx"], runs[False]["dx"]), label
 
 
 @pytest.mark.parametrize("name", ["tiny", "stage1", "stage2", "stage3", "stage1_f16", "highres"])
@@ -152,10 +163,17 @@ def test_outputs_fully_written_and_deterministic():
         assert torch.isfinite(t).all()
     y2 = L.wtconv_fwd(d["x"], *p)
     g2 = L.wtconv_bwd_weight(d["x"], d["dy"], *p)
+    dxf = torch.full_like(d["x"], float("nan"))
+    gf = {n: torch.full_like(t, float("nan")) for n, t in gr.items()}
+    L.wtconv_bwd(d["x"], d["dy"], *p, dx=dxf, grads=gf)
+    dxf2, gf2 = L.wtconv_bwd(d["x"], d["dy"], *p)
     torch.cuda.synchronize()
     assert torch.equal(y, y2)
+    assert torch.equal(dxf, dx) and torch.equal(dxf2, dx)
     for n in L.GRAD_NAMES:
         assert torch.equal(gr[n], g2[n])
+        assert torch.isfinite(gf[n]).all()
+        assert torch.equal(gf[n], gf2[n])
 
 
 def test_input_gradient_is_rotated_forward():
@@ -200,3 +218,27 @@ def test_autograd_module_matches_oracle():
     assert rel_err(x.grad.double().cpu().numpy(), go["dx"]) < 1e-5
     assert rel_err(m.w_wav.grad.double().cpu().numpy(), go["dw_wav"]) < 1e-5
     assert rel_err(m.s_base.grad.double().cpu().numpy(), go["ds_base"]) < 1e-5
+
+
+@pytest.mark.parametrize("which", ["input", "params"])
+def test_autograd_module_partial_backward(which):
+    """Only the input gradient (frozen parameters) or only the parameter
+    gradients (input without grad): the module takes the single call."""
+    from aware_conv_amd import WTConv2d
+    torch.manual_seed(1)
+    m = WTConv2d(8, kernel_size=5, levels=2).cuda()
+    x = torch.randn(2, 8, 32, 32, device="cuda", requires_grad=(which == "input"))
+    if which == "input":
+        for prm in m.parameters():
+            prm.requires_grad_(False)
+    dy = torch.randn(2, 8, 32, 32, device="cuda")
+    m(x).backward(dy)
+    torch.cuda.synchronize()
+    p = [getattr(m, n).detach().double().cpu().numpy() for n in ("w_base", "b_base", "s_base", "w_wav", "s_wav")]
+    go = oracle.bwd(x.detach().double().cpu().numpy(), dy.double().cpu().numpy(), *p)
+    if which == "input":
+        assert rel_err(x.grad.double().cpu().numpy(), go["dx"]) < 1e-5
+    else:
+        assert x.grad is None
+        assert rel_err(m.w_base.grad.double().cpu().numpy(), go["dw_base"]) < 1e-5
+        assert rel_err(m.s_wav.grad.double().cpu().numpy(), go["ds_wav"]) < 1e-5
