@@ -140,33 +140,81 @@ constexpr int bank_cost(int first_job, int njobs_l, int S, int NS, int NG, int R
     return cost;
 }
 
-// Level start, pitch and array gap, each over one period of the bank index:
-// the level starts on the bank of its first lane's tile (R times its job
-// index), then the pitch is searched with no gap, then the gap.  Least bank
-// multiplicity wins, then least LDS.
+// Level start, pitch and array gap, each over one period of the bank index.
+// The core of every array starts on a multiple of `al` floats and pitch and
+// gap keep it there, so that rows can be moved with 8- and 16-byte LDS
+// accesses.  Pitch and start are searched together (with al = 1 the start is
+// put on the bank of the first lane's tile, R times its job index), then the
+// gap.  Least bank multiplicity wins, then least LDS.
 constexpr Layout plan_layout(int first_job, int njobs_l, int S, int NS, int NG, int R, int Q,
-                             int rows, int minpitch, int base) {
-    int off = base;
-    while (((off - R * first_job) % 32 + 32) % 32 != 0) ++off;
-    int bp = minpitch, bc = 1 << 30;
-    for (int dp = 0; dp < 32; ++dp) {
-        const int c = bank_cost(first_job, njobs_l, S, NS, NG, R, Q, minpitch + dp,
-                                rows * (minpitch + dp), off);
-        if (c < bc) {
-            bc = c;
-            bp = minpitch + dp;
+                             int rows, int minpitch, int base, int h, int al) {
+    int p0 = minpitch;
+    while (p0 % al) ++p0;
+    int bp = p0, boff = base, bc = 1 << 30;
+    for (int dp = 0; dp < 32; dp += al) {
+        const int pitch = p0 + dp;
+        for (int off = base; off < base + 32; ++off) {
+            if (al == 1) {
+                if (((off - R * first_job) % 32 + 32) % 32 != 0) continue;
+            } else if ((off + h * pitch + h) % al != 0) {
+                continue;
+            }
+            const int c = bank_cost(first_job, njobs_l, S, NS, NG, R, Q, pitch, rows * pitch, off);
+            if (c < bc) {
+                bc = c;
+                bp = pitch;
+                boff = off;
+            }
         }
     }
     int bg = 0;
     bc = 1 << 30;
-    for (int gap = 0; gap < 32; ++gap) {
-        const int c = bank_cost(first_job, njobs_l, S, NS, NG, R, Q, bp, rows * bp + gap, off);
+    for (int gap = 0; gap < 32; gap += al) {
+        const int c = bank_cost(first_job, njobs_l, S, NS, NG, R, Q, bp, rows * bp + gap, boff);
         if (c < bc) {
             bc = c;
             bg = gap;
         }
     }
-    return Layout{bp, rows * bp + bg, off};
+    return Layout{bp, rows * bp + bg, boff};
+}
+
+// n consecutive floats between registers and LDS at an element offset that is
+// a multiple of A floats (A = 1, 2 or 4): 16-, 8- or 4-byte accesses.
+template <int N, int A>
+__device__ __forceinline__ void lds_put(float* dst, const float* v) {
+    if constexpr (A % 4 == 0 && N % 4 == 0) {
+#pragma unroll
+        for (int c = 0; c < N; c += 4)
+            *reinterpret_cast<float4*>(dst + c) = make_float4(v[c], v[c + 1], v[c + 2], v[c + 3]);
+    } else if constexpr (A % 2 == 0 && N % 2 == 0) {
+#pragma unroll
+        for (int c = 0; c < N; c += 2)
+            *reinterpret_cast<float2*>(dst + c) = make_float2(v[c], v[c + 1]);
+    } else {
+#pragma unroll
+        for (int c = 0; c < N; ++c) dst[c] = v[c];
+    }
+}
+
+template <int N, int A>
+__device__ __forceinline__ void lds_get(const float* src, float* v) {
+    if constexpr (A % 4 == 0 && N % 4 == 0) {
+#pragma unroll
+        for (int c = 0; c < N; c += 4) {
+            const float4 q = *reinterpret_cast<const float4*>(src + c);
+            v[c] = q.x; v[c + 1] = q.y; v[c + 2] = q.z; v[c + 3] = q.w;
+        }
+    } else if constexpr (A % 2 == 0 && N % 2 == 0) {
+#pragma unroll
+        for (int c = 0; c < N; c += 2) {
+            const float2 q = *reinterpret_cast<const float2*>(src + c);
+            v[c] = q.x; v[c + 1] = q.y;
+        }
+    } else {
+#pragma unroll
+        for (int c = 0; c < N; ++c) v[c] = src[c];
+    }
 }
 
 // LDS geometry of a group of P planes.  Level 0 holds the input planes,
@@ -179,7 +227,10 @@ constexpr Layout plan_layout(int first_job, int njobs_l, int S, int NS, int NG, 
 // HT_ > 0: an H x W output tile of a larger plane with HT_ levels handled in
 // the tile; level l carries a halo of h(l) = p 2^(HT_-l) real neighbouring
 // values (the receptive footprint of the coarser levels) around its core.
-template <int K_, int L_, int H_, int W_, int P_, int NT_, int HT_ = 0>
+// AMAX_ caps the row alignment (floats): 4 lets the row phases use 16-byte
+// LDS accesses, 2 leaves the pitch free to spread the conv windows of a
+// wavefront over every bank.
+template <int K_, int L_, int H_, int W_, int P_, int NT_, int HT_ = 0, int AMAX_ = 4>
 struct Geo {
     static constexpr int K = K_, L = L_, H = H_, W = W_, P = P_, NT = NT_, HT = HT_;
     static constexpr int p = K / 2, KK = K * K;
@@ -210,6 +261,17 @@ struct Geo {
     __host__ __device__ static constexpr int minpitch(int l) {
         return h(l) + maxi(NS(l) * R + p, wl(l) + h(l));
     }
+    // alignment (floats) of the core rows of level l: the widest LDS access
+    // the fp32 item width of the plane (and of the halo) allows, halved per
+    // level
+    __host__ __device__ static constexpr int vec_f32(int n) {
+        return n % 4 == 0 ? 4 : (n % 2 == 0 ? 2 : 1);
+    }
+    __host__ __device__ static constexpr int al(int l) {
+        int a0 = HT ? (vec_f32(W) < vec_f32(ah(0)) ? vec_f32(W) : vec_f32(ah(0))) : vec_f32(W);
+        if (a0 > AMAX_) a0 = AMAX_;
+        return (a0 >> l) > 1 ? (a0 >> l) : 1;
+    }
 
     struct Table {
         Layout lv[L_ + 1];
@@ -220,13 +282,21 @@ struct Geo {
         int base = 0;
         for (int l = 0; l <= L; ++l) {
             t.lv[l] = plan_layout(jstart(l), jobs(l), S(l), NS(l), NG(l), R, Q, rows(l),
-                                  minpitch(l), base);
+                                  minpitch(l), base, h(l), al(l));
             base = t.lv[l].off + P * S(l) * t.lv[l].astride;
         }
         t.end = base;
         return t;
     }
     static constexpr Table TB = make_table();
+    static constexpr bool aligned_table() {
+        for (int l = 0; l <= L; ++l) {
+            const int a = al(l), pt = TB.lv[l].pitch, o = TB.lv[l].off;
+            if (pt % a || TB.lv[l].astride % a || (o + h(l) * pt + h(l)) % a) return false;
+        }
+        return true;
+    }
+    static_assert(aligned_table(), "array cores aligned for vector LDS access");
     __host__ __device__ static constexpr int pitch(int l) { return TB.lv[l].pitch; }
     __host__ __device__ static constexpr int arr(int l) { return TB.lv[l].astride; }
     __host__ __device__ static constexpr int off(int l) { return TB.lv[l].off; }
@@ -253,6 +323,11 @@ struct Geo {
     static_assert((H % (1 << L)) == 0 && (W % (1 << L)) == 0, "H, W % 2^L");
     static_assert(NT % 64 == 0, "whole waves");
 };
+
+// Layout of the whole-plane gradient kernels: each lane reads two windows
+// per tile (dy and x), so window reads outweigh the row phases.
+template <int K, int L, int H, int W, int P, int NT>
+using GeoGrad = Geo<K, L, H, W, P, NT, 0, 2>;
 
 // One lane's tile: array level, plane, subband, tile row group and column
 // strip.  Decoded once; the lane keeps it on every group of planes.
@@ -442,20 +517,21 @@ struct Fetch {
         o[3] = d0 - d1;
     }
 
-    template <bool VSIDE>
-    static __device__ __forceinline__ void put(float* lds, int l, int pl, int i, int j,
-                                               const float (&o)[4]) {
-        float* dst;
-        int A;
-        if constexpr (VSIDE) {
-            dst = lds + G::vidx(l, pl, 0, i, j);
-            A = l == 1 ? G::varr(1) : G::varr(2);
-        } else {
-            dst = lds + G::uidx(l, pl, 0, i, j);
-            A = l == 1 ? G::arr(1) : G::arr(G::L >= 2 ? 2 : 1);
-        }
+    // N consecutive coefficients of each subband of level l at row i,
+    // columns j..j+N-1: to the x side (aligned rows) or the compact dy side.
+    template <bool VSIDE, int l, int N>
+    static __device__ __forceinline__ void put_row(float* lds, int pl, int i, int j,
+                                                   const float (&sub)[4][N]) {
 #pragma unroll
-        for (int s = 0; s < 4; ++s) dst[s * A] = o[s];
+        for (int sb = 0; sb < 4; ++sb) {
+            if constexpr (VSIDE) {
+                float* dst = lds + G::vidx(l, pl, sb, i, j);
+#pragma unroll
+                for (int m = 0; m < N; ++m) dst[m] = sub[sb][m];
+            } else {
+                lds_put<N, G::al(l)>(lds + G::uidx(l, pl, sb, i, j), sub[sb]);
+            }
+        }
     }
 
     // Write the pixels to the level-0 array (WRITE_X) and the level-1 (and,
@@ -476,28 +552,33 @@ struct Fetch {
                 if constexpr (WRITE_X) {
                     float* o = lds + G::uidx(0, pl, 0, fy, fx);
 #pragma unroll
-                    for (int k = 0; k < ROWS; ++k)
-#pragma unroll
-                        for (int e = 0; e < V; ++e) o[k * G::pitch(0) + e] = x[k][e];
+                    for (int k = 0; k < ROWS; ++k) lds_put<V, G::al(0)>(o + k * G::pitch(0), x[k]);
                 }
                 float ll[ROWS / 2][V / 2];
 #pragma unroll
-                for (int rr = 0; rr < ROWS / 2; ++rr)
+                for (int rr = 0; rr < ROWS / 2; ++rr) {
+                    float sub[4][V / 2];
 #pragma unroll
                     for (int m = 0; m < V / 2; ++m) {
                         float o[4];
                         butterfly(x[2 * rr][2 * m], x[2 * rr][2 * m + 1], x[2 * rr + 1][2 * m],
                                   x[2 * rr + 1][2 * m + 1], o);
                         ll[rr][m] = o[0];
-                        put<VSIDE>(lds, 1, pl, fy / 2 + rr, fx / 2 + m, o);
+#pragma unroll
+                        for (int sb = 0; sb < 4; ++sb) sub[sb][m] = o[sb];
                     }
+                    put_row<VSIDE, 1, V / 2>(lds, pl, fy / 2 + rr, fx / 2, sub);
+                }
                 if constexpr (ROWS == 4) {
+                    float sub[4][V / 4];
 #pragma unroll
                     for (int m = 0; m < V / 4; ++m) {
                         float o[4];
                         butterfly(ll[0][2 * m], ll[0][2 * m + 1], ll[1][2 * m], ll[1][2 * m + 1], o);
-                        put<VSIDE>(lds, 2, pl, fy / 4, fx / 4 + m, o);
+#pragma unroll
+                        for (int sb = 0; sb < 4; ++sb) sub[sb][m] = o[sb];
                     }
+                    put_row<VSIDE, 2, V / 4>(lds, pl, fy / 4, fx / 4, sub);
                 }
             }
         }
@@ -648,7 +729,6 @@ template <class G, typename T>
 __device__ __forceinline__ void final_to_lds(float* lds, int tid) {
     constexpr int V = vec_elems<T>(G::W);
     constexpr int NV = G::W / V, RP = G::H / 2, ITEMS = G::P * RP * NV;
-    constexpr int A1 = G::arr(1);
 #pragma unroll
     for (int it = 0; it < cdiv(ITEMS, G::NT); ++it) {
         const int item = tid + it * G::NT;
@@ -657,10 +737,15 @@ __device__ __forceinline__ void final_to_lds(float* lds, int tid) {
             const int i = (item / NV) % RP;
             const int pl = item / (NV * RP);
             float* x0 = lds + G::uidx(0, pl, 0, 2 * i, cv * V);
-            const float* cs = lds + G::uidx(1, pl, 0, i, cv * (V / 2));
+            float r0[V], r1[V], c[4][V / 2];
+            lds_get<V, G::al(0)>(x0, r0);
+            lds_get<V, G::al(0)>(x0 + G::pitch(0), r1);
+#pragma unroll
+            for (int sb = 0; sb < 4; ++sb)
+                lds_get<V / 2, G::al(1)>(lds + G::uidx(1, pl, sb, i, cv * (V / 2)), c[sb]);
 #pragma unroll
             for (int m = 0; m < V / 2; ++m) {
-                float ll = cs[m];
+                float ll = c[0][m];
                 if constexpr (G::L >= 2) {
                     constexpr int A2 = G::arr(2);
                     const int j = cv * (V / 2) + m;
@@ -670,14 +755,16 @@ __device__ __forceinline__ void final_to_lds(float* lds, int tid) {
                     const float f2 = fmaf(sy2, c2[3 * A2], c2[A2]);
                     ll += fmaf(sx2, f2, e2);
                 }
-                const float lh = cs[A1 + m], hl = cs[2 * A1 + m], hh = cs[3 * A1 + m];
+                const float lh = c[1][m], hl = c[2][m], hh = c[3][m];
                 const float e0 = ll + hl, f0 = lh + hh;  // row 2i   (row bit 0)
                 const float e1 = ll - hl, f1 = lh - hh;  // row 2i+1 (row bit 1)
-                x0[2 * m] += e0 + f0;
-                x0[2 * m + 1] += e0 - f0;
-                x0[G::pitch(0) + 2 * m] += e1 + f1;
-                x0[G::pitch(0) + 2 * m + 1] += e1 - f1;
+                r0[2 * m] += e0 + f0;
+                r0[2 * m + 1] += e0 - f0;
+                r1[2 * m] += e1 + f1;
+                r1[2 * m + 1] += e1 - f1;
             }
+            lds_put<V, G::al(0)>(x0, r0);
+            lds_put<V, G::al(0)>(x0 + G::pitch(0), r1);
         }
     }
 }
@@ -708,8 +795,7 @@ __device__ __forceinline__ void store_out(const float* lds, T* __restrict__ out,
 #pragma unroll
                 for (int k = 0; k < ROWS; ++k) {
                     float v[V];
-#pragma unroll
-                    for (int e = 0; e < V; ++e) v[e] = x0p[k * G::pitch(0) + e];
+                    lds_get<V, G::al(0)>(x0p + k * G::pitch(0), v);
                     store_vec<T, V>(o + k * Wp, v);
                 }
             }
@@ -911,7 +997,7 @@ __global__ __launch_bounds__(NT) void k_plane_bww(
                                                   const T* __restrict__ dy,
                                                   float* __restrict__ part, int B, int C,
                                                   int gpw) {
-    using G = Geo<K, L, H, W, P, NT>;
+    using G = GeoGrad<K, L, H, W, P, NT>;
     constexpr int KK = G::KK, Q = G::Q, R = G::R;
     extern __shared__ float lds[];
     const int tid = threadIdx.x;
@@ -1019,7 +1105,7 @@ __global__ __launch_bounds__(NT) void k_plane_bwd(
     const T* __restrict__ x, const T* __restrict__ dy, const T* __restrict__ wb,
     const T* __restrict__ sb, const T* __restrict__ ww, const T* __restrict__ sw,
     T* __restrict__ dx, float* __restrict__ part, int B, int C, int gpw) {
-    using G = Geo<K, L, H, W, P, NT>;
+    using G = GeoGrad<K, L, H, W, P, NT>;
     using F = Fetch<G, T>;
     constexpr int KK = G::KK, Q = G::Q, R = G::R, DY = bwd_dy_base<G>();
     extern __shared__ float lds[];

@@ -20,9 +20,10 @@ constexpr size_t kMaxLds = 163840;  // LDS of one gfx950 compute unit
 template <int K, int L, int H, int W, int P, int NT, typename T>
 Variant make_variant(int dtype) {
     using G = Geo<K, L, H, W, P, NT>;
+    using GG = GeoGrad<K, L, H, W, P, NT>;
     const size_t la = apply_lds_bytes<G>();
-    const size_t lb = bww_lds_bytes<G>();
-    constexpr size_t ld = bwd_lds_bytes<G>();
+    const size_t lb = bww_lds_bytes<GG>();
+    constexpr size_t ld = bwd_lds_bytes<GG>();
     const void* fused = nullptr;
     if constexpr (ld <= kMaxLds)
         fused = reinterpret_cast<const void*>(&k_plane_bwd<K, L, H, W, P, NT, T>);
