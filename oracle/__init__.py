@@ -88,23 +88,28 @@ def _params(C, L, k, w_base, b_base, s_base, w_wav, s_wav):
 
 
 def haar_analysis(z):
-    """One analysis step H: z [h, w] -> subbands [4, h/2, w/2] (LL, LH, HL,
-    HH), the stride-2 2x2 Haar filtering the oracle's cascade uses."""
+    """One analysis step H: z [h, w] -> subbands [4, ceil(h/2), ceil(w/2)]
+    (LL, LH, HL, HH), the stride-2 2x2 Haar filtering the oracle's cascade
+    uses; an odd side reads one appended zero row (column)."""
     z = _f64(z)
     h, w = z.shape
-    out = np.empty((4, h // 2, w // 2))
+    out = np.empty((4, (h + 1) // 2, (w + 1) // 2))
     if _load().oracle_haar_analysis(h, w, _ptr(z), _ptr(out)) != 0:
-        raise ValueError("odd size")
+        raise ValueError("bad size")
     return out
 
 
-def haar_synthesis(sub):
-    """One synthesis step H^T: subbands [4, h, w] -> [2h, 2w]."""
+def haar_synthesis(sub, shape=None):
+    """One synthesis step H^T: subbands [4, h, w] -> [2h, 2w], or cropped to
+    `shape` (rows, cols), which must have ceil(rows/2) = h, ceil(cols/2) = w."""
     sub = _f64(sub)
     _, h, w = sub.shape
-    out = np.empty((2 * h, 2 * w))
-    if _load().oracle_haar_synthesis(2 * h, 2 * w, _ptr(sub), _ptr(out)) != 0:
-        raise ValueError("odd size")
+    rows, cols = shape if shape is not None else (2 * h, 2 * w)
+    if (rows + 1) // 2 != h or (cols + 1) // 2 != w:
+        raise ValueError("shape does not match the subbands")
+    out = np.empty((rows, cols))
+    if _load().oracle_haar_synthesis(rows, cols, _ptr(sub), _ptr(out)) != 0:
+        raise ValueError("bad size")
     return out
 
 

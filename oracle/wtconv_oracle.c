@@ -37,7 +37,13 @@
  * Readings where the pages are silent (each listed in the design notes):
  *   subband order (LL, LH, HL, HH); base conv carries a bias, wavelet convs
  *   do not; scales beta[C], gamma[L,C,4] multiply after the conv; each level
- *   zero-pads its own coefficient grid; H, W divisible by 2^L.
+ *   zero-pads its own coefficient grid.
+ *
+ * Grids with an odd side: the tutorial's analysis is a stride-2 convolution
+ * with TensorFlow's 'SAME' padding (cybasar.com, section 3), which for an
+ * odd side appends one zero row (column) at the end, so level l has
+ * ceil(h_{l-1}/2) rows.  H^T is the transpose of that map: the transposed
+ * stride-2 convolution cropped back to the h_{l-1} rows of the finer grid.
  *
  * Layouts (all contiguous, row-major):
  *   x, y, dy, dx : [B][C][H][W]
@@ -127,31 +133,40 @@ static void conv_same_adj_kernel(const double* dout, const double* z, int h,
         }
 }
 
-/* H: z is h x w (both even); sub[s] is (h/2) x (w/2). */
+/* Rows (columns) of the next coarser grid. */
+static int half_up(int n) { return (n + 1) / 2; }
+
+/* H: z is h x w; sub[s] is ceil(h/2) x ceil(w/2).  Taps past the end of z
+   read zero (the appended row / column of an odd side). */
 static void haar_analysis(const double* z, int h, int w, double* sub[4]) {
-    int h2 = h / 2, w2 = w / 2;
+    int h2 = half_up(h), w2 = half_up(w);
     for (int s = 0; s < 4; ++s)
         for (int i = 0; i < h2; ++i)
             for (int j = 0; j < w2; ++j) {
                 double acc = 0.0;
                 for (int a = 0; a < 2; ++a)
-                    for (int b = 0; b < 2; ++b)
-                        acc += HAAR[s][a][b] * z[(2 * i + a) * w + (2 * j + b)];
+                    for (int b = 0; b < 2; ++b) {
+                        int r = 2 * i + a, q = 2 * j + b;
+                        if (r < h && q < w) acc += HAAR[s][a][b] * z[r * w + q];
+                    }
                 sub[s][i * w2 + j] = acc;
             }
 }
 
-/* H^T: z (h x w) = transposed stride-2 conv of the four subbands. */
+/* H^T: z (h x w) = transposed stride-2 conv of the four subbands
+   (ceil(h/2) x ceil(w/2)), cropped to h x w. */
 static void haar_synthesis(double* const sub[4], int h, int w, double* z) {
-    int h2 = h / 2, w2 = w / 2;
+    int h2 = half_up(h), w2 = half_up(w);
     memset(z, 0, sizeof(double) * (size_t)h * w);
     for (int s = 0; s < 4; ++s)
         for (int i = 0; i < h2; ++i)
             for (int j = 0; j < w2; ++j) {
                 double c = sub[s][i * w2 + j];
                 for (int a = 0; a < 2; ++a)
-                    for (int b = 0; b < 2; ++b)
-                        z[(2 * i + a) * w + (2 * j + b)] += HAAR[s][a][b] * c;
+                    for (int b = 0; b < 2; ++b) {
+                        int r = 2 * i + a, q = 2 * j + b;
+                        if (r < h && q < w) z[r * w + q] += HAAR[s][a][b] * c;
+                    }
             }
 }
 
@@ -166,7 +181,11 @@ typedef struct {
     double* T[8];      /* Y^l_LL + R^{l+1} */
 } plane_ws;
 
-static int lvl_h(int H, int l) { return H >> l; }
+/* Side of level l's grid: l halvings, each rounded up. */
+static int lvl_h(int H, int l) {
+    for (int m = 0; m < l; ++m) H = half_up(H);
+    return H;
+}
 
 static void ws_alloc(plane_ws* ws, int L, int H, int W) {
     ws->L = L; ws->H = H; ws->W = W;
@@ -245,7 +264,6 @@ int oracle_fwd(int B, int C, int H, int W, int L, int k, const double* x,
     if (B < 0 || C < 0 || H < 0 || W < 0 || L < 1 || L > 8 || k < 1 ||
         (k % 2) == 0)
         return -1;
-    if ((H % (1 << L)) || (W % (1 << L))) return -2;
     long nplanes = (long)B * C;
     size_t hw = (size_t)H * W;
 #pragma omp parallel
@@ -275,7 +293,6 @@ int oracle_bwd(int B, int C, int H, int W, int L, int k, const double* x,
     if (B < 0 || C < 0 || H < 0 || W < 0 || L < 1 || L > 8 || k < 1 ||
         (k % 2) == 0)
         return -1;
-    if ((H % (1 << L)) || (W % (1 << L))) return -2;
     int kk = k * k;
     long nplanes = (long)B * C;
     size_t hw = (size_t)H * W;
@@ -417,18 +434,19 @@ int oracle_bwd(int B, int C, int H, int W, int L, int k, const double* x,
 }
 
 /* Test hooks: the single-level building blocks, exposed so that the test
-   suite can pin them on their own (z is h x w, sub is 4 x (h/2) x (w/2)). */
+   suite can pin them on their own (z is h x w, sub is
+   4 x ceil(h/2) x ceil(w/2)). */
 int oracle_haar_analysis(int h, int w, const double* z, double* sub) {
-    if (h < 0 || w < 0 || (h % 2) || (w % 2)) return -2;
-    size_t q = (size_t)(h / 2) * (w / 2);
+    if (h < 0 || w < 0) return -2;
+    size_t q = (size_t)half_up(h) * half_up(w);
     double* s4[4] = {sub, sub + q, sub + 2 * q, sub + 3 * q};
     haar_analysis(z, h, w, s4);
     return 0;
 }
 
 int oracle_haar_synthesis(int h, int w, const double* sub, double* z) {
-    if (h < 0 || w < 0 || (h % 2) || (w % 2)) return -2;
-    size_t q = (size_t)(h / 2) * (w / 2);
+    if (h < 0 || w < 0) return -2;
+    size_t q = (size_t)half_up(h) * half_up(w);
     double* s4[4] = {(double*)sub, (double*)sub + q, (double*)sub + 2 * q,
                      (double*)sub + 3 * q};
     haar_synthesis(s4, h, w, z);

@@ -75,6 +75,53 @@ def test_haar_filters_match_printed_values():
             np.testing.assert_array_equal(sub[:, 0, 0], filt[:, a, b])
 
 
+@pytest.mark.parametrize("h,w", [(5, 7), (1, 1), (3, 4), (6, 9)])
+def test_haar_odd_sides_reconstruct_and_are_adjoint(h, w):
+    """With one zero row (column) appended to an odd side, H is orthonormal
+    on the padded grid, so the cropped H^T inverts it exactly, and the two
+    maps are each other's transpose."""
+    r = np.random.default_rng(h * 10 + w)
+    z = r.normal(size=(h, w))
+    sub = oracle.haar_analysis(z)
+    assert sub.shape == (4, (h + 1) // 2, (w + 1) // 2)
+    np.testing.assert_allclose(oracle.haar_synthesis(sub, (h, w)), z, rtol=0, atol=1e-14)
+    s = r.normal(size=sub.shape)
+    lhs = (sub * s).sum()
+    rhs = (z * oracle.haar_synthesis(s, (h, w))).sum()
+    assert abs(lhs - rhs) < 1e-13 * max(1.0, abs(lhs))
+    # the padded tap reads zero: same subbands as analysing the padded grid
+    zp = np.zeros((h + h % 2, w + w % 2))
+    zp[:h, :w] = z
+    np.testing.assert_array_equal(oracle.haar_analysis(zp), sub)
+
+
+@pytest.mark.parametrize("H,W,L,k,extra", [(15, 13, 2, 3, 0), (21, 10, 3, 5, 0), (5, 5, 3, 3, 8),
+                                           (30, 30, 3, 5, 0), (9, 14, 1, 5, 4)])
+def test_padding_once_equals_padding_per_level(H, W, L, k, extra):
+    """Appending zeros once, up to any multiple of 2^L, and cropping the
+    result gives the per-level padded cascade: a block entirely in the padding
+    has zero coefficients, so every grid is the per-level grid extended by
+    zeros, and coefficients past a grid only reach outputs past the image."""
+    r = np.random.default_rng(H * W + L)
+    B, C = 2, 2
+    x = r.normal(size=(B, C, H, W))
+    dy = r.normal(size=x.shape)
+    p = rand_params(C, L, k, seed=4)
+    m = 1 << L
+    Hp, Wp = -(-H // m) * m + extra, -(-W // m) * m + extra
+    xp = np.zeros((B, C, Hp, Wp))
+    xp[..., :H, :W] = x
+    dyp = np.zeros_like(xp)
+    dyp[..., :H, :W] = dy
+    y, yp = fwd(x, p), fwd(xp, p)
+    np.testing.assert_allclose(y, yp[..., :H, :W], rtol=0, atol=1e-12 * np.abs(y).max())
+    g, gp = bwd(x, dy, p), bwd(xp, dyp, p)
+    np.testing.assert_allclose(g["dx"], gp["dx"][..., :H, :W], rtol=0,
+                               atol=1e-12 * np.abs(g["dx"]).max())
+    for n in ("dw_base", "db_base", "ds_base", "dw_wav", "ds_wav"):
+        np.testing.assert_allclose(g[n], gp[n], rtol=0, atol=1e-12 * np.abs(g[n]).max(), err_msg=n)
+
+
 def test_haar_orthonormal_and_parseval():
     r = np.random.default_rng(1)
     z = r.normal(size=(12, 10))
@@ -269,12 +316,12 @@ def loss(x, p, dy):
     return float((fwd(x, p) * dy).sum())
 
 
-@pytest.mark.parametrize("L,k", [(2, 3), (2, 5), (3, 3)])
-def test_gradients_by_central_differences(L, k):
+@pytest.mark.parametrize("L,k,H,W", [(2, 3, 8, 8), (2, 5, 8, 8), (3, 3, 8, 8), (2, 3, 7, 5)])
+def test_gradients_by_central_differences(L, k, H, W):
     """Every element of every gradient against the central difference of
     <dy, y>.  y is linear in x and in each parameter tensor taken alone, so
     the difference quotient is exact up to rounding for any step."""
-    B, C, H, W = 2, 2, 8, 8
+    B, C = 2, 2
     r = np.random.default_rng(L * 10 + k)
     x = r.normal(size=(B, C, H, W))
     dy = r.normal(size=(B, C, H, W))

@@ -6,7 +6,10 @@ stride-2 analysis is torch's grouped conv2d with the printed Haar filters
 conv2d and its scale, the synthesis is torch's conv_transpose2d with the same
 filters, run from the deepest level up with the deeper reconstruction added to
 the convolved LL (gist.science/pt summary, "Metodologia"), and the base path
-is a depthwise conv2d with bias times its scale.  Its gradients come from
+is a depthwise conv2d with bias times its scale.  A grid with an odd side gets
+one zero row (column) appended before its analysis, as TensorFlow's 'SAME'
+padding does for the tutorial's stride-2 convolutions, and the transposed
+convolution's output is cropped back to that grid.  Its gradients come from
 torch.autograd, so the oracle's hand-written backward is checked against an
 implementation it shares nothing with.
 """
@@ -40,8 +43,11 @@ def torch_wtconv(x, wb, bb, sb, ww, sw):
     dec = golden_filters().repeat(C, 1, 1, 1)  # [4C, 1, 2, 2], channel-major
     A = x
     Ys = []
+    sizes = []
     for l in range(L):
-        S = F.conv2d(A, dec, stride=2, groups=C)  # [B, 4C, h, w]
+        h, w = A.shape[-2:]
+        sizes.append((h, w))
+        S = F.conv2d(F.pad(A, (0, w % 2, 0, h % 2)), dec, stride=2, groups=C)  # [B, 4C, h', w']
         h, w = S.shape[-2:]
         A = S.view(B, C, 4, h, w)[:, :, 0]
         Y = F.conv2d(S, ww[l].reshape(4 * C, 1, k, k), padding=k // 2, groups=4 * C)
@@ -54,6 +60,7 @@ def torch_wtconv(x, wb, bb, sb, ww, sw):
         if R is not None:
             Y5 = torch.cat([(Y5[:, :, 0] + R).unsqueeze(2), Y5[:, :, 1:]], dim=2)
         R = F.conv_transpose2d(Y5.reshape(B, 4 * C, h, w), dec, stride=2, groups=C)
+        R = R[:, :, :sizes[l][0], :sizes[l][1]]
     base = F.conv2d(x, wb.reshape(C, 1, k, k), bb, padding=k // 2, groups=C)
     return base * sb.reshape(1, C, 1, 1) + R
 
@@ -65,6 +72,13 @@ CASES = [  # B, C, H, W, L, k
     (3, 2, 32, 16, 4, 3),
     (1, 4, 64, 64, 5, 5),
     (1, 2, 28, 28, 2, 7),
+    # sides not divisible by 2^L: odd grids at one or more levels
+    (2, 3, 15, 13, 2, 3),
+    (1, 2, 21, 10, 3, 5),
+    (2, 2, 7, 9, 3, 3),
+    (1, 2, 5, 5, 3, 3),
+    (1, 1, 1, 3, 2, 3),
+    (1, 2, 30, 30, 3, 5),
 ]
 
 
