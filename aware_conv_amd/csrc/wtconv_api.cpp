@@ -19,13 +19,14 @@ int check_shape(const wtconv_shape* s) {
     if (s->L < 1 || s->L > WTCONV_MAX_LEVELS) return WTCONV_ERR_LEVELS;
     if (s->k < 1 || s->k > 7 || (s->k % 2) == 0) return WTCONV_ERR_KERNEL;
     if (s->dtype != WTCONV_F32 && s->dtype != WTCONV_F16) return WTCONV_ERR_DTYPE;
-    const int m = 1 << s->L;
-    if ((s->H % m) != 0 || (s->W % m) != 0) return WTCONV_ERR_SHAPE;
-    // element counts must fit the kernels' 64-bit offsets and 32-bit grids
+    // element counts (also of the zero-extended planes, at most 2^L - 1
+    // rows and columns more) must fit the kernels' 64-bit offsets and 32-bit
+    // grids
+    if (s->H > (1 << 24) || s->W > (1 << 24)) return WTCONV_ERR_SHAPE;
     const unsigned long long n = (unsigned long long)s->B * (unsigned long long)s->C *
-                                 (unsigned long long)s->H * (unsigned long long)s->W;
-    if (s->H > 0 && s->W > 0 && n / ((unsigned long long)s->H * s->W) !=
-                                    (unsigned long long)s->B * s->C)
+                                 (unsigned long long)(s->H + 64) *
+                                 (unsigned long long)(s->W + 64);
+    if (n / ((unsigned long long)(s->H + 64) * (s->W + 64)) != (unsigned long long)s->B * s->C)
         return WTCONV_ERR_SHAPE;
     if (n > (1ULL << 40)) return WTCONV_ERR_SHAPE;
     return WTCONV_OK;
@@ -57,21 +58,113 @@ int check_params(const wtconv_shape* s, const void* w_base, const void* b_base,
     return WTCONV_OK;
 }
 
-// Two kernel families: whole planes staged in LDS (the shapes this build
-// instantiates), else output tiles of large planes plus per-plane deep levels.
-bool use_plane(const wtconv_shape* s) { return wtc::plane_supported(*s); }
+// How a shape runs.  Two kernel families take a shape directly: whole planes
+// staged in LDS (the shapes this build instantiates), else output tiles of
+// large planes plus per-plane deep levels.  Any other shape runs on planes
+// zero-extended at their end (into the workspace), and its results are
+// cropped back.
+struct Plan {
+    bool ok;
+    bool padded;
+    bool plane;          // whole-plane kernels (else tiles)
+    wtconv_shape run;    // the shape the kernels see
+    size_t inner;        // workspace bytes of the kernels on `run`
+    size_t buf;          // bytes of one zero-extended activation tensor
+};
+
+constexpr size_t kWsAlign = 256;
+size_t round_up(size_t n, size_t m) { return (n + m - 1) / m * m; }
+int round_up_int(int n, int m) { return (n + m - 1) / m * m; }
+
+bool direct(const wtconv_shape& s, bool* plane) {
+    if (wtc::plane_supported(s)) {
+        *plane = true;
+        return true;
+    }
+    *plane = false;
+    return wtc::tile_supported(s);
+}
+
+Plan plan_for(const wtconv_shape* s) {
+    Plan pl{};
+    pl.run = *s;
+    if (empty_act(s)) {
+        pl.ok = true;
+        return pl;
+    }
+    if (direct(*s, &pl.plane)) {
+        pl.ok = true;
+    } else {
+        // the smallest extension with a whole-plane kernel, else the tile
+        // path's row and vector multiples
+        const int m = 1 << s->L;
+        wtconv_shape a = *s;
+        a.H = round_up_int(s->H, m);
+        a.W = round_up_int(s->W, m);
+        wtconv_shape b = *s;
+        b.H = round_up_int(s->H, m > 4 ? m : 4);
+        const int vw = s->dtype == WTCONV_F32 ? 4 : 8;
+        b.W = round_up_int(s->W, m > vw ? m : vw);
+        bool plane = false;
+        if (wtc::plane_supported(a)) {
+            pl.run = a;
+            pl.plane = true;
+            pl.ok = true;
+        } else if (direct(b, &plane)) {
+            pl.run = b;
+            pl.plane = plane;
+            pl.ok = true;
+        }
+        pl.padded = pl.ok;
+    }
+    if (!pl.ok) return pl;
+    pl.inner = pl.plane ? wtc::plane_workspace_bytes(pl.run) : wtc::tile_workspace_bytes(pl.run);
+    if (pl.padded) pl.buf = round_up(act_bytes(&pl.run), kWsAlign);
+    return pl;
+}
 
 int check_supported(const wtconv_shape* s) {
-    if (empty_act(s)) return WTCONV_OK;
-    return (use_plane(s) || wtc::tile_supported(*s)) ? WTCONV_OK : WTCONV_ERR_UNSUPPORTED;
+    return plan_for(s).ok ? WTCONV_OK : WTCONV_ERR_UNSUPPORTED;
 }
 
+// The maximum over the calls: the kernels' own workspace, plus (zero-extended
+// shapes) three activation tensors of the extended shape.
 size_t workspace_bytes(const wtconv_shape* s) {
-    if (empty_act(s)) return 0;
-    return use_plane(s) ? wtc::plane_workspace_bytes(*s) : wtc::tile_workspace_bytes(*s);
+    const Plan pl = plan_for(s);
+    if (!pl.ok || empty_act(s)) return 0;
+    if (!pl.padded) return pl.inner;
+    return round_up(pl.inner, kWsAlign) + 3 * pl.buf;
 }
+
+// Workspace a forward or input-gradient call needs (the whole-plane kernels
+// need none).
+size_t apply_workspace_bytes(const wtconv_shape* s) {
+    const Plan pl = plan_for(s);
+    if (pl.ok && !pl.padded && pl.plane) return 0;
+    return workspace_bytes(s);
+}
+
+int check_workspace(size_t need, const void* workspace, size_t ws_bytes) {
+    if (ws_bytes < need) return WTCONV_ERR_WORKSPACE;
+    if (need > 0 && !workspace) return WTCONV_ERR_NULL;
+    if (need > 0 && !aligned(workspace, 16)) return WTCONV_ERR_ALIGN;
+    return WTCONV_OK;
+}
+
+// Zero-extended buffer i of the workspace (after the kernels' own part).
+void* ext_buf(const Plan& pl, void* workspace, int i) {
+    return static_cast<char*>(workspace) + round_up(pl.inner, kWsAlign) + size_t(i) * pl.buf;
+}
+
+long planes_of(const wtconv_shape* s) { return long(s->B) * s->C; }
 
 int hip_status(hipError_t e) { return e == hipSuccess ? WTCONV_OK : WTCONV_ERR_HIP; }
+
+hipError_t run_apply(const Plan& pl, const void* in, const Params& p, void* out, bool flip,
+                     void* workspace, hipStream_t st) {
+    if (pl.plane) return wtc::plane_apply(pl.run, in, p, out, flip, st);
+    return wtc::tile_apply(pl.run, in, p, out, flip, workspace, st);
+}
 
 // Shared by the forward and the input gradient (flip = true).
 int apply(const wtconv_shape* s, const void* in, const void* w_base, const void* b_base,
@@ -85,17 +178,21 @@ int apply(const wtconv_shape* s, const void* in, const void* w_base, const void*
     if (!in || !out) return WTCONV_ERR_NULL;
     if (!aligned(in, 16) || !aligned(out, 16)) return WTCONV_ERR_ALIGN;
     if (overlap(in, out, act_bytes(s))) return WTCONV_ERR_ALIAS;
-    rc = check_supported(s);
+    const Plan pl = plan_for(s);
+    if (!pl.ok) return WTCONV_ERR_UNSUPPORTED;
+    rc = check_workspace(apply_workspace_bytes(s), workspace, ws_bytes);
     if (rc) return rc;
     Params p{w_base, b_base, s_base, w_wav, s_wav};
     hipStream_t st = static_cast<hipStream_t>(stream);
-    if (use_plane(s)) return hip_status(wtc::plane_apply(*s, in, p, out, flip, st));
-    // tiles of large planes: deeper levels go through the workspace
-    const size_t need = workspace_bytes(s);
-    if (ws_bytes < need) return WTCONV_ERR_WORKSPACE;
-    if (need > 0 && !workspace) return WTCONV_ERR_NULL;
-    if (need > 0 && !aligned(workspace, 16)) return WTCONV_ERR_ALIGN;
-    return hip_status(wtc::tile_apply(*s, in, p, out, flip, workspace, st));
+    if (!pl.padded) return hip_status(run_apply(pl, in, p, out, flip, workspace, st));
+    const wtconv_shape& r = pl.run;
+    void* xin = ext_buf(pl, workspace, 0);
+    void* xout = ext_buf(pl, workspace, 1);
+    hipError_t e = wtc::copy_planes(in, xin, planes_of(s), s->H, s->W, r.H, r.W, s->dtype, st);
+    if (e == hipSuccess) e = run_apply(pl, xin, p, xout, flip, workspace, st);
+    if (e == hipSuccess)
+        e = wtc::copy_planes(xout, out, planes_of(s), r.H, r.W, s->H, s->W, s->dtype, st);
+    return hip_status(e);
 }
 
 // Shared by the weight gradient and the fused backward (dx != NULL).
@@ -122,23 +219,39 @@ int backward(const wtconv_shape* s, const void* x, const void* dy, const void* w
         return WTCONV_ERR_ALIGN;
     if (fused && (overlap(dx, dy, act_bytes(s)) || overlap(dx, x, act_bytes(s))))
         return WTCONV_ERR_ALIAS;
-    rc = check_supported(s);
+    const Plan pl = plan_for(s);
+    if (!pl.ok) return WTCONV_ERR_UNSUPPORTED;
+    rc = check_workspace(workspace_bytes(s), workspace, ws_bytes);
     if (rc) return rc;
-    const size_t need = workspace_bytes(s);
-    if (ws_bytes < need) return WTCONV_ERR_WORKSPACE;
-    if (need > 0 && !workspace) return WTCONV_ERR_NULL;
-    if (need > 0 && !aligned(workspace, 16)) return WTCONV_ERR_ALIGN;
-    if (use_plane(s)) {
-        if (fused) return hip_status(wtc::plane_bwd(*s, x, dy, p, dx, g, workspace, st));
-        return hip_status(wtc::plane_bwd_weight(*s, x, dy, p, g, workspace, st));
+    const wtconv_shape& r = pl.run;
+    hipError_t err = hipSuccess;
+    const void* xr = x;
+    const void* dyr = dy;
+    void* dxr = dx;
+    if (pl.padded) {
+        void* xe = ext_buf(pl, workspace, 0);
+        void* dye = ext_buf(pl, workspace, 1);
+        err = wtc::copy_planes(x, xe, planes_of(s), s->H, s->W, r.H, r.W, s->dtype, st);
+        if (err == hipSuccess)
+            err = wtc::copy_planes(dy, dye, planes_of(s), s->H, s->W, r.H, r.W, s->dtype, st);
+        if (err != hipSuccess) return hip_status(err);
+        xr = xe;
+        dyr = dye;
+        dxr = ext_buf(pl, workspace, 2);
     }
-    // tiles of large planes: the input gradient, then the weight gradient,
-    // one after the other on the stream (both use the workspace)
-    if (fused) {
-        const int r = hip_status(wtc::tile_apply(*s, dy, p, dx, true, workspace, st));
-        if (r) return r;
+    if (pl.plane) {
+        err = fused ? wtc::plane_bwd(r, xr, dyr, p, dxr, g, workspace, st)
+                    : wtc::plane_bwd_weight(r, xr, dyr, p, g, workspace, st);
+    } else {
+        // tiles of large planes: the input gradient, then the weight
+        // gradient, one after the other on the stream (both use the
+        // workspace)
+        if (fused) err = wtc::tile_apply(r, dyr, p, dxr, true, workspace, st);
+        if (err == hipSuccess) err = wtc::tile_bwd_weight(r, xr, dyr, p, g, workspace, st);
     }
-    return hip_status(wtc::tile_bwd_weight(*s, x, dy, p, g, workspace, st));
+    if (err == hipSuccess && fused && pl.padded)
+        err = wtc::copy_planes(dxr, dx, planes_of(s), r.H, r.W, s->H, s->W, s->dtype, st);
+    return hip_status(err);
 }
 
 }  // namespace
@@ -192,7 +305,7 @@ const char* wtconv_strerror(int code) {
     switch (code) {
         case WTCONV_OK: return "ok";
         case WTCONV_ERR_NULL: return "a required pointer is NULL";
-        case WTCONV_ERR_SHAPE: return "invalid shape (negative dimension, H or W not a multiple of 2^L, or too large)";
+        case WTCONV_ERR_SHAPE: return "invalid shape (negative or too large dimension)";
         case WTCONV_ERR_KERNEL: return "kernel size must be odd and between 1 and 7";
         case WTCONV_ERR_LEVELS: return "levels must be between 1 and WTCONV_MAX_LEVELS";
         case WTCONV_ERR_DTYPE: return "unknown dtype";

@@ -60,4 +60,9 @@ hipError_t tile_bwd_weight(const wtconv_shape& s, const void* x, const void* dy,
                            const Params& p, const Grads& g, void* workspace,
                            hipStream_t stream);
 
+// Planes of Hs x Ws -> planes of Hd x Wd: the top-left min(Hs,Hd) x
+// min(Ws,Wd) corner copied, zeros elsewhere (zero extension or cropping).
+hipError_t copy_planes(const void* src, void* dst, long planes, int Hs, int Ws, int Hd, int Wd,
+                       int dtype, hipStream_t stream);
+
 }  // namespace wtc

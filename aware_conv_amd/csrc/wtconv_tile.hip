@@ -261,6 +261,7 @@ bool tile_supported(const wtconv_shape& s) {
     // the plane
     const int vec = s.dtype == WTCONV_F32 ? 4 : 8;
     if ((s.H % 4) || (s.W % vec)) return false;
+    if ((s.H % (1 << s.L)) || (s.W % (1 << s.L))) return false;
     if (s.L > tile_lt(s) && deep_bww_lds(s) > kMaxLds) return false;
     return true;
 }

@@ -296,6 +296,8 @@ def main():
         "effective_hbm_gbs": round(step_bytes / (elapsed / args.steps) / 1e9, 1),
         "effective_hbm_frac": round(step_bytes / (elapsed / args.steps) / 1e9 / PEAK_HBM_GBS, 4),
         "per_call_ms": {k: round(v, 5) for k, v in avg_ms.items()},
+        # inference alone: the forward call of the same timed steps
+        "inference_images_per_s": round(wl.B / (avg_ms["wtconv_fwd"] * 1e-3), 1),
         "roofline": {
             "kernel": dom,
             "bound": "alu",

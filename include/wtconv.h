@@ -27,6 +27,13 @@
  * unfused operator up to floating-point evaluation order ("Principais
  * Contribuicoes").
  *
+ * Sides of any length: a grid with an odd side gets one zero row (column)
+ * appended at its end before its analysis, as the stride-2 'SAME' Haar
+ * convolutions of the cybasar.com tutorial (section 3) do, and the synthesis
+ * crops back to that grid.  The library runs such shapes on planes
+ * zero-extended at their end to a multiple of 2^L (in the workspace) and
+ * crops the results, which is the same operator.
+ *
  * Tensors (all contiguous, row-major, device memory, element type `dtype`):
  *   x, y, dy, dx : [B][C][H][W]
  *   w_base       : [C][1][k][k]       b_base, s_base : [C]
@@ -67,7 +74,7 @@ typedef struct {
 
 #define WTCONV_OK 0
 #define WTCONV_ERR_NULL (-1)        /* a required pointer is NULL */
-#define WTCONV_ERR_SHAPE (-2)       /* negative dim, or H or W not a multiple of 2^L */
+#define WTCONV_ERR_SHAPE (-2)       /* negative or too large dimension */
 #define WTCONV_ERR_KERNEL (-3)      /* k even, < 1 or > 7 */
 #define WTCONV_ERR_LEVELS (-4)      /* L outside 1..WTCONV_MAX_LEVELS */
 #define WTCONV_ERR_DTYPE (-5)       /* dtype not a wtconv_dtype */
@@ -90,8 +97,9 @@ int wtconv_workspace_size(const wtconv_shape* s, size_t* bytes);
  * fused Haar analysis, closed-form synthesis, folded scales).  x and y are
  * [B][C][H][W]; y must not overlap x.  Planes too large for on-chip staging
  * with more than three levels use the workspace for the deeper levels'
- * contribution (1/64 of the input); pass wtconv_workspace_size() bytes, or
- * NULL when it reported 0.
+ * contribution (1/64 of the input), and shapes run on zero-extended planes
+ * keep those planes there; pass wtconv_workspace_size() bytes, or NULL when
+ * it reported 0.
  */
 int wtconv_fwd(const wtconv_shape* s, const void* x, const void* w_base,
                const void* b_base, const void* s_base, const void* w_wav,

@@ -59,12 +59,21 @@ def good(lb, **kw):
 
 
 @pytest.mark.parametrize("kw,code", [
-    (dict(B=-1), -2), (dict(H=-56), -2), (dict(H=54), -2), (dict(W=58), -2),
+    (dict(B=-1), -2), (dict(H=-56), -2), (dict(H=1 << 25), -2),
     (dict(L=0), -4), (dict(L=7), -4), (dict(k=4), -3), (dict(k=9), -3), (dict(k=0), -3),
     (dict(dtype=2), -5),
+    # sides that are not multiples of 2^L run on zero-extended planes in the
+    # workspace: without one the call is refused
+    (dict(H=54), -7), (dict(W=58), -7), (dict(H=55, W=55), -7),
 ])
 def test_shape_errors(lb, kw, code):
     assert fwd(lb, good(lb, **kw)) == code
+
+
+def test_odd_sides_need_room_for_extended_planes(lb):
+    # 55 x 55 at L = 2 runs on 56 x 56 planes: three of them plus the partials
+    s55, s56 = good(lb, H=55, W=55), good(lb, H=56, W=56)
+    assert lb.wtconv_workspace_size(s55) >= 3 * 2 * 8 * 56 * 56 * 4 + lb.wtconv_workspace_size(s56)
 
 
 def test_null_and_alignment_errors(lb):
@@ -101,7 +110,8 @@ def test_bwd_weight_workspace_checks(lb):
 
 def test_workspace_size_queries(lb):
     n = ctypes.c_size_t(7)
-    assert lb.lib.wtconv_workspace_size(ctypes.byref(good(lb, H=6, W=6, L=1)), ctypes.byref(n)) == -8
+    huge = good(lb, H=8192, W=8192, L=4)  # deep levels too large for one workgroup
+    assert lb.lib.wtconv_workspace_size(ctypes.byref(huge), ctypes.byref(n)) == -8
     assert n.value == 7  # untouched on error
     assert lb.lib.wtconv_workspace_size(ctypes.byref(good(lb)), None) == -1
     assert lb.wtconv_workspace_size(good(lb, B=0)) == 0
@@ -136,4 +146,5 @@ def test_fused_bwd_checks(lb):
     assert call(dx=FAKE) == -9              # dx aliases x
     assert call(dx=FAKE2) == -9             # dx aliases dy
     assert call(shape=good(lb, k=2)) == -3
-    assert call(shape=good(lb, H=6, W=6, L=1)) == -8
+    far = [ctypes.c_void_p(n << 40) for n in (1, 2, 3)]  # 1 TiB apart: no overlap
+    assert call(shape=good(lb, H=8192, W=8192, L=4), x=far[0], dy=far[1], dx=far[2]) == -8

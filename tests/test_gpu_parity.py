@@ -140,6 +140,33 @@ def test_tiled_planes(k, L, H, W, dtype):
     assert_parity(d, dtype, "tiled k%d L%d %dx%d %s" % (k, L, H, W, dtype))
 
 
+ANY_SIZE = [  # k, L, H, W, dtype: sides the kernels do not take directly
+    (5, 2, 55, 55, "f32"),    # zero-extended to 56 x 56 (whole planes)
+    (5, 2, 27, 27, "f16"),    # to 28 x 28, fp16
+    (5, 1, 13, 13, "f32"),    # to 14 x 14
+    (3, 3, 30, 17, "f32"),    # to 32 x 24, tiles
+    (7, 2, 6, 10, "f32"),     # to 8 x 12, tiles
+    (5, 3, 56, 56, "f32"),    # L = 3 at 56: divisible, tiles directly
+    (5, 5, 100, 90, "f32"),   # to 128 x 96, tiles plus two deep levels
+    (3, 2, 9, 7, "f16"),      # to 12 x 8, fp16 tiles
+    (1, 1, 5, 3, "f32"),
+]
+
+
+@pytest.mark.parametrize("k,L,H,W,dtype", ANY_SIZE)
+def test_any_size(k, L, H, W, dtype):
+    """Odd grids at some level: the oracle pads every level's grid on its own;
+    the library zero-extends the planes once and crops."""
+    B, C = 3, 4
+    d = wi.make_inputs(B, C, H, W, L, k, dtype, seed=k * 31 + L * 7 + H * 3 + W)
+    g = torch.Generator().manual_seed(13)
+    td = d["x"].dtype
+    d["s_base"] = (1 + 0.5 * torch.randn(C, generator=g)).to(td)
+    d["s_wav"] = (0.3 + 0.5 * torch.randn(L, C, 4, generator=g)).to(td)
+    d["b_base"] = (0.5 * torch.randn(C, generator=g)).to(td)
+    assert_parity(d, dtype, "any-size k%d L%d %dx%d %s" % (k, L, H, W, dtype))
+
+
 def test_single_image_single_channel():
     d = wi.make_inputs(1, 1, 56, 56, 2, 5, "f32", seed=5)
     assert_parity(d, "f32", "B1C1")
