@@ -30,6 +30,11 @@ class Shape(ctypes.Structure):
                 ("dtype", ctypes.c_int)]
 
 
+class DwShape(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int), ("C", ctypes.c_int), ("H", ctypes.c_int),
+                ("W", ctypes.c_int), ("k", ctypes.c_int), ("dtype", ctypes.c_int)]
+
+
 lib = ctypes.CDLL(LIB_PATH)
 _vp = ctypes.c_void_p
 _sp = ctypes.POINTER(Shape)
@@ -43,11 +48,19 @@ lib.wtconv_bwd_weight.argtypes = [_sp] + [_vp] * 12 + [_vp, ctypes.c_size_t, _vp
 lib.wtconv_bwd_weight.restype = ctypes.c_int
 lib.wtconv_bwd.argtypes = [_sp] + [_vp] * 13 + [_vp, ctypes.c_size_t, _vp]
 lib.wtconv_bwd.restype = ctypes.c_int
+_dp = ctypes.POINTER(DwShape)
+lib.dwconv_workspace_size.argtypes = [_dp, ctypes.POINTER(ctypes.c_size_t)]
+lib.dwconv_workspace_size.restype = ctypes.c_int
+lib.dwconv_fwd.argtypes = [_dp] + [_vp] * 5
+lib.dwconv_fwd.restype = ctypes.c_int
+lib.dwconv_bwd.argtypes = [_dp] + [_vp] * 7 + [ctypes.c_size_t, _vp]
+lib.dwconv_bwd.restype = ctypes.c_int
 lib.wtconv_strerror.argtypes = [ctypes.c_int]
 lib.wtconv_strerror.restype = ctypes.c_char_p
 
 EXPORTED = ("wtconv_workspace_size", "wtconv_fwd", "wtconv_bwd_input",
-            "wtconv_bwd_weight", "wtconv_bwd", "wtconv_strerror")
+            "wtconv_bwd_weight", "wtconv_bwd", "wtconv_strerror",
+            "dwconv_workspace_size", "dwconv_fwd", "dwconv_bwd")
 
 
 class WTConvError(RuntimeError):
@@ -172,3 +185,44 @@ def wtconv_bwd(x, dy, w_base, b_base, s_base, w_wav, s_wav, dx=None, grads=None,
         _ptr(w_wav), _ptr(s_wav), _ptr(dx), *[_ptr(grads[n]) for n in GRAD_NAMES],
         _ptr(ws), nws, _stream(stream, x.device)), "wtconv_bwd")
     return dx, grads
+
+
+# ---------------------------------------------------------------------------
+# Plain depthwise conv baseline (include/dwconv.h)
+# ---------------------------------------------------------------------------
+
+def dw_shape_of(x, w):
+    B, C, H, W = x.shape
+    return DwShape(int(B), int(C), int(H), int(W), int(w.shape[-1]), _dtype_code(x.dtype))
+
+
+def dwconv_workspace_size(shape):
+    n = ctypes.c_size_t(0)
+    _check(lib.dwconv_workspace_size(ctypes.byref(shape), ctypes.byref(n)),
+           "dwconv_workspace_size")
+    return int(n.value)
+
+
+def dwconv_fwd(x, w, bias, y=None, stream=None):
+    """y = depthwise conv of x with w [C, 1, k, k] plus bias [C]; returns y."""
+    s = dw_shape_of(x, w)
+    if y is None:
+        y = torch.empty_like(x)
+    _check(lib.dwconv_fwd(ctypes.byref(s), _ptr(x), _ptr(w), _ptr(bias), _ptr(y),
+                          _stream(stream, x.device)), "dwconv_fwd")
+    return y
+
+
+def dwconv_bwd(x, dy, w, dx=None, dw=None, db=None, workspace=None, stream=None):
+    """(dx, dw, db) of the depthwise conv in one pass."""
+    s = dw_shape_of(x, w)
+    dx = torch.empty_like(dy) if dx is None else dx
+    dw = torch.empty_like(w) if dw is None else dw
+    db = torch.empty(w.shape[0], dtype=w.dtype, device=w.device) if db is None else db
+    need = dwconv_workspace_size(s)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=x.device)
+    _check(lib.dwconv_bwd(ctypes.byref(s), _ptr(x), _ptr(dy), _ptr(w), _ptr(dx), _ptr(dw),
+                          _ptr(db), _ptr(workspace), workspace.numel() * workspace.element_size(),
+                          _stream(stream, x.device)), "dwconv_bwd")
+    return dx, dw, db

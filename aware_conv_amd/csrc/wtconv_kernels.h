@@ -465,7 +465,7 @@ struct Fetch {
     static constexpr int NV = FW / V, RB = FH / ROWS;
     static_assert(FW % V == 0 && FH % ROWS == 0, "footprint in whole items");
     static constexpr int ITEMS = G::P * RB * NV, IT = cdiv(ITEMS, G::NT);
-    static constexpr int LEVELS = ROWS == 4 ? 2 : 1;  // levels computed here
+    static constexpr int LEVELS = ROWS == 4 ? 2 : (G::L >= 1 ? 1 : 0);  // levels computed here
     using raw_t = typename RawVec<V * int(sizeof(T))>::type;
     raw_t r[IT][ROWS];
 
@@ -554,31 +554,33 @@ struct Fetch {
 #pragma unroll
                     for (int k = 0; k < ROWS; ++k) lds_put<V, G::al(0)>(o + k * G::pitch(0), x[k]);
                 }
-                float ll[ROWS / 2][V / 2];
+                if constexpr (G::L >= 1) {  // (L = 0: plain depthwise conv)
+                    float ll[ROWS / 2][V / 2];
 #pragma unroll
-                for (int rr = 0; rr < ROWS / 2; ++rr) {
-                    float sub[4][V / 2];
+                    for (int rr = 0; rr < ROWS / 2; ++rr) {
+                        float sub[4][V / 2];
 #pragma unroll
-                    for (int m = 0; m < V / 2; ++m) {
-                        float o[4];
-                        butterfly(x[2 * rr][2 * m], x[2 * rr][2 * m + 1], x[2 * rr + 1][2 * m],
-                                  x[2 * rr + 1][2 * m + 1], o);
-                        ll[rr][m] = o[0];
+                        for (int m = 0; m < V / 2; ++m) {
+                            float o[4];
+                            butterfly(x[2 * rr][2 * m], x[2 * rr][2 * m + 1], x[2 * rr + 1][2 * m],
+                                      x[2 * rr + 1][2 * m + 1], o);
+                            ll[rr][m] = o[0];
 #pragma unroll
-                        for (int sb = 0; sb < 4; ++sb) sub[sb][m] = o[sb];
+                            for (int sb = 0; sb < 4; ++sb) sub[sb][m] = o[sb];
+                        }
+                        put_row<VSIDE, 1, V / 2>(lds, pl, fy / 2 + rr, fx / 2, sub);
                     }
-                    put_row<VSIDE, 1, V / 2>(lds, pl, fy / 2 + rr, fx / 2, sub);
-                }
-                if constexpr (ROWS == 4) {
-                    float sub[4][V / 4];
+                    if constexpr (ROWS == 4) {
+                        float sub[4][V / 4];
 #pragma unroll
-                    for (int m = 0; m < V / 4; ++m) {
-                        float o[4];
-                        butterfly(ll[0][2 * m], ll[0][2 * m + 1], ll[1][2 * m], ll[1][2 * m + 1], o);
+                        for (int m = 0; m < V / 4; ++m) {
+                            float o[4];
+                            butterfly(ll[0][2 * m], ll[0][2 * m + 1], ll[1][2 * m], ll[1][2 * m + 1], o);
 #pragma unroll
-                        for (int sb = 0; sb < 4; ++sb) sub[sb][m] = o[sb];
+                            for (int sb = 0; sb < 4; ++sb) sub[sb][m] = o[sb];
+                        }
+                        put_row<VSIDE, 2, V / 4>(lds, pl, fy / 4, fx / 4, sub);
                     }
-                    put_row<VSIDE, 2, V / 4>(lds, pl, fy / 4, fx / 4, sub);
                 }
             }
         }
@@ -727,44 +729,47 @@ __device__ __forceinline__ void cascade_level(float* lds, int tid) {
 // coefficient is expanded over its 2x2 block.
 template <class G, typename T>
 __device__ __forceinline__ void final_to_lds(float* lds, int tid) {
-    constexpr int V = vec_elems<T>(G::W);
-    constexpr int NV = G::W / V, RP = G::H / 2, ITEMS = G::P * RP * NV;
+    // L = 0 (plain depthwise conv): y is the base conv, already in place
+    if constexpr (G::L >= 1) {
+        constexpr int V = vec_elems<T>(G::W);
+        constexpr int NV = G::W / V, RP = G::H / 2, ITEMS = G::P * RP * NV;
 #pragma unroll
-    for (int it = 0; it < cdiv(ITEMS, G::NT); ++it) {
-        const int item = tid + it * G::NT;
-        if (ITEMS % G::NT == 0 || item < ITEMS) {
-            const int cv = item % NV;
-            const int i = (item / NV) % RP;
-            const int pl = item / (NV * RP);
-            float* x0 = lds + G::uidx(0, pl, 0, 2 * i, cv * V);
-            float r0[V], r1[V], c[4][V / 2];
-            lds_get<V, G::al(0)>(x0, r0);
-            lds_get<V, G::al(0)>(x0 + G::pitch(0), r1);
+        for (int it = 0; it < cdiv(ITEMS, G::NT); ++it) {
+            const int item = tid + it * G::NT;
+            if (ITEMS % G::NT == 0 || item < ITEMS) {
+                const int cv = item % NV;
+                const int i = (item / NV) % RP;
+                const int pl = item / (NV * RP);
+                float* x0 = lds + G::uidx(0, pl, 0, 2 * i, cv * V);
+                float r0[V], r1[V], c[4][V / 2];
+                lds_get<V, G::al(0)>(x0, r0);
+                lds_get<V, G::al(0)>(x0 + G::pitch(0), r1);
 #pragma unroll
-            for (int sb = 0; sb < 4; ++sb)
-                lds_get<V / 2, G::al(1)>(lds + G::uidx(1, pl, sb, i, cv * (V / 2)), c[sb]);
+                for (int sb = 0; sb < 4; ++sb)
+                    lds_get<V / 2, G::al(1)>(lds + G::uidx(1, pl, sb, i, cv * (V / 2)), c[sb]);
 #pragma unroll
-            for (int m = 0; m < V / 2; ++m) {
-                float ll = c[0][m];
-                if constexpr (G::L >= 2) {
-                    constexpr int A2 = G::arr(2);
-                    const int j = cv * (V / 2) + m;
-                    const float* c2 = lds + G::uidx(2, pl, 0, i >> 1, j >> 1);
-                    const float sy2 = (i & 1) ? -1.f : 1.f, sx2 = (j & 1) ? -1.f : 1.f;
-                    const float e2 = fmaf(sy2, c2[2 * A2], c2[0]);
-                    const float f2 = fmaf(sy2, c2[3 * A2], c2[A2]);
-                    ll += fmaf(sx2, f2, e2);
+                for (int m = 0; m < V / 2; ++m) {
+                    float ll = c[0][m];
+                    if constexpr (G::L >= 2) {
+                        constexpr int A2 = G::arr(2);
+                        const int j = cv * (V / 2) + m;
+                        const float* c2 = lds + G::uidx(2, pl, 0, i >> 1, j >> 1);
+                        const float sy2 = (i & 1) ? -1.f : 1.f, sx2 = (j & 1) ? -1.f : 1.f;
+                        const float e2 = fmaf(sy2, c2[2 * A2], c2[0]);
+                        const float f2 = fmaf(sy2, c2[3 * A2], c2[A2]);
+                        ll += fmaf(sx2, f2, e2);
+                    }
+                    const float lh = c[1][m], hl = c[2][m], hh = c[3][m];
+                    const float e0 = ll + hl, f0 = lh + hh;  // row 2i   (row bit 0)
+                    const float e1 = ll - hl, f1 = lh - hh;  // row 2i+1 (row bit 1)
+                    r0[2 * m] += e0 + f0;
+                    r0[2 * m + 1] += e0 - f0;
+                    r1[2 * m] += e1 + f1;
+                    r1[2 * m + 1] += e1 - f1;
                 }
-                const float lh = c[1][m], hl = c[2][m], hh = c[3][m];
-                const float e0 = ll + hl, f0 = lh + hh;  // row 2i   (row bit 0)
-                const float e1 = ll - hl, f1 = lh - hh;  // row 2i+1 (row bit 1)
-                r0[2 * m] += e0 + f0;
-                r0[2 * m + 1] += e0 - f0;
-                r1[2 * m] += e1 + f1;
-                r1[2 * m + 1] += e1 - f1;
+                lds_put<V, G::al(0)>(x0, r0);
+                lds_put<V, G::al(0)>(x0 + G::pitch(0), r1);
             }
-            lds_put<V, G::al(0)>(x0, r0);
-            lds_put<V, G::al(0)>(x0 + G::pitch(0), r1);
         }
     }
 }
@@ -817,9 +822,11 @@ __device__ __forceinline__ void fold_weights(float* wf, const T* __restrict__ wb
     constexpr int KK = G::KK;
     for (int i = tid; i < G::NWF; i += G::NT) {
         float v;
+        // sb == NULL: no base scale (the plain depthwise conv)
+        const float beta = sb ? to_f(sb[c]) : 1.f;
         if (i < KK) {
             const int t = FLIP ? KK - 1 - i : i;
-            v = to_f(sb[c]) * to_f(wb[size_t(c) * KK + t]);
+            v = beta * to_f(wb[size_t(c) * KK + t]);
         } else if (i < G::NWF - 1) {
             const int jj = i - KK, ls = jj / KK, t = jj % KK;
             const int l = ls >> 2, s = ls & 3;
@@ -827,7 +834,7 @@ __device__ __forceinline__ void fold_weights(float* wf, const T* __restrict__ wb
             const size_t gi = (size_t(l) * C + c) * 4 + s;
             v = to_f(sw[gi]) * ldexpf(1.f, -2 * (l + 1)) * to_f(ww[gi * KK + tt]);
         } else {
-            v = FLIP ? 0.f : to_f(sb[c]) * to_f(bb[c]);
+            v = FLIP ? 0.f : beta * to_f(bb[c]);
         }
         wf[i] = v;
     }
@@ -1234,13 +1241,16 @@ __global__ __launch_bounds__(256) void k_bww_final(
         g[i] = s;
     }
     __syncthreads();
-    const float beta = to_f(sb[c]);
+    // sb == NULL: no base scale (the plain depthwise conv), no dsb
+    const float beta = sb ? to_f(sb[c]) : 1.f;
     for (int i = tid; i < KK; i += nt) dwb[size_t(c) * KK + i] = from_f<T>(beta * g[i]);
     if (tid == 0) {
         dbb[c] = from_f<T>(beta * g[KK]);
-        float dot = 0.f;
-        for (int t = 0; t < KK; ++t) dot = fmaf(to_f(wb[size_t(c) * KK + t]), g[t], dot);
-        dsb[c] = from_f<T>(fmaf(to_f(bb[c]), g[KK], dot));
+        if (dsb) {
+            float dot = 0.f;
+            for (int t = 0; t < KK; ++t) dot = fmaf(to_f(wb[size_t(c) * KK + t]), g[t], dot);
+            dsb[c] = from_f<T>(fmaf(to_f(bb[c]), g[KK], dot));
+        }
     }
     for (int i = tid; i < 4 * L * KK; i += nt) {
         const int ls = i / KK, t = i % KK, l = ls >> 2, s = ls & 3;

@@ -35,7 +35,8 @@ Variant make_variant(int dtype) {
 }
 
 // (K, L, H, W, planes per group, threads).  The ConvNeXt-T stage shapes
-// first, then small shapes for edge cases.
+// first, then small shapes for edge cases; L = 0 rows are the plain 7 x 7
+// depthwise conv baseline on the stage shapes (and a small edge case).
 #define WTC_PLANE_VARIANTS(X) \
     X(5, 2, 56, 56, 1, 256)   \
     X(5, 2, 28, 28, 2, 256)   \
@@ -51,7 +52,11 @@ Variant make_variant(int dtype) {
     X(3, 2, 16, 32, 2, 256)   \
     X(5, 4, 32, 32, 1, 256)   \
     X(3, 5, 32, 32, 1, 256)   \
-    X(5, 6, 64, 64, 1, 512)
+    X(5, 6, 64, 64, 1, 512)   \
+    X(7, 0, 56, 56, 1, 256)   \
+    X(7, 0, 28, 28, 4, 256)   \
+    X(7, 0, 14, 14, 8, 256)   \
+    X(7, 0, 12, 20, 2, 256)
 
 const Variant* find_variant(const wtconv_shape& s) {
     static const Variant table[] = {

@@ -22,6 +22,10 @@ Also reported, on the same JSON line:
                else null
   cpu_baseline the fp64 oracle (test infrastructure, timed as it stands) on
                the host cores, on the same workload, about ten seconds of work
+  dw7x7_baseline  the plain 7x7 depthwise conv with bias (include/dwconv.h,
+               the layer WTConv replaces) timed the same way on the same
+               activations: forward + one-pass backward per step, and the
+               WTConv/dw7x7 throughput ratios for training and inference
 """
 import argparse
 import hashlib
@@ -152,6 +156,48 @@ def cpu_baseline(wl, min_seconds=10.0):
             "sample": "%d full %s batch(es) of %d images (fwd + bwd), fp64, %.1f s" % (reps, wl.name, wl.B, el)}
 
 
+def dw7_baseline(L, torch, sets, wl, warmup, steps, stream):
+    """Step time of the 7x7 depthwise conv (forward + fused backward) on the
+    same rotated activations, or None when the shape has no kernel."""
+    k = 7
+    dev = sets[0]["x"].device
+    g = torch.Generator().manual_seed(1)
+    w = (0.02 * torch.randn(wl.C, 1, k, k, generator=g)).to(sets[0]["x"].dtype).to(dev)
+    b = (0.02 * torch.randn(wl.C, generator=g)).to(sets[0]["x"].dtype).to(dev)
+    try:
+        need = L.dwconv_workspace_size(L.dw_shape_of(sets[0]["x"], w))
+    except L.WTConvError:
+        return None
+    ws = torch.empty(max(16, need), dtype=torch.uint8, device=dev)
+    dw, db = torch.empty_like(w), torch.empty_like(b)
+
+    def step(t, ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        L.dwconv_fwd(t["x"], w, b, y=t["y"], stream=stream)
+        if ev is not None:
+            ev[1].record(stream)
+        L.dwconv_bwd(t["x"], t["dy"], w, dx=t["dx"], dw=dw, db=db, workspace=ws, stream=stream)
+        if ev is not None:
+            ev[2].record(stream)
+
+    for i in range(warmup):
+        step(sets[i % len(sets)])
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step(sets[i % len(sets)], evs[i])
+    torch.cuda.synchronize()
+    el = time.perf_counter() - t0
+    fwd_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / steps
+    bwd_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / steps
+    return {"k": k, "ms_per_step": round(el * 1e3 / steps, 4),
+            "images_per_s": round(wl.B * steps / el, 1),
+            "per_call_ms": {"dwconv_fwd": round(fwd_ms, 5), "dwconv_bwd": round(bwd_ms, 5)},
+            "inference_images_per_s": round(wl.B / (fwd_ms * 1e-3), 1)}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -162,6 +208,8 @@ def main():
     ap.add_argument("--backward", choices=("fused", "split"), default="fused",
                     help="fused: wtconv_bwd; split: wtconv_bwd_input + wtconv_bwd_weight")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-dw-baseline", action="store_true",
+                    help="skip the 7x7 depthwise conv baseline")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a plain device copy of the step's input size "
                          "(calibrates rocprofv3 byte counters)")
@@ -249,6 +297,10 @@ def main():
     per = {c: [e[i].elapsed_time(e[i + 1]) for e in evs] for i, c in enumerate(calls)}
     avg_ms = {k: sum(v) / len(v) for k, v in per.items()}
 
+    dw = None
+    if not args.no_dw_baseline:
+        dw = dw7_baseline(L, torch, sets, wl, args.warmup, args.steps, stream)
+
     if args.copy_probe:
         src = torch.ones(COPY_PROBE_BYTES // 4, dtype=torch.float32, device=dev)
         dst = torch.empty_like(src)
@@ -312,6 +364,11 @@ def main():
             "algo_bytes_per_launch": algo_bytes[dom],
         },
     }
+    if dw is not None:
+        dw["wtconv_over_dw_train"] = round(value / dw["images_per_s"], 3)
+        dw["wtconv_over_dw_infer"] = round(rec["inference_images_per_s"] /
+                                           dw["inference_images_per_s"], 3)
+        rec["dw7x7_baseline"] = dw
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(wl)
     print(json.dumps(rec), flush=True)

@@ -20,8 +20,12 @@ def lb():
 
 
 def declared_functions():
-    src = open(os.path.join(ROOT, "include", "wtconv.h")).read()
-    return sorted(set(re.findall(r"^\s*(?:int|const char\*)\s+(wtconv_\w+)\s*\(", src, re.M)))
+    names = set()
+    for h in sorted(os.listdir(os.path.join(ROOT, "include"))):
+        if h.endswith(".h"):
+            src = open(os.path.join(ROOT, "include", h)).read()
+            names |= set(re.findall(r"^\s*(?:int|const char\*)\s+(\w+)\s*\(", src, re.M))
+    return sorted(names)
 
 
 def test_exports_every_declared_symbol(lb):
@@ -148,3 +152,20 @@ def test_fused_bwd_checks(lb):
     assert call(shape=good(lb, k=2)) == -3
     far = [ctypes.c_void_p(n << 40) for n in (1, 2, 3)]  # 1 TiB apart: no overlap
     assert call(shape=good(lb, H=8192, W=8192, L=4), x=far[0], dy=far[1], dx=far[2]) == -8
+
+
+def test_dwconv_checks(lb):
+    s = lb.DwShape(2, 8, 56, 56, 7, lb.WTCONV_F32)
+    f, b = lb.lib.dwconv_fwd, lb.lib.dwconv_bwd
+    assert f(ctypes.byref(s), FAKE, FAKE, FAKE, FAKE, None) == -9      # y aliases x
+    assert f(ctypes.byref(s), None, FAKE, FAKE, FAKE2, None) == -1
+    assert f(ctypes.byref(s), MIS, FAKE, FAKE, FAKE2, None) == -6
+    assert f(ctypes.byref(lb.DwShape(2, 8, 56, 56, 6, 0)), FAKE, FAKE, FAKE, FAKE2, None) == -3
+    assert f(ctypes.byref(lb.DwShape(2, 8, 57, 56, 7, 0)), FAKE, FAKE, FAKE, FAKE2, None) == -8
+    assert f(ctypes.byref(lb.DwShape(-1, 8, 56, 56, 7, 0)), FAKE, FAKE, FAKE, FAKE2, None) == -2
+    need = lb.dwconv_workspace_size(s)
+    assert need > 0
+    DX = ctypes.c_void_p(0x300000)
+    assert b(ctypes.byref(s), FAKE, FAKE2, FAKE, DX, FAKE, FAKE, FAKE, need - 1, None) == -7
+    assert b(ctypes.byref(s), FAKE, FAKE2, FAKE, FAKE2, FAKE, FAKE, FAKE, need, None) == -9
+    assert b(ctypes.byref(s), FAKE, FAKE2, FAKE, None, FAKE, FAKE, FAKE, need, None) == -1
