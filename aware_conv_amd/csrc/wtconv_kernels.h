@@ -1100,18 +1100,41 @@ constexpr size_t bwd_lds_bytes() {
     return a > b ? a : b;
 }
 
-// Fused backward: input gradient and weight-gradient partials of channel
-// blockIdx.x % C over the groups of chunk blockIdx.x / C, reading x and dy
-// once.  dy and x are analysed side by side in LDS; each lane reads the dy
-// window of its tile for the rotated-filter conv of the input gradient, keeps
-// the window's centre (its tile of dy, or of V^l_s) and correlates it with
-// the x window of the same tile for the weight gradient.  The input gradient
-// then goes through the same synthesis and deferred store as the forward.
-template <int K, int L, int H, int W, int P, int NT, typename T>
-__global__ __launch_bounds__(NT) void k_plane_bwd(
+// Rows of weight-gradient partials written by the fused backward.  The
+// C * ceil(B/P) (channel, group) items, channel-major, are split into nwg
+// equal contiguous ranges, one per workgroup; a workgroup writes one row for
+// each channel its range touches, so channel c has rows from workgroups
+// owner(c*ng) .. owner((c+1)*ng - 1), stored at row c * rmax + (w - first).
+struct LinearRows {
+    long total;  // items
+    int nwg, ng, rmax;
+    __host__ __device__ long q0(int w) const { return total * w / nwg; }
+    // the workgroup whose range holds item q
+    __host__ __device__ int owner(long q) const { return int(((q + 1) * nwg - 1) / total); }
+    __host__ __device__ int first(int c) const { return owner(long(c) * ng); }
+    __host__ __device__ int count(int c) const {
+        return owner(long(c + 1) * ng - 1) - first(c) + 1;
+    }
+};
+
+// Fused backward: input gradient and weight-gradient partials reading x and
+// dy once.  Workgroup w takes the items [q0(w), q0(w+1)) of LinearRows.
+// dy and x are analysed side by side in LDS; each lane reads the dy window
+// of its tile for the rotated-filter conv of the input gradient, keeps the
+// window's centre (its tile of dy, or of V^l_s) and correlates it with the x
+// window of the same tile for the weight gradient.  The input gradient then
+// goes through the same synthesis and deferred store as the forward.  With
+// CROSS, a range may span channels: entering a new channel, the finished
+// channel's taps are reduced to its row and the filters are folded again;
+// without, every range lies in one channel (nwg a multiple of C) and the
+// loop carries none of that.
+// Two workgroups per compute unit fit its LDS at the stage shapes: the
+// register budget is held to that occupancy.
+template <int K, int L, int H, int W, int P, int NT, typename T, bool CROSS>
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void k_plane_bwd(
     const T* __restrict__ x, const T* __restrict__ dy, const T* __restrict__ wb,
     const T* __restrict__ sb, const T* __restrict__ ww, const T* __restrict__ sw,
-    T* __restrict__ dx, float* __restrict__ part, int B, int C, int gpw) {
+    T* __restrict__ dx, float* __restrict__ part, int B, int C, LinearRows rows) {
     using G = GeoGrad<K, L, H, W, P, NT>;
     using F = Fetch<G, T>;
     constexpr int KK = G::KK, Q = G::Q, R = G::R, DY = bwd_dy_base<G>();
@@ -1119,19 +1142,18 @@ __global__ __launch_bounds__(NT) void k_plane_bwd(
     float* ldy = lds + DY;
     float* wf = ldy + G::side;
     const int tid = threadIdx.x;
-    const int c = blockIdx.x % C;
-    const int chunk = blockIdx.x / C;
     const int ngroups = cdiv(B, P);
-    const int g0 = chunk * gpw;
-    const int g1 = min(g0 + gpw, ngroups);
+    const long q0 = rows.q0(blockIdx.x);
+    const int nitems = int(rows.q0(blockIdx.x + 1) - q0);
+    // (channel, group) of the range's first item; later items step through
+    // the groups without divisions
+    int c = int(q0 / ngroups), grp = int(q0 % ngroups);
     F fx, fd;
-    if (g0 < g1) {
-        fx.issue(x, g0 * P, B, C, c, tid);
-        fd.issue(dy, g0 * P, B, C, c, tid);
+    if (nitems > 0) {
+        fx.issue(x, grp * P, B, C, c, tid);
+        fd.issue(dy, grp * P, B, C, c, tid);
     }
     for (int i = tid; i < DY + G::side; i += NT) lds[i] = 0.f;
-    fold_weights<G, T, true>(wf, wb, wb, sb, ww, sw, C, c, tid);
-    __syncthreads();
 
     const Job job = decode_job<G>(tid);
     const int wsrc = job.lvl == 0 ? 0 : KK * (1 + (job.lvl - 1) * 4 + job.s);
@@ -1144,20 +1166,48 @@ __global__ __launch_bounds__(NT) void k_plane_bwd(
     const bool full = nrows == Q && ncols == R;
     const int dst = win + G::p * pitch + G::p;
     float w[KK];
-#pragma unroll
-    for (int t = 0; t < KK; ++t) w[t] = wf[wsrc + t];
     float gacc[KK];
-#pragma unroll
-    for (int t = 0; t < KK; ++t) gacc[t] = 0.f;
     float sdy = 0.f;
+    int cur = -1, pend_b0 = -1, pend_c = 0;
+    if constexpr (!CROSS) {
+        // one channel for the whole range: fold once, before the loop
+        fold_weights<G, T, true>(wf, wb, wb, sb, ww, sw, C, c, tid);
+        __syncthreads();
+#pragma unroll
+        for (int t = 0; t < KK; ++t) w[t] = wf[wsrc + t];
+#pragma unroll
+        for (int t = 0; t < KK; ++t) gacc[t] = 0.f;
+        cur = c;
+    }
 
-    int pend_b0 = -1;
-    for (int g = g0; g < g1; ++g) {
-        const int b0 = g * P;
+    for (int it = 0; it < nitems; ++it) {
+        const int b0 = grp * P;
         wait_vmem();
         if (pend_b0 >= 0) {
-            store_out<G, T>(ldy, dx, pend_b0, B, C, c, tid);
+            store_out<G, T>(ldy, dx, pend_b0, B, C, pend_c, tid);
             __syncthreads();
+        }
+        if (CROSS && c != cur) {
+            if (cur >= 0) {
+                // the finished channel's row (its last dx is stored); the
+                // arrays the reduction used are zeroed again and the filters
+                // folded again below
+                reduce_row<G>(lds, gacc, sdy,
+                              part + (size_t(cur) * rows.rmax + (blockIdx.x - rows.first(cur))) *
+                                         G::NPART,
+                              G::NPART, tid);
+                __syncthreads();
+                constexpr int RED = NT * (KK + 1) < DY + G::side ? NT * (KK + 1) : DY + G::side;
+                for (int i = tid; i < RED; i += NT) lds[i] = 0.f;
+            }
+            fold_weights<G, T, true>(wf, wb, wb, sb, ww, sw, C, c, tid);
+            __syncthreads();
+#pragma unroll
+            for (int t = 0; t < KK; ++t) w[t] = wf[wsrc + t];
+#pragma unroll
+            for (int t = 0; t < KK; ++t) gacc[t] = 0.f;
+            sdy = 0.f;
+            cur = c;
         }
         fx.template commit<true, false>(lds, tid);
         fd.template commit<true, false>(ldy, tid);
@@ -1180,9 +1230,11 @@ __global__ __launch_bounds__(NT) void k_plane_bwd(
                     for (int j = 0; j < R; ++j) sdy += d[qq][j];
             corr_tile<K, Q, R>(d, lds + win, pitch, gacc);
         }
-        if (g + 1 < g1) {
-            fx.issue(x, b0 + P, B, C, c, tid);
-            fd.issue(dy, b0 + P, B, C, c, tid);
+        const bool wrap = grp + 1 == ngroups;
+        const int cn = wrap ? c + 1 : c, gn = wrap ? 0 : grp + 1;
+        if (it + 1 < nitems) {
+            fx.issue(x, gn * P, B, C, cn, tid);
+            fd.issue(dy, gn * P, B, C, cn, tid);
         }
         __syncthreads();
         if (job.on) {
@@ -1206,35 +1258,47 @@ __global__ __launch_bounds__(NT) void k_plane_bwd(
         });
         final_to_lds<G, T>(ldy, tid);
         pend_b0 = b0;
+        pend_c = c;
+        c = cn;
+        grp = gn;
         __syncthreads();
     }
     if (pend_b0 >= 0) {
-        store_out<G, T>(ldy, dx, pend_b0, B, C, c, tid);
+        store_out<G, T>(ldy, dx, pend_b0, B, C, pend_c, tid);
         __syncthreads();
     }
-    reduce_row<G>(lds, gacc, sdy, part + (size_t(chunk) * C + c) * G::NPART, G::NPART, tid);
+    if (cur >= 0)
+        reduce_row<G>(lds, gacc, sdy,
+                      part + (size_t(cur) * rows.rmax + (blockIdx.x - rows.first(cur))) * G::NPART,
+                      G::NPART, tid);
 }
 
-// Sum the partial rows of every chunk in order and apply the chain rule
+// Sum the partial rows of each channel in order and apply the chain rule
 // through the fold: dKb = beta G_b, dbias = beta sum dy,
 // dbeta = <Kb, G_b> + bias sum dy, dK[l,s] = gamma 4^-l G[l,s],
-// dgamma[l,s] = 4^-l <K[l,s], G[l,s]>.  nchunk = 0 gives zero gradients.
+// dgamma[l,s] = 4^-l <K[l,s], G[l,s]>.  Rows of channel c: with
+// rows.nwg = 0, `nchunk` rows at (chunk * C + c); otherwise the LinearRows
+// rows of c.  nchunk = 0 (and rows.nwg = 0) gives zero gradients.
 template <typename T>
 __global__ __launch_bounds__(256) void k_bww_final(
-    const float* __restrict__ part, int nchunk, int C, int K, int L, const T* __restrict__ wb,
-    const T* __restrict__ bb, const T* __restrict__ sb, const T* __restrict__ ww,
-    const T* __restrict__ sw, T* __restrict__ dwb, T* __restrict__ dbb, T* __restrict__ dsb,
-    T* __restrict__ dww, T* __restrict__ dsw) {
+    const float* __restrict__ part, int nchunk, LinearRows rows, int C, int K, int L,
+    const T* __restrict__ wb, const T* __restrict__ bb, const T* __restrict__ sb,
+    const T* __restrict__ ww, const T* __restrict__ sw, T* __restrict__ dwb,
+    T* __restrict__ dbb, T* __restrict__ dsb, T* __restrict__ dww, T* __restrict__ dsw) {
     extern __shared__ float g[];
     const int KK = K * K, NPART = KK + 1 + 4 * L * KK;
     const int c = blockIdx.x, tid = threadIdx.x, nt = blockDim.x;
+    const bool lin = rows.nwg > 0;
+    const int nrow = lin ? rows.count(c) : nchunk;
+    const size_t base = lin ? size_t(c) * rows.rmax : size_t(c);
+    const size_t step = lin ? 1 : size_t(C);
     for (int i = tid; i < NPART; i += nt) {
         float v[8];
         float s = 0.f;
-        for (int ch0 = 0; ch0 < nchunk; ch0 += 8) {
+        for (int ch0 = 0; ch0 < nrow; ch0 += 8) {
 #pragma unroll
             for (int u = 0; u < 8; ++u)
-                v[u] = ch0 + u < nchunk ? part[(size_t(ch0 + u) * C + c) * NPART + i] : 0.f;
+                v[u] = ch0 + u < nrow ? part[(base + size_t(ch0 + u) * step) * NPART + i] : 0.f;
 #pragma unroll
             for (int u = 0; u < 8; ++u) s += v[u];
         }

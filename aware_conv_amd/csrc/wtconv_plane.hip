@@ -1,72 +1,24 @@
-// Whole-plane variants of the fused WTConv kernels: the variant table,
-// launch sizing and the host entry points for shapes whose planes fit LDS.
-#include "wtconv_kernels.h"
+// Whole-plane kernels of the fused WTConv layer: variant lookup, launch
+// sizing and the host entry points for shapes whose planes fit LDS.
+#include "wtconv_plane_variant.h"
 
 namespace wtc {
 namespace {
 using namespace dev;
 
-struct Variant {
-    int K, L, H, W, dtype, P, NT;
-    const void* fwd;
-    const void* bwi;
-    const void* bww;
-    const void* bwd;  // fused backward, NULL where its LDS does not fit
-    size_t lds_apply, lds_bww, lds_bwd;
-};
-
-constexpr size_t kMaxLds = 163840;  // LDS of one gfx950 compute unit
-
-template <int K, int L, int H, int W, int P, int NT, typename T>
-Variant make_variant(int dtype) {
-    using G = Geo<K, L, H, W, P, NT>;
-    using GG = GeoGrad<K, L, H, W, P, NT>;
-    const size_t la = apply_lds_bytes<G>();
-    const size_t lb = bww_lds_bytes<GG>();
-    constexpr size_t ld = bwd_lds_bytes<GG>();
-    const void* fused = nullptr;
-    if constexpr (ld <= kMaxLds)
-        fused = reinterpret_cast<const void*>(&k_plane_bwd<K, L, H, W, P, NT, T>);
-    return Variant{K, L, H, W, dtype, P, NT,
-                   reinterpret_cast<const void*>(&k_plane_apply<K, L, H, W, P, NT, T, false>),
-                   reinterpret_cast<const void*>(&k_plane_apply<K, L, H, W, P, NT, T, true>),
-                   reinterpret_cast<const void*>(&k_plane_bww<K, L, H, W, P, NT, T>),
-                   fused, la, lb, ld};
-}
-
-// (K, L, H, W, planes per group, threads).  The ConvNeXt-T stage shapes
-// first, then small shapes for edge cases; L = 0 rows are the plain 7 x 7
-// depthwise conv baseline on the stage shapes (and a small edge case).
-#define WTC_PLANE_VARIANTS(X) \
-    X(5, 2, 56, 56, 1, 256)   \
-    X(5, 2, 28, 28, 2, 256)   \
-    X(5, 1, 14, 14, 8, 256)   \
-    X(5, 2, 32, 32, 1, 256)   \
-    X(1, 1, 8, 8, 8, 256)     \
-    X(3, 1, 8, 8, 8, 256)     \
-    X(3, 2, 16, 16, 4, 256)   \
-    X(3, 3, 16, 16, 4, 256)   \
-    X(5, 3, 16, 16, 4, 256)   \
-    X(7, 2, 16, 16, 4, 256)   \
-    X(7, 1, 14, 14, 8, 256)   \
-    X(3, 2, 16, 32, 2, 256)   \
-    X(5, 4, 32, 32, 1, 256)   \
-    X(3, 5, 32, 32, 1, 256)   \
-    X(5, 6, 64, 64, 1, 512)   \
-    X(7, 0, 56, 56, 1, 256)   \
-    X(7, 0, 28, 28, 4, 256)   \
-    X(7, 0, 14, 14, 8, 256)   \
-    X(7, 0, 12, 20, 2, 256)
+using Variant = PlaneVariant;
 
 const Variant* find_variant(const wtconv_shape& s) {
-    static const Variant table[] = {
-#define WTC_X(K, L, H, W, P, NT) make_variant<K, L, H, W, P, NT, float>(WTCONV_F32), \
-                                 make_variant<K, L, H, W, P, NT, __half>(WTCONV_F16),
-        WTC_PLANE_VARIANTS(WTC_X)
-#undef WTC_X
-    };
-    for (const Variant& v : table)
-        if (v.K == s.k && v.L == s.L && v.H == s.H && v.W == s.W && v.dtype == s.dtype) return &v;
+    const PlaneVariant* (*parts[])(int*) = {plane_table_0, plane_table_1, plane_table_2,
+                                            plane_table_3};
+    for (auto part : parts) {
+        int n = 0;
+        const Variant* t = part(&n);
+        for (int i = 0; i < n; ++i)
+            if (t[i].K == s.k && t[i].L == s.L && t[i].H == s.H && t[i].W == s.W &&
+                t[i].dtype == s.dtype)
+                return &t[i];
+    }
     return nullptr;
 }
 
@@ -106,14 +58,30 @@ int bww_chunks(const wtconv_shape& s, int P, int slots) {
 
 bool plane_supported(const wtconv_shape& s) { return find_variant(s) != nullptr; }
 
+// Fused backward: workgroups over balanced ranges of (channel, group)
+// items, at most this many (a compute unit holds at most 8 of them).
+constexpr int kMaxBwdWGs = 2048;
+
+// Upper bound of the partial rows per channel of the fused backward for any
+// workgroup count up to kMaxBwdWGs (ranges of at least floor(T / nwg) items).
+int bwd_rows_bound(const wtconv_shape& s, int P) {
+    const long ng = cdiv(s.B, P), total = ng * s.C;
+    const long nwg = total < kMaxBwdWGs ? total : kMaxBwdWGs;
+    const long per = total / (nwg > 0 ? nwg : 1);
+    long r = (ng + per - 1) / (per > 0 ? per : 1) + 1;
+    if (r > ng) r = ng;
+    return int(r);
+}
+
 size_t plane_workspace_bytes(const wtconv_shape& s) {
     const Variant* v = find_variant(s);
     if (!v || s.B == 0 || s.C == 0) return 0;
     const int ngroups = cdiv(s.B, v->P);
     const int nchunk = ngroups < kMaxChunks ? ngroups : kMaxChunks;
+    const int rows = nchunk > bwd_rows_bound(s, v->P) ? nchunk : bwd_rows_bound(s, v->P);
     const int KK = s.k * s.k;
     const size_t npart = size_t(KK) + 1 + size_t(4) * s.L * KK;
-    return size_t(nchunk) * s.C * npart * sizeof(float);
+    return size_t(rows) * s.C * npart * sizeof(float);
 }
 
 hipError_t plane_apply(const wtconv_shape& s, const void* in, const Params& p, void* out,
@@ -140,11 +108,12 @@ hipError_t plane_apply(const wtconv_shape& s, const void* in, const Params& p, v
 
 namespace {
 template <typename T>
-hipError_t launch_final(const wtconv_shape& s, const float* part, int nchunk, const Params& p,
-                        const Grads& g, hipStream_t stream) {
+hipError_t launch_final(const wtconv_shape& s, const float* part, int nchunk,
+                        const LinearRows& rows, const Params& p, const Grads& g,
+                        hipStream_t stream) {
     const int KK = s.k * s.k;
     const size_t lds = sizeof(float) * (size_t(KK) + 1 + size_t(4) * s.L * KK);
-    hipLaunchKernelGGL(k_bww_final<T>, dim3(s.C), dim3(256), lds, stream, part, nchunk, s.C,
+    hipLaunchKernelGGL(k_bww_final<T>, dim3(s.C), dim3(256), lds, stream, part, nchunk, rows, s.C,
                        s.k, s.L, (const T*)p.w_base, (const T*)p.b_base, (const T*)p.s_base,
                        (const T*)p.w_wav, (const T*)p.s_wav, (T*)g.dw_base, (T*)g.db_base,
                        (T*)g.ds_base, (T*)g.dw_wav, (T*)g.ds_wav);
@@ -154,8 +123,9 @@ hipError_t launch_final(const wtconv_shape& s, const float* part, int nchunk, co
 
 hipError_t finalize_grads(const wtconv_shape& s, const float* part, int rows, const Params& p,
                           const Grads& g, hipStream_t stream) {
-    return s.dtype == WTCONV_F32 ? launch_final<float>(s, part, rows, p, g, stream)
-                                 : launch_final<__half>(s, part, rows, p, g, stream);
+    const LinearRows none{1, 0, 0, 0};
+    return s.dtype == WTCONV_F32 ? launch_final<float>(s, part, rows, none, p, g, stream)
+                                 : launch_final<__half>(s, part, rows, none, p, g, stream);
 }
 
 hipError_t plane_bwd_weight(const wtconv_shape& s, const void* x, const void* dy,
@@ -187,19 +157,41 @@ hipError_t plane_bwd(const wtconv_shape& s, const void* x, const void* dy, const
     }
     hipError_t e = prepare(v->bwd, v->lds_bwd);
     if (e != hipSuccess) return e;
-    const int nchunk = bww_chunks(s, v->P, resident_wgs(v->bwd, v->NT, v->lds_bwd));
-    int gpw = cdiv(cdiv(s.B, v->P), nchunk), B = s.B, C = s.C;
+    const int ngroups = cdiv(s.B, v->P);
+    const long total = long(ngroups) * s.C;
+    long nwg = resident_wgs(v->bwd, v->NT, v->lds_bwd);
+    if (nwg > kMaxBwdWGs) nwg = kMaxBwdWGs;
+    // a multiple of C puts every range inside one channel, which the kernel
+    // without mid-range reductions runs faster: take it when it keeps at
+    // least 7/8 of the resident slots (or covers every item)
+    const long per_c = nwg / s.C;
+    bool cross = true;
+    if (per_c >= 1 && per_c * s.C * 8 >= nwg * 7) {
+        nwg = per_c * s.C;
+        cross = false;
+    }
+    if (nwg >= total) {
+        nwg = total;  // one item per range: inside one channel
+        cross = false;
+    }
+    LinearRows rows{total, int(nwg), ngroups, 0};
+    for (int c = 0; c < s.C; ++c)
+        if (rows.count(c) > rows.rmax) rows.rmax = rows.count(c);
+    if (rows.rmax > bwd_rows_bound(s, v->P)) return hipErrorInvalidValue;  // workspace
+    int B = s.B, C = s.C;
     float* part = static_cast<float*>(workspace);
     const void* wb = p.w_base;
     const void* sb = p.s_base;
     const void* ww = p.w_wav;
     const void* sw = p.s_wav;
-    void* args[] = {&x, &dy, &wb, &sb, &ww, &sw, &dx, &part, &B, &C, &gpw};
-    e = hipLaunchKernel(v->bwd, dim3(unsigned(nchunk) * unsigned(s.C)), dim3(v->NT), args,
-                        v->lds_bwd, stream);
+    void* args[] = {&x, &dy, &wb, &sb, &ww, &sw, &dx, &part, &B, &C, &rows};
+    const void* fn = cross ? v->bwd_cross : v->bwd;
+    if (cross && (e = prepare(fn, v->lds_bwd)) != hipSuccess) return e;
+    e = hipLaunchKernel(fn, dim3(unsigned(nwg)), dim3(v->NT), args, v->lds_bwd, stream);
     if (e == hipSuccess) e = hipGetLastError();
     if (e != hipSuccess) return e;
-    return finalize_grads(s, part, nchunk, p, g, stream);
+    return s.dtype == WTCONV_F32 ? launch_final<float>(s, part, 0, rows, p, g, stream)
+                                 : launch_final<__half>(s, part, 0, rows, p, g, stream);
 }
 
 hipError_t zero_grads(const wtconv_shape& s, const Params& p, const Grads& g,

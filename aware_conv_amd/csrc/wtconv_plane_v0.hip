@@ -1,0 +1,18 @@
+// Part 0 of the whole-plane variant table.
+#include "wtconv_plane_variant.h"
+
+namespace wtc {
+
+// The ConvNeXt-T stage shapes.
+const PlaneVariant* plane_table_0(int* n) {
+    static const PlaneVariant table[] = {
+        WTC_PLANE_ROW(5, 2, 56, 56, 1, 256)
+        WTC_PLANE_ROW(5, 2, 28, 28, 2, 256)
+        WTC_PLANE_ROW(5, 1, 14, 14, 8, 256)
+        WTC_PLANE_ROW(5, 2, 32, 32, 1, 256)
+    };
+    *n = int(sizeof(table) / sizeof(table[0]));
+    return table;
+}
+
+}  // namespace wtc
