@@ -243,11 +243,10 @@ int backward(const wtconv_shape* s, const void* x, const void* dy, const void* w
         err = fused ? wtc::plane_bwd(r, xr, dyr, p, dxr, g, workspace, st)
                     : wtc::plane_bwd_weight(r, xr, dyr, p, g, workspace, st);
     } else {
-        // tiles of large planes: the input gradient, then the weight
-        // gradient, one after the other on the stream (both use the
-        // workspace)
-        if (fused) err = wtc::tile_apply(r, dyr, p, dxr, true, workspace, st);
-        if (err == hipSuccess) err = wtc::tile_bwd_weight(r, xr, dyr, p, g, workspace, st);
+        // tiles of large planes: both passes one after the other on the
+        // stream, sharing the box sums of dy
+        err = fused ? wtc::tile_bwd(r, xr, dyr, p, dxr, g, workspace, st)
+                    : wtc::tile_bwd_weight(r, xr, dyr, p, g, workspace, st);
     }
     if (err == hipSuccess && fused && pl.padded)
         err = wtc::copy_planes(dxr, dx, planes_of(s), r.H, r.W, s->H, s->W, s->dtype, st);

@@ -59,6 +59,10 @@ hipError_t tile_apply(const wtconv_shape& s, const void* in, const Params& p, vo
 hipError_t tile_bwd_weight(const wtconv_shape& s, const void* x, const void* dy,
                            const Params& p, const Grads& g, void* workspace,
                            hipStream_t stream);
+// Both gradients: the weight gradient, then the input gradient (the box sums
+// of dy computed for the first serve the deep levels of the second).
+hipError_t tile_bwd(const wtconv_shape& s, const void* x, const void* dy, const Params& p,
+                    void* dx, const Grads& g, void* workspace, hipStream_t stream);
 
 // Planes of Hs x Ws -> planes of Hd x Wd: the top-left min(Hs,Hd) x
 // min(Ws,Wd) corner copied, zeros elsewhere (zero extension or cropping).

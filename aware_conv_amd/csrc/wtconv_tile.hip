@@ -18,13 +18,21 @@
 namespace wtc {
 namespace dev {
 
+// Outputs per work item along a row of a deep conv, and row chunks per
+// (level, subband, tap row) of a deep correlation.
+constexpr int kDeepRS = 8, kDeepNCH = 6;
+
 // LDS plan of a deep workgroup (floats): folded filters, then per level m of
 // P (m = 0: P itself) a bordered x-side array set, then unbordered results.
+// Rows are padded to whole kDeepRS segments so that a segment's window stays
+// in its row.
 struct DeepLayout {
     int hp, wp, p, LD, KK;
     __host__ __device__ int h(int m) const { return hp >> m; }
     __host__ __device__ int w(int m) const { return wp >> m; }
-    __host__ __device__ int bp(int m) const { return w(m) + 2 * p; }           // bordered pitch
+    __host__ __device__ int bp(int m) const {  // bordered pitch
+        return (w(m) + kDeepRS - 1) / kDeepRS * kDeepRS + 2 * p;
+    }
     __host__ __device__ int barr(int m) const { return (h(m) + 2 * p) * bp(m); }
     __host__ __device__ int nsub(int m) const { return m ? 4 : 1; }
     __host__ __device__ int wf() const { return 0; }
@@ -40,23 +48,52 @@ struct DeepLayout {
     }
     __host__ __device__ int end_apply() const { return coff(LD + 1); }
     __host__ __device__ int end_bww() const { return uoff(LD + 1) * 2 - LD * 4 * KK; }
+    // correlation partials after the two array sets: [item][K]
+    __host__ __device__ int end_bww_red(int K) const {
+        return end_bww() + LD * 4 * K * kDeepNCH * K;
+    }
     __host__ __device__ int u(int m, int s, int i, int j) const {
         return uoff(m) + s * barr(m) + (i + p) * bp(m) + p + j;
     }
 };
 
-// P[i][j] = sum of the 2^LT x 2^LT block of the plane -> bordered array m = 0.
+// P = U^LT_LL of every plane: P[i][j] is the sum of the plane's 2^LT x 2^LT
+// block (i, j).  One workgroup per row of P; each lane sums a 4-column strip
+// of the block rows with one vector load per row, then the n/4 lanes of a
+// block add their strips with cross-lane exchanges (n = 2^LT >= 4).
 template <typename T>
-__device__ void box_sums(const T* __restrict__ src, int Wp, int LT, const DeepLayout& D,
-                         float* lds, int base, int tid, int nt) {
-    const int n = 1 << LT;
+__global__ __launch_bounds__(128) void k_box_sums(const T* __restrict__ src,
+                                                  float* __restrict__ P, int Hp, int Wp,
+                                                  int LT) {
+    const int n = 1 << LT, hd = Hp >> LT, wd = Wp >> LT;
+    const int row = blockIdx.x % hd;
+    const size_t plane = blockIdx.x / hd;
+    const T* s0 = src + (plane * Hp + size_t(row) * n) * Wp;
+    float* out = P + (plane * hd + row) * wd;
+    const int nq = Wp / 4, per = n / 4;  // quads per row, quads per block
+    for (int q0 = 0; q0 < nq; q0 += blockDim.x) {
+        const int q = q0 + threadIdx.x;
+        float acc = 0.f;
+        if (q < nq) {
+            for (int r = 0; r < n; ++r) {
+                float v[4];
+                load_vec<T, 4>(s0 + size_t(r) * Wp + 4 * q, v);
+                acc += (v[0] + v[1]) + (v[2] + v[3]);
+            }
+        }
+        // lanes q, q^1, ... of one block are in one wavefront and either all
+        // hold a quad or none does (nq is a multiple of per)
+        for (int k = 1; k < per; k <<= 1) acc += __shfl_xor(acc, k);
+        if (q < nq && (q % per) == 0) out[q / per] = acc;
+    }
+}
+
+// P of one plane -> bordered array m = 0.
+__device__ void load_p(const float* __restrict__ Pp, const DeepLayout& D, float* lds, int base,
+                       int tid, int nt) {
     for (int e = tid; e < D.hp * D.wp; e += nt) {
         const int i = e / D.wp, j = e % D.wp;
-        const T* s = src + (size_t(i) * n) * Wp + size_t(j) * n;
-        float acc = 0.f;
-        for (int u = 0; u < n; ++u)
-            for (int v = 0; v < n; ++v) acc += to_f(s[size_t(u) * Wp + v]);
-        lds[base + (i + D.p) * D.bp(0) + D.p + j] = acc;
+        lds[base + (i + D.p) * D.bp(0) + D.p + j] = Pp[e];
     }
 }
 
@@ -79,16 +116,18 @@ __device__ void deep_analysis(const DeepLayout& D, float* lds, int shift, int ti
     }
 }
 
-// Sum of levels LT+1..L of one plane at level-LT resolution (fp32).
-template <typename T, bool FLIP>
+// Sum of levels LT+1..L of one plane at level-LT resolution (fp32), from
+// the plane's box sums P.  Each work item computes kDeepRS outputs of one
+// row of one subband from a K x (kDeepRS + K - 1) window held in registers.
+template <typename T, int K, bool FLIP>
 __global__ __launch_bounds__(256) void k_deep_apply(
-    const T* __restrict__ in, const T* __restrict__ ww, const T* __restrict__ sw,
-    float* __restrict__ deep, int B, int C, int Hp, int Wp, int L, int LT, int K) {
+    const float* __restrict__ P, const T* __restrict__ ww, const T* __restrict__ sw,
+    float* __restrict__ deep, int B, int C, int Hp, int Wp, int L, int LT) {
     extern __shared__ float lds[];
     const int tid = threadIdx.x, nt = blockDim.x;
     const int b = blockIdx.x / C, c = blockIdx.x % C;
-    const DeepLayout D{Hp >> LT, Wp >> LT, K / 2, L - LT, K * K};
-    const int KK = D.KK;
+    constexpr int KK = K * K, RS = kDeepRS;
+    const DeepLayout D{Hp >> LT, Wp >> LT, K / 2, L - LT, KK};
     for (int i = tid; i < D.end_apply(); i += nt) lds[i] = 0.f;
     __syncthreads();
     // folded filters of absolute levels LT+1..L: gamma * 4^-l * K (rotated
@@ -100,20 +139,35 @@ __global__ __launch_bounds__(256) void k_deep_apply(
         const int tt = FLIP ? KK - 1 - t : t;
         lds[i] = to_f(sw[gi]) * ldexpf(1.f, -2 * la) * to_f(ww[gi * KK + tt]);
     }
-    box_sums<T>(in + (size_t(b) * C + c) * Hp * Wp, Wp, LT, D, lds, D.uoff(0), tid, nt);
+    load_p(P + (size_t(b) * C + c) * D.hp * D.wp, D, lds, D.uoff(0), tid, nt);
     __syncthreads();
     deep_analysis(D, lds, 0, tid, nt);
     // subband convs
     for (int m = 1; m <= D.LD; ++m) {
-        const int h = D.h(m), w = D.w(m);
-        for (int e = tid; e < 4 * h * w; e += nt) {
-            const int s = e / (h * w), i = (e / w) % h, j = e % w;
+        const int h = D.h(m), w = D.w(m), nseg = (w + RS - 1) / RS;
+        for (int e = tid; e < 4 * h * nseg; e += nt) {
+            const int s = e / (h * nseg), i = (e / nseg) % h, j0 = (e % nseg) * RS;
             const float* wk = lds + (m - 1) * 4 * KK + s * KK;
-            float acc = 0.f;
-            for (int uu = 0; uu < K; ++uu)
-                for (int vv = 0; vv < K; ++vv)
-                    acc = fmaf(wk[uu * K + vv], lds[D.u(m, s, i + uu - D.p, j + vv - D.p)], acc);
-            lds[D.coff(m) + (s * h + i) * w + j] = acc;
+            float acc[RS];
+#pragma unroll
+            for (int r = 0; r < RS; ++r) acc[r] = 0.f;
+#pragma unroll
+            for (int uu = 0; uu < K; ++uu) {
+                const float* src = lds + D.u(m, s, i + uu - D.p, j0 - D.p);
+                float row[RS + K - 1];
+#pragma unroll
+                for (int t = 0; t < RS + K - 1; ++t) row[t] = src[t];
+#pragma unroll
+                for (int vv = 0; vv < K; ++vv) {
+                    const float wv = wk[uu * K + vv];
+#pragma unroll
+                    for (int r = 0; r < RS; ++r) acc[r] = fmaf(wv, row[r + vv], acc[r]);
+                }
+            }
+            float* o = lds + D.coff(m) + (s * h + i) * w + j0;
+#pragma unroll
+            for (int r = 0; r < RS; ++r)
+                if (j0 + r < w) o[r] = acc[r];
         }
     }
     __syncthreads();
@@ -144,39 +198,63 @@ __global__ __launch_bounds__(256) void k_deep_apply(
     }
 }
 
-// Correlations of levels LT+1..L of one plane, written as one full partial
-// row (zeros outside those levels) at row (row0 + b) * C + c.
-template <typename T>
-__global__ __launch_bounds__(256) void k_deep_bww(const T* __restrict__ x,
-                                                  const T* __restrict__ dy,
+// Correlations of levels LT+1..L of one plane (from the box sums of x and
+// dy), written as one full partial row (zeros outside those levels) at row
+// (row0 + b) * C + c.  A work item is one (level, subband, tap row) over a
+// chunk of the rows, with K tap accumulators; the chunks are summed in order.
+template <int K>
+__global__ __launch_bounds__(256) void k_deep_bww(const float* __restrict__ px,
+                                                  const float* __restrict__ pdy,
                                                   float* __restrict__ part, int B, int C,
-                                                  int Hp, int Wp, int L, int LT, int K,
-                                                  int row0, int npart) {
+                                                  int Hp, int Wp, int L, int LT, int row0,
+                                                  int npart) {
     extern __shared__ float lds[];
     const int tid = threadIdx.x, nt = blockDim.x;
     const int b = blockIdx.x / C, c = blockIdx.x % C;
-    const DeepLayout D{Hp >> LT, Wp >> LT, K / 2, L - LT, K * K};
-    const int KK = D.KK;
+    constexpr int KK = K * K, NCH = kDeepNCH;
+    const DeepLayout D{Hp >> LT, Wp >> LT, K / 2, L - LT, KK};
     const int shift = D.uoff(D.LD + 1) - D.uoff(0);  // dy side follows the x side
     for (int i = tid; i < D.end_bww(); i += nt) lds[i] = 0.f;
     __syncthreads();
-    const size_t po = (size_t(b) * C + c) * Hp * Wp;
-    box_sums<T>(x + po, Wp, LT, D, lds, D.uoff(0), tid, nt);
-    box_sums<T>(dy + po, Wp, LT, D, lds, D.uoff(0) + shift, tid, nt);
+    const size_t po = (size_t(b) * C + c) * D.hp * D.wp;
+    load_p(px + po, D, lds, D.uoff(0), tid, nt);
+    load_p(pdy + po, D, lds, D.uoff(0) + shift, tid, nt);
     __syncthreads();
     deep_analysis(D, lds, 0, tid, nt);
     deep_analysis(D, lds, shift, tid, nt);
+    float* red = lds + D.end_bww();
+    const int items = D.LD * 4 * K * NCH;
+    for (int e = tid; e < items; e += nt) {
+        const int ch = e % NCH;
+        int r = e / NCH;
+        const int uu = r % K;
+        r /= K;
+        const int s = r % 4, m = r / 4 + 1;
+        const int h = D.h(m), w = D.w(m);
+        const int i0 = ch * h / NCH, i1 = (ch + 1) * h / NCH;
+        float acc[K];
+#pragma unroll
+        for (int vv = 0; vv < K; ++vv) acc[vv] = 0.f;
+        for (int i = i0; i < i1; ++i)
+            for (int j = 0; j < w; ++j) {
+                const float v = lds[D.u(m, s, i, j) + shift];
+                const float* xr = lds + D.u(m, s, i + uu - D.p, j - D.p);
+#pragma unroll
+                for (int vv = 0; vv < K; ++vv) acc[vv] = fmaf(v, xr[vv], acc[vv]);
+            }
+#pragma unroll
+        for (int vv = 0; vv < K; ++vv) red[e * K + vv] = acc[vv];
+    }
+    __syncthreads();
     float* row = part + (size_t(row0 + b) * C + c) * npart;
+    const int first = KK + 1 + LT * 4 * KK;
     for (int o = tid; o < npart; o += nt) {
-        const int first = KK + 1 + LT * 4 * KK;
         float acc = 0.f;
         if (o >= first) {
-            const int r = o - first, ms = r / KK, t = r % KK, m = ms / 4 + 1, s = ms % 4;
-            const int uu = t / K, vv = t % K, h = D.h(m), w = D.w(m);
-            for (int i = 0; i < h; ++i)
-                for (int j = 0; j < w; ++j)
-                    acc = fmaf(lds[D.u(m, s, i, j) + shift],
-                               lds[D.u(m, s, i + uu - D.p, j + vv - D.p)], acc);
+            const int r = o - first, ms = r / KK, t = r % KK;
+            const int uu = t / K, vv = t % K;
+            const int e0 = (ms * K + uu) * NCH;  // ms = (m - 1) * 4 + s
+            for (int ch = 0; ch < NCH; ++ch) acc += red[(e0 + ch) * K + vv];
         }
         row[o] = acc;
     }
@@ -211,7 +289,9 @@ DeepLayout deep_layout(const wtconv_shape& s) {
 }
 
 size_t deep_apply_lds(const wtconv_shape& s) { return sizeof(float) * deep_layout(s).end_apply(); }
-size_t deep_bww_lds(const wtconv_shape& s) { return sizeof(float) * deep_layout(s).end_bww(); }
+size_t deep_bww_lds(const wtconv_shape& s) {
+    return sizeof(float) * deep_layout(s).end_bww_red(s.k);
+}
 
 constexpr size_t kMaxLds = 160 * 1024;
 constexpr int kMaxTileChunks = 64;
@@ -246,10 +326,29 @@ int tile_chunks(const wtconv_shape& s, int slots) {
     return (units + upw - 1) / upw;
 }
 
+template <typename T, int K>
+const void* deep_apply_fn_k(bool flip) {
+    return flip ? reinterpret_cast<const void*>(&k_deep_apply<T, K, true>)
+                : reinterpret_cast<const void*>(&k_deep_apply<T, K, false>);
+}
+
 template <typename T>
-const void* deep_apply_fn(bool flip) {
-    return flip ? reinterpret_cast<const void*>(&k_deep_apply<T, true>)
-                : reinterpret_cast<const void*>(&k_deep_apply<T, false>);
+const void* deep_apply_fn(bool flip, int k) {
+    switch (k) {
+        case 1: return deep_apply_fn_k<T, 1>(flip);
+        case 3: return deep_apply_fn_k<T, 3>(flip);
+        case 5: return deep_apply_fn_k<T, 5>(flip);
+        default: return deep_apply_fn_k<T, 7>(flip);
+    }
+}
+
+const void* deep_bww_fn(int k) {
+    switch (k) {
+        case 1: return reinterpret_cast<const void*>(&k_deep_bww<1>);
+        case 3: return reinterpret_cast<const void*>(&k_deep_bww<3>);
+        case 5: return reinterpret_cast<const void*>(&k_deep_bww<5>);
+        default: return reinterpret_cast<const void*>(&k_deep_bww<7>);
+    }
 }
 
 }  // namespace
@@ -266,40 +365,69 @@ bool tile_supported(const wtconv_shape& s) {
     return true;
 }
 
-size_t tile_workspace_bytes(const wtconv_shape& s) {
-    if (!tile_supported(s) || s.B == 0 || s.C == 0) return 0;
+// Workspace: [partial rows | deep contribution D] (used one after the other),
+// then the box sums P of x and of dy (levels deeper than the tile's).
+namespace {
+constexpr size_t kAlign = 256;
+size_t align_up(size_t n) { return (n + kAlign - 1) / kAlign * kAlign; }
+size_t p_bytes(const wtconv_shape& s) {
+    const int LT = tile_lt(s);
+    return size_t(s.B) * s.C * (s.H >> LT) * (s.W >> LT) * sizeof(float);
+}
+size_t head_bytes(const wtconv_shape& s) {
     const int LT = tile_lt(s);
     const size_t KK = size_t(s.k) * s.k, npart = KK + 1 + 4 * size_t(s.L) * KK;
     const int units = tile_units_per_channel(s);
     const size_t chunks = size_t(units < kMaxTileChunks ? units : kMaxTileChunks) +
                           (s.L > LT ? size_t(s.B) : 0);
     const size_t bww = chunks * s.C * npart * sizeof(float);
-    const size_t deep =
-        s.L > LT ? size_t(s.B) * s.C * (s.H >> LT) * (s.W >> LT) * sizeof(float) : 0;
-    return bww > deep ? bww : deep;
+    const size_t deep = s.L > LT ? p_bytes(s) : 0;
+    return align_up(bww > deep ? bww : deep);
+}
+float* p_of(const wtconv_shape& s, void* workspace, int which) {
+    return reinterpret_cast<float*>(static_cast<char*>(workspace) + head_bytes(s) +
+                                    which * align_up(p_bytes(s)));
 }
 
-hipError_t tile_apply(const wtconv_shape& s, const void* in, const Params& p, void* out,
-                      bool flip, void* workspace, hipStream_t stream) {
-    const TileVariant* v = find_tile(s);
-    if (!v) return hipErrorInvalidValue;
+hipError_t launch_box_sums(const wtconv_shape& s, const void* src, float* P,
+                           hipStream_t stream) {
     const int LT = tile_lt(s);
-    int B = s.B, C = s.C, H = s.H, W = s.W, L = s.L, K = s.k, LTv = LT;
-    float* deep = nullptr;
+    const unsigned blocks = unsigned(size_t(s.B) * s.C * (s.H >> LT));
+    if (s.dtype == WTCONV_F32)
+        hipLaunchKernelGGL(k_box_sums<float>, dim3(blocks), dim3(128), 0, stream,
+                           static_cast<const float*>(src), P, s.H, s.W, LT);
+    else
+        hipLaunchKernelGGL(k_box_sums<__half>, dim3(blocks), dim3(128), 0, stream,
+                           static_cast<const __half*>(src), P, s.H, s.W, LT);
+    return hipGetLastError();
+}
+
+// Deep levels' contribution D (head of the workspace) from the box sums P.
+hipError_t launch_deep_apply(const wtconv_shape& s, const float* P, const Params& p, bool flip,
+                             float* deep, hipStream_t stream) {
+    const int LT = tile_lt(s);
+    int B = s.B, C = s.C, H = s.H, W = s.W, L = s.L, LTv = LT;
+    const void* fn = s.dtype == WTCONV_F32 ? deep_apply_fn<float>(flip, s.k)
+                                           : deep_apply_fn<__half>(flip, s.k);
+    const size_t lds = deep_apply_lds(s);
     hipError_t e;
-    if (s.L > LT) {
-        deep = static_cast<float*>(workspace);
-        const void* fn = s.dtype == WTCONV_F32 ? deep_apply_fn<float>(flip)
-                                               : deep_apply_fn<__half>(flip);
-        const size_t lds = deep_apply_lds(s);
-        if ((e = set_lds(fn, lds)) != hipSuccess) return e;
-        const void* ww = p.w_wav;
-        const void* sw = p.s_wav;
-        void* args[] = {&in, &ww, &sw, &deep, &B, &C, &H, &W, &L, &LTv, &K};
-        e = hipLaunchKernel(fn, dim3(unsigned(B) * unsigned(C)), dim3(256), args, lds, stream);
-        if (e != hipSuccess) return e;
-    }
+    if ((e = set_lds(fn, lds)) != hipSuccess) return e;
+    const void* ww = p.w_wav;
+    const void* sw = p.s_wav;
+    void* args[] = {&P, &ww, &sw, &deep, &B, &C, &H, &W, &L, &LTv};
+    e = hipLaunchKernel(fn, dim3(unsigned(B) * unsigned(C)), dim3(256), args, lds, stream);
+    if (e != hipSuccess) return e;
+    return hipGetLastError();
+}
+
+// The tile kernels of the forward (flip = false) or input gradient, with the
+// deep contribution (NULL: none).
+hipError_t launch_tiles(const wtconv_shape& s, const TileVariant* v, const void* in,
+                        const Params& p, void* out, bool flip, const float* deep,
+                        hipStream_t stream) {
+    int B = s.B, C = s.C, H = s.H, W = s.W;
     const void* fn = flip ? v->bwi : v->fwd;
+    hipError_t e;
     if ((e = set_lds(fn, v->lds_apply)) != hipSuccess) return e;
     const long total = long(s.C) * tile_units_per_channel(s);
     long nwg = resident(fn, v->NT, v->lds_apply);
@@ -316,18 +444,19 @@ hipError_t tile_apply(const wtconv_shape& s, const void* in, const Params& p, vo
     return hipGetLastError();
 }
 
-hipError_t tile_bwd_weight(const wtconv_shape& s, const void* x, const void* dy,
-                           const Params& p, const Grads& g, void* workspace,
-                           hipStream_t stream) {
-    const TileVariant* v = find_tile(s);
-    if (!v) return hipErrorInvalidValue;
+// Partial rows of the tiles and (with deeper levels) of the planes' deep
+// levels, then the finalize.  Px, Pdy hold the box sums when L > LT.
+hipError_t launch_weight_grads(const wtconv_shape& s, const TileVariant* v, const void* x,
+                               const void* dy, const float* Px, const float* Pdy,
+                               const Params& p, const Grads& g, void* workspace,
+                               hipStream_t stream) {
     const int LT = tile_lt(s);
     hipError_t e;
     if ((e = set_lds(v->bww, v->lds_bww)) != hipSuccess) return e;
     const int nchunk = tile_chunks(s, resident(v->bww, v->NT, v->lds_bww));
     const int units = tile_units_per_channel(s);
     int upw = (units + nchunk - 1) / nchunk;
-    int B = s.B, C = s.C, H = s.H, W = s.W, L = s.L, K = s.k, LTv = LT;
+    int B = s.B, C = s.C, H = s.H, W = s.W, L = s.L, LTv = LT;
     int npart = s.k * s.k * (1 + 4 * s.L) + 1;
     float* part = static_cast<float*>(workspace);
     {
@@ -338,18 +467,72 @@ hipError_t tile_bwd_weight(const wtconv_shape& s, const void* x, const void* dy,
     }
     int rows = nchunk;
     if (s.L > LT) {
-        const void* fn = s.dtype == WTCONV_F32
-                             ? reinterpret_cast<const void*>(&k_deep_bww<float>)
-                             : reinterpret_cast<const void*>(&k_deep_bww<__half>);
+        const void* fn = deep_bww_fn(s.k);
         const size_t lds = deep_bww_lds(s);
         if ((e = set_lds(fn, lds)) != hipSuccess) return e;
         int row0 = nchunk;
-        void* args[] = {&x, &dy, &part, &B, &C, &H, &W, &L, &LTv, &K, &row0, &npart};
+        void* args[] = {&Px, &Pdy, &part, &B, &C, &H, &W, &L, &LTv, &row0, &npart};
         e = hipLaunchKernel(fn, dim3(unsigned(B) * unsigned(C)), dim3(256), args, lds, stream);
         if (e != hipSuccess) return e;
         rows += s.B;
     }
     return finalize_grads(s, part, rows, p, g, stream);
+}
+}  // namespace
+
+size_t tile_workspace_bytes(const wtconv_shape& s) {
+    if (!tile_supported(s) || s.B == 0 || s.C == 0) return 0;
+    const int LT = tile_lt(s);
+    return head_bytes(s) + (s.L > LT ? 2 * align_up(p_bytes(s)) : 0);
+}
+
+hipError_t tile_apply(const wtconv_shape& s, const void* in, const Params& p, void* out,
+                      bool flip, void* workspace, hipStream_t stream) {
+    const TileVariant* v = find_tile(s);
+    if (!v) return hipErrorInvalidValue;
+    float* deep = nullptr;
+    if (s.L > tile_lt(s)) {
+        deep = static_cast<float*>(workspace);
+        float* P = p_of(s, workspace, 0);
+        hipError_t e = launch_box_sums(s, in, P, stream);
+        if (e == hipSuccess) e = launch_deep_apply(s, P, p, flip, deep, stream);
+        if (e != hipSuccess) return e;
+    }
+    return launch_tiles(s, v, in, p, out, flip, deep, stream);
+}
+
+hipError_t tile_bwd_weight(const wtconv_shape& s, const void* x, const void* dy,
+                           const Params& p, const Grads& g, void* workspace,
+                           hipStream_t stream) {
+    const TileVariant* v = find_tile(s);
+    if (!v) return hipErrorInvalidValue;
+    float* Px = nullptr;
+    float* Pdy = nullptr;
+    if (s.L > tile_lt(s)) {
+        Px = p_of(s, workspace, 0);
+        Pdy = p_of(s, workspace, 1);
+        hipError_t e = launch_box_sums(s, x, Px, stream);
+        if (e == hipSuccess) e = launch_box_sums(s, dy, Pdy, stream);
+        if (e != hipSuccess) return e;
+    }
+    return launch_weight_grads(s, v, x, dy, Px, Pdy, p, g, workspace, stream);
+}
+
+hipError_t tile_bwd(const wtconv_shape& s, const void* x, const void* dy, const Params& p,
+                    void* dx, const Grads& g, void* workspace, hipStream_t stream) {
+    const TileVariant* v = find_tile(s);
+    if (!v) return hipErrorInvalidValue;
+    // the weight gradient first (its rows share the head of the workspace
+    // with D), keeping the box sums of dy for the input gradient's deep levels
+    hipError_t e = tile_bwd_weight(s, x, dy, p, g, workspace, stream);
+    if (e != hipSuccess) return e;
+    float* deep = nullptr;
+    if (s.L > tile_lt(s)) {
+        deep = static_cast<float*>(workspace);
+        e = launch_deep_apply(s, p_of(s, workspace, 1), p, true, deep, stream);
+        if (e != hipSuccess) return e;
+    }
+    return launch_tiles(s, v, dy, p, dx, true, deep, stream);
 }
 
 }  // namespace wtc
