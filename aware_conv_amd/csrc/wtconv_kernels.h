@@ -440,6 +440,58 @@ __device__ __forceinline__ void store_vec(T* __restrict__ dst, const float (&v)[
 // Phases
 // ---------------------------------------------------------------------------
 
+// Raw buffer resources over one group's planes.  Accesses at or past the
+// resource's size read zeros and write nothing, so lanes without an item (or
+// planes past the batch) need no branch, and the compiler can count the
+// outstanding memory operations of a straight-line loop body exactly.
+using rsrc_t = __amdgpu_buffer_rsrc_t;
+constexpr int kBufFlags = 0x00020000;  // raw 32-bit dwords, no swizzle
+constexpr int kOutOfRange = int(0x80000000u);  // an offset past every resource here
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, int bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, kBufFlags);
+}
+
+// Planes b0 .. b0+P-1 of channel c (those below B): base pointer and size.
+template <class G, typename T>
+struct GroupSpan {
+    const T* base;
+    int bytes;
+    __device__ GroupSpan(const T* src, int b0, int B, int C, int c) {
+        constexpr int HW = G::H * G::W;
+        const int nvalid = min(G::P, B - b0);
+        base = src + (size_t(b0) * C + c) * HW;
+        bytes = nvalid > 0 ? ((nvalid - 1) * C * HW + HW) * int(sizeof(T)) : 0;
+    }
+};
+
+template <int BYTES>
+__device__ __forceinline__ typename std::conditional<
+    BYTES == 16, uint4, typename std::conditional<BYTES == 8, uint2, uint32_t>::type>::type
+buf_load(rsrc_t r, int off) {
+    if constexpr (BYTES == 16) {
+        const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+        return uint4{v[0], v[1], v[2], v[3]};
+    } else if constexpr (BYTES == 8) {
+        const auto v = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
+        return uint2{v[0], v[1]};
+    } else {
+        return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
+    }
+}
+
+__device__ __forceinline__ void buf_store(const uint4& v, rsrc_t r, int off) {
+    typedef unsigned int v4u __attribute__((ext_vector_type(4)));
+    __builtin_amdgcn_raw_buffer_store_b128(v4u{v.x, v.y, v.z, v.w}, r, off, 0, 0);
+}
+__device__ __forceinline__ void buf_store(const uint2& v, rsrc_t r, int off) {
+    typedef unsigned int v2u __attribute__((ext_vector_type(2)));
+    __builtin_amdgcn_raw_buffer_store_b64(v2u{v.x, v.y}, r, off, 0, 0);
+}
+__device__ __forceinline__ void buf_store(const uint32_t& v, rsrc_t r, int off) {
+    __builtin_amdgcn_raw_buffer_store_b32(v, r, off, 0, 0);
+}
+
 template <int BYTES>
 struct RawVec;
 template <>
@@ -494,6 +546,28 @@ struct Fetch {
 #pragma unroll
                 for (int k = 0; k < ROWS; ++k) r[it][k] = raw_t{};
             }
+        }
+    }
+
+    // Whole planes: the same loads through a buffer resource, with no
+    // branch (items past ITEMS and planes past B read zeros).
+    __device__ __forceinline__ void issue_buf(const T* __restrict__ src, int b0, int B, int C,
+                                              int c, int tid) {
+        static_assert(G::HT == 0, "whole planes only");
+        const GroupSpan<G, T> g(src, b0, B, C, c);
+        const rsrc_t rs = make_rsrc(g.base, g.bytes);
+#pragma unroll
+        for (int it = 0; it < IT; ++it) {
+            const int item = tid + it * G::NT;
+            const int cv = item % NV;
+            const int rb = (item / NV) % RB;
+            const int pl = item / (NV * RB);
+            const bool in = ITEMS % G::NT == 0 || item < ITEMS;
+            const int off = in ? ((pl * C * G::H + ROWS * rb) * G::W + cv * V) * int(sizeof(T))
+                               : kOutOfRange;
+#pragma unroll
+            for (int k = 0; k < ROWS; ++k)
+                r[it][k] = buf_load<V * int(sizeof(T))>(rs, off + (in ? k * G::W * int(sizeof(T)) : 0));
         }
     }
 
@@ -774,6 +848,72 @@ __device__ __forceinline__ void final_to_lds(float* lds, int tid) {
     }
 }
 
+// Whole planes: final_to_lds and the store in one pass.  Each item computes
+// two output rows (one level-1 coefficient row) by V columns from the base
+// conv in the level-0 array and the convolved subbands, and stores them to
+// the group's planes through a buffer resource (no LDS write-back, no branch:
+// lanes past ITEMS re-read a valid item and store out of range).
+template <class G, typename T>
+__device__ __forceinline__ void final_store(const float* lds, T* __restrict__ out, int b0, int B,
+                                            int C, int c, int tid) {
+    static_assert(G::HT == 0, "whole planes only");
+    constexpr int V = vec_elems<T>(G::W);
+    constexpr int NV = G::W / V, RP = G::H / 2, ITEMS = G::P * RP * NV;
+    constexpr int BYTES = V * int(sizeof(T));
+    using raw_t = typename RawVec<BYTES>::type;
+    const GroupSpan<G, T> g(out, b0, B, C, c);
+    const rsrc_t rs = make_rsrc(g.base, g.bytes);
+#pragma unroll
+    for (int it = 0; it < cdiv(ITEMS, G::NT); ++it) {
+        const int raw_item = tid + it * G::NT;
+        const bool in = ITEMS % G::NT == 0 || raw_item < ITEMS;
+        const int item = in ? raw_item : ITEMS - 1;
+        const int cv = item % NV;
+        const int i = (item / NV) % RP;
+        const int pl = item / (NV * RP);
+        const float* x0 = lds + G::uidx(0, pl, 0, 2 * i, cv * V);
+        float r0[V], r1[V];
+        lds_get<V, G::al(0)>(x0, r0);
+        lds_get<V, G::al(0)>(x0 + G::pitch(0), r1);
+        if constexpr (G::L >= 1) {
+            float cf[4][V / 2];
+#pragma unroll
+            for (int sb = 0; sb < 4; ++sb)
+                lds_get<V / 2, G::al(1)>(lds + G::uidx(1, pl, sb, i, cv * (V / 2)), cf[sb]);
+#pragma unroll
+            for (int m = 0; m < V / 2; ++m) {
+                float ll = cf[0][m];
+                if constexpr (G::L >= 2) {
+                    constexpr int A2 = G::arr(2);
+                    const int j = cv * (V / 2) + m;
+                    const float* c2 = lds + G::uidx(2, pl, 0, i >> 1, j >> 1);
+                    const float sy2 = (i & 1) ? -1.f : 1.f, sx2 = (j & 1) ? -1.f : 1.f;
+                    const float e2 = fmaf(sy2, c2[2 * A2], c2[0]);
+                    const float f2 = fmaf(sy2, c2[3 * A2], c2[A2]);
+                    ll += fmaf(sx2, f2, e2);
+                }
+                const float lh = cf[1][m], hl = cf[2][m], hh = cf[3][m];
+                const float e0 = ll + hl, f0 = lh + hh;  // row 2i   (row bit 0)
+                const float e1 = ll - hl, f1 = lh - hh;  // row 2i+1 (row bit 1)
+                r0[2 * m] += e0 + f0;
+                r0[2 * m + 1] += e0 - f0;
+                r1[2 * m] += e1 + f1;
+                r1[2 * m + 1] += e1 - f1;
+            }
+        }
+        union {
+            raw_t raw;
+            T e[V];
+        } u0, u1;
+        store_vec<T, V>(u0.e, r0);
+        store_vec<T, V>(u1.e, r1);
+        const int off = in ? ((pl * C * G::H + 2 * i) * G::W + cv * V) * int(sizeof(T))
+                           : kOutOfRange;
+        buf_store(u0.raw, rs, off);
+        buf_store(u1.raw, rs, off + (in ? G::W * int(sizeof(T)) : 0));
+    }
+}
+
 // The finished group (y in the core of the level-0 array) -> HBM, ROWS x V
 // per item.  In tile mode the core sits at (y0, x0) of an Hp x Wp plane and
 // items outside the plane are skipped.
@@ -864,8 +1004,10 @@ constexpr size_t bww_lds_bytes() {
 // (channel, group of P planes) pairs, channel-major, are split into gridDim.x
 // equal contiguous ranges, one per workgroup; the filters are folded again
 // whenever a workgroup's range enters a new channel.  The next group's input
-// is loaded into registers while the current one is computed, and a group's
-// output is stored at the start of the next iteration.
+// is loaded into registers while the current one is computed; the output is
+// synthesised and stored in one pass.  Loads and stores go through buffer
+// resources with no branch, so the only wait before a group's input is used
+// is for that input.
 template <int K, int L, int H, int W, int P, int NT, typename T, bool FLIP>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(
     waves_for_lds(apply_lds_bytes<Geo<K, L, H, W, P, NT>>(), NT) < 4
@@ -886,7 +1028,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(
     const int q0 = int(total * blockIdx.x / gridDim.x);
     const int q1 = int(total * (blockIdx.x + 1) / gridDim.x);
     F fx;
-    if (q0 < q1) fx.issue(in, (q0 % ngroups) * P, B, C, q0 / ngroups, tid);
+    if (q0 < q1) fx.issue_buf(in, (q0 % ngroups) * P, B, C, q0 / ngroups, tid);
     for (int i = tid; i < G::side; i += NT) lds[i] = 0.f;
 
     const Job job = decode_job<G>(tid);
@@ -902,7 +1044,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(
 
     float w[KK];
     float init = 0.f;
-    int cur = -1, pend_b0 = -1, pend_c = 0;
+    int cur = -1;
     for (int q = q0; q < q1; ++q) {
         const int c = q / ngroups;
         const int b0 = (q % ngroups) * P;
@@ -914,11 +1056,6 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(
             init = job.lvl == 0 ? wf[G::NWF - 1] : 0.f;
             cur = c;
         }
-        wait_vmem();
-        if (pend_b0 >= 0) {
-            store_out<G, T>(lds, out, pend_b0, B, C, pend_c, tid);
-            __syncthreads();
-        }
         fx.template commit<true, false>(lds, tid);
         __syncthreads();
         static_for<F::LEVELS + 1, L + 1>([&](auto lc) {
@@ -928,7 +1065,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(
         float acc[Q][R];
         if (job.on) conv_tile<K, Q, R>(lds + win, pitch, w, init, acc);
         // the next group's loads fly during write-back, synthesis and store
-        if (q + 1 < q1) fx.issue(in, ((q + 1) % ngroups) * P, B, C, (q + 1) / ngroups, tid);
+        if (q + 1 < q1) fx.issue_buf(in, ((q + 1) % ngroups) * P, B, C, (q + 1) / ngroups, tid);
         __syncthreads();
         if (job.on) {
             if (full) {
@@ -951,12 +1088,9 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(
             cascade_level<G, L - decltype(lc)::value>(lds, tid);
             __syncthreads();
         });
-        final_to_lds<G, T>(lds, tid);
-        pend_b0 = b0;
-        pend_c = c;
+        final_store<G, T>(lds, out, b0, B, C, c, tid);
         __syncthreads();
     }
-    if (pend_b0 >= 0) store_out<G, T>(lds, out, pend_b0, B, C, pend_c, tid);
 }
 
 // Fixed-order workgroup reduction of the lanes' tap accumulators into one
@@ -1123,7 +1257,7 @@ struct LinearRows {
 // of its tile for the rotated-filter conv of the input gradient, keeps the
 // window's centre (its tile of dy, or of V^l_s) and correlates it with the x
 // window of the same tile for the weight gradient.  The input gradient then
-// goes through the same synthesis and deferred store as the forward.  With
+// goes through the same synthesis and store as the forward.  With
 // CROSS, a range may span channels: entering a new channel, the finished
 // channel's taps are reduced to its row and the filters are folded again;
 // without, every range lies in one channel (nwg a multiple of C) and the
@@ -1150,8 +1284,8 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void k_
     int c = int(q0 / ngroups), grp = int(q0 % ngroups);
     F fx, fd;
     if (nitems > 0) {
-        fx.issue(x, grp * P, B, C, c, tid);
-        fd.issue(dy, grp * P, B, C, c, tid);
+        fx.issue_buf(x, grp * P, B, C, c, tid);
+        fd.issue_buf(dy, grp * P, B, C, c, tid);
     }
     for (int i = tid; i < DY + G::side; i += NT) lds[i] = 0.f;
 
@@ -1168,7 +1302,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void k_
     float w[KK];
     float gacc[KK];
     float sdy = 0.f;
-    int cur = -1, pend_b0 = -1, pend_c = 0;
+    int cur = -1;
     if constexpr (!CROSS) {
         // one channel for the whole range: fold once, before the loop
         fold_weights<G, T, true>(wf, wb, wb, sb, ww, sw, C, c, tid);
@@ -1182,16 +1316,10 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void k_
 
     for (int it = 0; it < nitems; ++it) {
         const int b0 = grp * P;
-        wait_vmem();
-        if (pend_b0 >= 0) {
-            store_out<G, T>(ldy, dx, pend_b0, B, C, pend_c, tid);
-            __syncthreads();
-        }
         if (CROSS && c != cur) {
             if (cur >= 0) {
-                // the finished channel's row (its last dx is stored); the
-                // arrays the reduction used are zeroed again and the filters
-                // folded again below
+                // the finished channel's row; the arrays the reduction used
+                // are zeroed again and the filters folded again below
                 reduce_row<G>(lds, gacc, sdy,
                               part + (size_t(cur) * rows.rmax + (blockIdx.x - rows.first(cur))) *
                                          G::NPART,
@@ -1233,8 +1361,8 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void k_
         const bool wrap = grp + 1 == ngroups;
         const int cn = wrap ? c + 1 : c, gn = wrap ? 0 : grp + 1;
         if (it + 1 < nitems) {
-            fx.issue(x, gn * P, B, C, cn, tid);
-            fd.issue(dy, gn * P, B, C, cn, tid);
+            fx.issue_buf(x, gn * P, B, C, cn, tid);
+            fd.issue_buf(dy, gn * P, B, C, cn, tid);
         }
         __syncthreads();
         if (job.on) {
@@ -1256,15 +1384,9 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void k_
             cascade_level<G, L - decltype(lc)::value>(ldy, tid);
             __syncthreads();
         });
-        final_to_lds<G, T>(ldy, tid);
-        pend_b0 = b0;
-        pend_c = c;
+        final_store<G, T>(ldy, dx, b0, B, C, c, tid);
         c = cn;
         grp = gn;
-        __syncthreads();
-    }
-    if (pend_b0 >= 0) {
-        store_out<G, T>(ldy, dx, pend_b0, B, C, pend_c, tid);
         __syncthreads();
     }
     if (cur >= 0)
