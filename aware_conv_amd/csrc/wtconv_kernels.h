@@ -859,7 +859,10 @@ __device__ __forceinline__ void final_store(const float* lds, T* __restrict__ ou
     static_assert(G::HT == 0, "whole planes only");
     constexpr int V = vec_elems<T>(G::W);
     constexpr int NV = G::W / V, RP = G::H / 2, ITEMS = G::P * RP * NV;
-    constexpr int BYTES = V * int(sizeof(T));
+    // columns per pass: at most 4 floats, so that an 8-wide fp16 item keeps
+    // few values live (two 8-byte stores per row instead of one 16-byte)
+    constexpr int CW = V < 4 ? V : 4, NCH = V / CW;
+    constexpr int BYTES = CW * int(sizeof(T));
     using raw_t = typename RawVec<BYTES>::type;
     const GroupSpan<G, T> g(out, b0, B, C, c);
     const rsrc_t rs = make_rsrc(g.base, g.bytes);
@@ -871,46 +874,51 @@ __device__ __forceinline__ void final_store(const float* lds, T* __restrict__ ou
         const int cv = item % NV;
         const int i = (item / NV) % RP;
         const int pl = item / (NV * RP);
-        const float* x0 = lds + G::uidx(0, pl, 0, 2 * i, cv * V);
-        float r0[V], r1[V];
-        lds_get<V, G::al(0)>(x0, r0);
-        lds_get<V, G::al(0)>(x0 + G::pitch(0), r1);
-        if constexpr (G::L >= 1) {
-            float cf[4][V / 2];
-#pragma unroll
-            for (int sb = 0; sb < 4; ++sb)
-                lds_get<V / 2, G::al(1)>(lds + G::uidx(1, pl, sb, i, cv * (V / 2)), cf[sb]);
-#pragma unroll
-            for (int m = 0; m < V / 2; ++m) {
-                float ll = cf[0][m];
-                if constexpr (G::L >= 2) {
-                    constexpr int A2 = G::arr(2);
-                    const int j = cv * (V / 2) + m;
-                    const float* c2 = lds + G::uidx(2, pl, 0, i >> 1, j >> 1);
-                    const float sy2 = (i & 1) ? -1.f : 1.f, sx2 = (j & 1) ? -1.f : 1.f;
-                    const float e2 = fmaf(sy2, c2[2 * A2], c2[0]);
-                    const float f2 = fmaf(sy2, c2[3 * A2], c2[A2]);
-                    ll += fmaf(sx2, f2, e2);
-                }
-                const float lh = cf[1][m], hl = cf[2][m], hh = cf[3][m];
-                const float e0 = ll + hl, f0 = lh + hh;  // row 2i   (row bit 0)
-                const float e1 = ll - hl, f1 = lh - hh;  // row 2i+1 (row bit 1)
-                r0[2 * m] += e0 + f0;
-                r0[2 * m + 1] += e0 - f0;
-                r1[2 * m] += e1 + f1;
-                r1[2 * m + 1] += e1 - f1;
-            }
-        }
-        union {
-            raw_t raw;
-            T e[V];
-        } u0, u1;
-        store_vec<T, V>(u0.e, r0);
-        store_vec<T, V>(u1.e, r1);
         const int off = in ? ((pl * C * G::H + 2 * i) * G::W + cv * V) * int(sizeof(T))
                            : kOutOfRange;
-        buf_store(u0.raw, rs, off);
-        buf_store(u1.raw, rs, off + (in ? G::W * int(sizeof(T)) : 0));
+#pragma unroll
+        for (int ch = 0; ch < NCH; ++ch) {
+            const int col = cv * V + ch * CW;
+            const float* x0 = lds + G::uidx(0, pl, 0, 2 * i, col);
+            float r0[CW], r1[CW];
+            lds_get<CW, G::al(0)>(x0, r0);
+            lds_get<CW, G::al(0)>(x0 + G::pitch(0), r1);
+            if constexpr (G::L >= 1) {
+                float cf[4][CW / 2];
+#pragma unroll
+                for (int sb = 0; sb < 4; ++sb)
+                    lds_get<CW / 2, G::al(1)>(lds + G::uidx(1, pl, sb, i, col / 2), cf[sb]);
+#pragma unroll
+                for (int m = 0; m < CW / 2; ++m) {
+                    float ll = cf[0][m];
+                    if constexpr (G::L >= 2) {
+                        constexpr int A2 = G::arr(2);
+                        const int j = col / 2 + m;
+                        const float* c2 = lds + G::uidx(2, pl, 0, i >> 1, j >> 1);
+                        const float sy2 = (i & 1) ? -1.f : 1.f, sx2 = (j & 1) ? -1.f : 1.f;
+                        const float e2 = fmaf(sy2, c2[2 * A2], c2[0]);
+                        const float f2 = fmaf(sy2, c2[3 * A2], c2[A2]);
+                        ll += fmaf(sx2, f2, e2);
+                    }
+                    const float lh = cf[1][m], hl = cf[2][m], hh = cf[3][m];
+                    const float e0 = ll + hl, f0 = lh + hh;  // row 2i   (row bit 0)
+                    const float e1 = ll - hl, f1 = lh - hh;  // row 2i+1 (row bit 1)
+                    r0[2 * m] += e0 + f0;
+                    r0[2 * m + 1] += e0 - f0;
+                    r1[2 * m] += e1 + f1;
+                    r1[2 * m + 1] += e1 - f1;
+                }
+            }
+            union {
+                raw_t raw;
+                T e[CW];
+            } u0, u1;
+            store_vec<T, CW>(u0.e, r0);
+            store_vec<T, CW>(u1.e, r1);
+            const int o = off + (in ? ch * BYTES : 0);
+            buf_store(u0.raw, rs, o);
+            buf_store(u1.raw, rs, o + (in ? G::W * int(sizeof(T)) : 0));
+        }
     }
 }
 
@@ -1008,12 +1016,18 @@ constexpr size_t bww_lds_bytes() {
 // synthesised and stored in one pass.  Loads and stores go through buffer
 // resources with no branch, so the only wait before a group's input is used
 // is for that input.
+// Register budget of the forward: the waves per SIMD the LDS footprint
+// allows, at most 4 (3 for fp16, whose 8-wide rows need more registers).
+template <int K, int L, int H, int W, int P, int NT, typename T>
+constexpr int apply_waves() {
+    const int w = waves_for_lds(apply_lds_bytes<Geo<K, L, H, W, P, NT>>(), NT);
+    const int cap = sizeof(T) == 2 ? 3 : 4;
+    return w < cap ? w : cap;
+}
+
 template <int K, int L, int H, int W, int P, int NT, typename T, bool FLIP>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(
-    waves_for_lds(apply_lds_bytes<Geo<K, L, H, W, P, NT>>(), NT) < 4
-        ? waves_for_lds(apply_lds_bytes<Geo<K, L, H, W, P, NT>>(), NT)
-        : 4,
-    8))) void k_plane_apply(
+    apply_waves<K, L, H, W, P, NT, T>(), 8))) void k_plane_apply(
     const T* __restrict__ in, const T* __restrict__ wb, const T* __restrict__ bb,
     const T* __restrict__ sb, const T* __restrict__ ww, const T* __restrict__ sw,
     T* __restrict__ out, int B, int C) {
