@@ -6,7 +6,10 @@
 A step is one pass of the whole hot path over one batch on synthetic inputs
 already resident in device memory: wtconv_fwd, then the backward, by default
 the fused wtconv_bwd (input and parameter gradients reading x and dy once),
-with --backward split the two calls wtconv_bwd_input and wtconv_bwd_weight.  W untimed steps, then exactly K timed steps bracketed by
+with --backward split the two calls wtconv_bwd_input and wtconv_bwd_weight.
+By default the step's kernels are replayed from a HIP graph (one per buffer
+set), as a training loop that captures its step would run them; --launch
+eager times the calls as issued (also reported as eager_ms_per_step).  W untimed steps, then exactly K timed steps bracketed by
 device synchronisation; value = images per second over the K steps.  Each
 step reads its own set of buffers, rotating over enough sets that no step
 finds the previous step's tensors in the 256 MB last-level cache.
@@ -156,7 +159,28 @@ def cpu_baseline(wl, min_seconds=10.0):
             "sample": "%d full %s batch(es) of %d images (fwd + bwd), fp64, %.1f s" % (reps, wl.name, wl.B, el)}
 
 
-def dw7_baseline(L, torch, sets, wl, warmup, steps, stream):
+def time_graphs(torch, sets, step, warmup, steps):
+    """Capture one step per buffer set into a HIP graph (nothing is allocated
+    inside: every output is preallocated), then time `steps` replays in
+    rotation after `warmup`; returns the elapsed seconds."""
+    graphs = []
+    for t in sets:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            step(t)
+        graphs.append(g)
+    torch.cuda.synchronize()
+    for i in range(warmup):
+        graphs[i % len(graphs)].replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        graphs[i % len(graphs)].replay()
+    torch.cuda.synchronize()
+    return time.perf_counter() - t0
+
+
+def dw7_baseline(L, torch, sets, wl, warmup, steps, stream, launch):
     """Step time of the 7x7 depthwise conv (forward + fused backward) on the
     same rotated activations, or None when the shape has no kernel."""
     k = 7
@@ -172,14 +196,15 @@ def dw7_baseline(L, torch, sets, wl, warmup, steps, stream):
     dw, db = torch.empty_like(w), torch.empty_like(b)
 
     def step(t, ev=None):
+        st = torch.cuda.current_stream(dev)
         if ev is not None:
-            ev[0].record(stream)
-        L.dwconv_fwd(t["x"], w, b, y=t["y"], stream=stream)
+            ev[0].record(st)
+        L.dwconv_fwd(t["x"], w, b, y=t["y"], stream=st)
         if ev is not None:
-            ev[1].record(stream)
-        L.dwconv_bwd(t["x"], t["dy"], w, dx=t["dx"], dw=dw, db=db, workspace=ws, stream=stream)
+            ev[1].record(st)
+        L.dwconv_bwd(t["x"], t["dy"], w, dx=t["dx"], dw=dw, db=db, workspace=ws, stream=st)
         if ev is not None:
-            ev[2].record(stream)
+            ev[2].record(st)
 
     for i in range(warmup):
         step(sets[i % len(sets)])
@@ -192,6 +217,8 @@ def dw7_baseline(L, torch, sets, wl, warmup, steps, stream):
     el = time.perf_counter() - t0
     fwd_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / steps
     bwd_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / steps
+    if launch == "graph":
+        el = time_graphs(torch, sets, step, warmup, steps)
     return {"k": k, "ms_per_step": round(el * 1e3 / steps, 4),
             "images_per_s": round(wl.B * steps / el, 1),
             "per_call_ms": {"dwconv_fwd": round(fwd_ms, 5), "dwconv_bwd": round(bwd_ms, 5)},
@@ -213,6 +240,11 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dw-baseline", action="store_true",
                     help="skip the 7x7 depthwise conv baseline")
+    ap.add_argument("--launch", choices=("graph", "eager"), default="graph",
+                    help="graph: time replays of one HIP graph per buffer set (the "
+                         "step's kernels without host launch gaps); eager: time the "
+                         "calls as issued.  Per-call times always come from an eager "
+                         "pass with events between the calls")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a plain device copy of the step's input size "
                          "(calibrates rocprofv3 byte counters)")
@@ -269,23 +301,24 @@ def main():
              ["wtconv_fwd", "wtconv_bwd_input", "wtconv_bwd_weight"])
 
     def step(t, ev=None):
+        st = torch.cuda.current_stream(dev)  # the capture stream while capturing
         p = (t["w_base"], t["b_base"], t["s_base"], t["w_wav"], t["s_wav"])
         run = {
-            "wtconv_fwd": lambda: L.wtconv_fwd(t["x"], *p, y=t["y"], workspace=ws, stream=stream),
+            "wtconv_fwd": lambda: L.wtconv_fwd(t["x"], *p, y=t["y"], workspace=ws, stream=st),
             "wtconv_bwd": lambda: L.wtconv_bwd(t["x"], t["dy"], *p, dx=t["dx"], grads=t["g"],
-                                               workspace=ws, stream=stream),
+                                               workspace=ws, stream=st),
             "wtconv_bwd_input": lambda: L.wtconv_bwd_input(t["dy"], p[0], p[2], p[3], p[4],
                                                            dx=t["dx"], workspace=ws,
-                                                           stream=stream),
+                                                           stream=st),
             "wtconv_bwd_weight": lambda: L.wtconv_bwd_weight(t["x"], t["dy"], *p, grads=t["g"],
-                                                             workspace=ws, stream=stream),
+                                                             workspace=ws, stream=st),
         }
         for i, c in enumerate(calls):
             if ev is not None:
-                ev[i].record(stream)
+                ev[i].record(st)
             run[c]()
         if ev is not None:
-            ev[len(calls)].record(stream)
+            ev[len(calls)].record(st)
 
     for i in range(args.warmup):
         step(sets[i % nsets])
@@ -297,12 +330,15 @@ def main():
         step(sets[i % nsets], evs[i])
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
+    eager_ms_step = elapsed * 1e3 / args.steps
     per = {c: [e[i].elapsed_time(e[i + 1]) for e in evs] for i, c in enumerate(calls)}
     avg_ms = {k: sum(v) / len(v) for k, v in per.items()}
+    if args.launch == "graph":
+        elapsed = time_graphs(torch, sets, step, args.warmup, args.steps)
 
     dw = None
     if not args.no_dw_baseline:
-        dw = dw7_baseline(L, torch, sets, wl, args.warmup, args.steps, stream)
+        dw = dw7_baseline(L, torch, sets, wl, args.warmup, args.steps, stream, args.launch)
 
     if args.copy_probe:
         src = torch.ones(COPY_PROBE_BYTES // 4, dtype=torch.float32, device=dev)
@@ -346,7 +382,8 @@ def main():
         "data": "synthetic (seeded N(0,1) activations, N(0,0.02^2) filters)",
         "config": {"workload": wl.name, "B": wl.B, "C": wl.C, "H": wl.H, "W": wl.W,
                    "levels": wl.L, "k": wl.k, "backward": args.backward,
-                   "buffer_sets": nsets},
+                   "launch": args.launch, "buffer_sets": nsets},
+        "eager_ms_per_step": round(eager_ms_step, 4),
         "step_algo_bytes": step_bytes,
         "effective_hbm_gbs": round(step_bytes / (elapsed / args.steps) / 1e9, 1),
         "effective_hbm_frac": round(step_bytes / (elapsed / args.steps) / 1e9 / PEAK_HBM_GBS, 4),
