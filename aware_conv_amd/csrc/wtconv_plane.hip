@@ -56,7 +56,14 @@ int bww_chunks(const wtconv_shape& s, int P, int slots) {
 
 }  // namespace
 
-bool plane_supported(const wtconv_shape& s) { return find_variant(s) != nullptr; }
+bool plane_supported(const wtconv_shape& s) {
+    const Variant* v = find_variant(s);
+    if (!v) return false;
+    // buffer offsets within a group (P planes of one channel, C planes
+    // apart) are 32-bit: larger shapes take the tile path
+    const size_t esz = s.dtype == WTCONV_F32 ? 4 : 2;
+    return size_t(v->P) * size_t(s.C) * size_t(s.H) * size_t(s.W) * esz < (size_t(1) << 31);
+}
 
 // Fused backward: workgroups over balanced ranges of (channel, group)
 // items, at most this many (a compute unit holds at most 8 of them).

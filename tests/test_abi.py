@@ -169,3 +169,10 @@ def test_dwconv_checks(lb):
     assert b(ctypes.byref(s), FAKE, FAKE2, FAKE, DX, FAKE, FAKE, FAKE, need - 1, None) == -7
     assert b(ctypes.byref(s), FAKE, FAKE2, FAKE, FAKE2, FAKE, FAKE, FAKE, need, None) == -9
     assert b(ctypes.byref(s), FAKE, FAKE2, FAKE, None, FAKE, FAKE, FAKE, need, None) == -1
+
+
+def test_huge_channel_counts_leave_the_whole_plane_path(lb):
+    # a group's buffer offsets are 32-bit: with 2^22 channels of 56 x 56 the
+    # library still sizes a workspace (the tile path takes the shape)
+    s = good(lb, B=1, C=1 << 22)
+    assert lb.wtconv_workspace_size(s) > 0
