@@ -571,6 +571,30 @@ struct Fetch {
         }
     }
 
+    // Tiles: the footprint of the tile at (y0, x0) of plane b through a
+    // buffer resource over that plane; items outside the plane (and b >= B)
+    // read zeros without a branch.  Hp, Wp, y0, x0 are multiples of 4 and of
+    // V, so an item is entirely inside or entirely outside.
+    __device__ __forceinline__ void issue_tile_buf(const T* __restrict__ src, int b, int B, int C,
+                                                   int c, int tid, int y0, int x0, int Hp,
+                                                   int Wp) {
+        const T* base = src + (size_t(min(b, B - 1)) * C + c) * Hp * Wp;
+        const rsrc_t rs = make_rsrc(base, b < B ? Hp * Wp * int(sizeof(T)) : 0);
+#pragma unroll
+        for (int it = 0; it < IT; ++it) {
+            const int item = tid + it * G::NT;
+            const int cv = item % NV;
+            const int rb = (item / NV) % RB;
+            const int yy = y0 - A0 + ROWS * rb, xx = x0 - A0 + cv * V;
+            const bool in = (ITEMS % G::NT == 0 || item < ITEMS) && yy >= 0 && yy < Hp &&
+                            xx >= 0 && xx < Wp;
+            const int off = in ? (yy * Wp + xx) * int(sizeof(T)) : kOutOfRange;
+#pragma unroll
+            for (int k = 0; k < ROWS; ++k)
+                r[it][k] = buf_load<V * int(sizeof(T))>(rs, off + (in ? k * Wp * int(sizeof(T)) : 0));
+        }
+    }
+
     static __device__ __forceinline__ void unpack(const raw_t& raw, float (&v)[V]) {
         union {
             raw_t r;
@@ -796,67 +820,54 @@ __device__ __forceinline__ void cascade_level(float* lds, int tid) {
     }
 }
 
-// y = base conv plus bias (already in the level-0 array) + synthesis, written
-// back in place.  Each item covers two output rows (one level-1 coefficient
-// row) by V columns.  Level 2, whose coarser levels are already folded into
-// its LL, is folded into the level-1 LL here, on the fly; then each level-1
-// coefficient is expanded over its 2x2 block.
-template <class G, typename T>
-__device__ __forceinline__ void final_to_lds(float* lds, int tid) {
-    // L = 0 (plain depthwise conv): y is the base conv, already in place
+// Output rows 2i and 2i+1, columns col .. col+CW-1 (of plane pl's core):
+// the base conv in the level-0 array plus the synthesis of the convolved
+// subbands (level 2, whose coarser levels are already folded into its LL,
+// folded into the level-1 LL on the fly, then each level-1 coefficient
+// expanded over its 2x2 block).
+template <class G, int CW>
+__device__ __forceinline__ void synth_rows(const float* lds, int pl, int i, int col,
+                                           float (&r0)[CW], float (&r1)[CW]) {
+    const float* x0 = lds + G::uidx(0, pl, 0, 2 * i, col);
+    lds_get<CW, G::al(0)>(x0, r0);
+    lds_get<CW, G::al(0)>(x0 + G::pitch(0), r1);
     if constexpr (G::L >= 1) {
-        constexpr int V = vec_elems<T>(G::W);
-        constexpr int NV = G::W / V, RP = G::H / 2, ITEMS = G::P * RP * NV;
+        float cf[4][CW / 2];
 #pragma unroll
-        for (int it = 0; it < cdiv(ITEMS, G::NT); ++it) {
-            const int item = tid + it * G::NT;
-            if (ITEMS % G::NT == 0 || item < ITEMS) {
-                const int cv = item % NV;
-                const int i = (item / NV) % RP;
-                const int pl = item / (NV * RP);
-                float* x0 = lds + G::uidx(0, pl, 0, 2 * i, cv * V);
-                float r0[V], r1[V], c[4][V / 2];
-                lds_get<V, G::al(0)>(x0, r0);
-                lds_get<V, G::al(0)>(x0 + G::pitch(0), r1);
+        for (int sb = 0; sb < 4; ++sb)
+            lds_get<CW / 2, G::al(1)>(lds + G::uidx(1, pl, sb, i, col / 2), cf[sb]);
 #pragma unroll
-                for (int sb = 0; sb < 4; ++sb)
-                    lds_get<V / 2, G::al(1)>(lds + G::uidx(1, pl, sb, i, cv * (V / 2)), c[sb]);
-#pragma unroll
-                for (int m = 0; m < V / 2; ++m) {
-                    float ll = c[0][m];
-                    if constexpr (G::L >= 2) {
-                        constexpr int A2 = G::arr(2);
-                        const int j = cv * (V / 2) + m;
-                        const float* c2 = lds + G::uidx(2, pl, 0, i >> 1, j >> 1);
-                        const float sy2 = (i & 1) ? -1.f : 1.f, sx2 = (j & 1) ? -1.f : 1.f;
-                        const float e2 = fmaf(sy2, c2[2 * A2], c2[0]);
-                        const float f2 = fmaf(sy2, c2[3 * A2], c2[A2]);
-                        ll += fmaf(sx2, f2, e2);
-                    }
-                    const float lh = c[1][m], hl = c[2][m], hh = c[3][m];
-                    const float e0 = ll + hl, f0 = lh + hh;  // row 2i   (row bit 0)
-                    const float e1 = ll - hl, f1 = lh - hh;  // row 2i+1 (row bit 1)
-                    r0[2 * m] += e0 + f0;
-                    r0[2 * m + 1] += e0 - f0;
-                    r1[2 * m] += e1 + f1;
-                    r1[2 * m + 1] += e1 - f1;
-                }
-                lds_put<V, G::al(0)>(x0, r0);
-                lds_put<V, G::al(0)>(x0 + G::pitch(0), r1);
+        for (int m = 0; m < CW / 2; ++m) {
+            float ll = cf[0][m];
+            if constexpr (G::L >= 2) {
+                constexpr int A2 = G::arr(2);
+                const int j = col / 2 + m;
+                const float* c2 = lds + G::uidx(2, pl, 0, i >> 1, j >> 1);
+                const float sy2 = (i & 1) ? -1.f : 1.f, sx2 = (j & 1) ? -1.f : 1.f;
+                const float e2 = fmaf(sy2, c2[2 * A2], c2[0]);
+                const float f2 = fmaf(sy2, c2[3 * A2], c2[A2]);
+                ll += fmaf(sx2, f2, e2);
             }
+            const float lh = cf[1][m], hl = cf[2][m], hh = cf[3][m];
+            const float e0 = ll + hl, f0 = lh + hh;  // row 2i   (row bit 0)
+            const float e1 = ll - hl, f1 = lh - hh;  // row 2i+1 (row bit 1)
+            r0[2 * m] += e0 + f0;
+            r0[2 * m + 1] += e0 - f0;
+            r1[2 * m] += e1 + f1;
+            r1[2 * m + 1] += e1 - f1;
         }
     }
 }
 
-// Whole planes: final_to_lds and the store in one pass.  Each item computes
-// two output rows (one level-1 coefficient row) by V columns from the base
-// conv in the level-0 array and the convolved subbands, and stores them to
-// the group's planes through a buffer resource (no LDS write-back, no branch:
-// lanes past ITEMS re-read a valid item and store out of range).
+// The synthesis and the store in one pass, through a buffer resource (no LDS
+// write-back, no branch: lanes past ITEMS re-read a valid item and store out
+// of range).  Whole planes (HT == 0): the group's planes.  Tiles: the core of
+// the tile at (y0, x0) of plane b of an Hp x Wp tensor; rows and columns
+// past the plane, and b >= B, store out of range.
 template <class G, typename T>
 __device__ __forceinline__ void final_store(const float* lds, T* __restrict__ out, int b0, int B,
-                                            int C, int c, int tid) {
-    static_assert(G::HT == 0, "whole planes only");
+                                            int C, int c, int tid, int y0 = 0, int x0 = 0,
+                                            int Hp = G::H, int Wp = G::W) {
     constexpr int V = vec_elems<T>(G::W);
     constexpr int NV = G::W / V, RP = G::H / 2, ITEMS = G::P * RP * NV;
     // columns per pass: at most 4 floats, so that an 8-wide fp16 item keeps
@@ -864,51 +875,38 @@ __device__ __forceinline__ void final_store(const float* lds, T* __restrict__ ou
     constexpr int CW = V < 4 ? V : 4, NCH = V / CW;
     constexpr int BYTES = CW * int(sizeof(T));
     using raw_t = typename RawVec<BYTES>::type;
-    const GroupSpan<G, T> g(out, b0, B, C, c);
-    const rsrc_t rs = make_rsrc(g.base, g.bytes);
+    rsrc_t rs;
+    int row_elems;  // elements between two output rows
+    if constexpr (G::HT == 0) {
+        const GroupSpan<G, T> g(out, b0, B, C, c);
+        rs = make_rsrc(g.base, g.bytes);
+        row_elems = G::W;
+    } else {
+        const T* base = out + (size_t(min(b0, B - 1)) * C + c) * Hp * Wp;
+        rs = make_rsrc(base, b0 < B ? Hp * Wp * int(sizeof(T)) : 0);
+        row_elems = Wp;
+    }
 #pragma unroll
     for (int it = 0; it < cdiv(ITEMS, G::NT); ++it) {
         const int raw_item = tid + it * G::NT;
-        const bool in = ITEMS % G::NT == 0 || raw_item < ITEMS;
+        bool in = ITEMS % G::NT == 0 || raw_item < ITEMS;
         const int item = in ? raw_item : ITEMS - 1;
         const int cv = item % NV;
         const int i = (item / NV) % RP;
         const int pl = item / (NV * RP);
-        const int off = in ? ((pl * C * G::H + 2 * i) * G::W + cv * V) * int(sizeof(T))
-                           : kOutOfRange;
+        int off;
+        if constexpr (G::HT == 0) {
+            off = ((pl * C * G::H + 2 * i) * G::W + cv * V) * int(sizeof(T));
+        } else {
+            const int yy = y0 + 2 * i, xx = x0 + cv * V;
+            in = in && yy < Hp && xx < Wp;
+            off = (yy * Wp + xx) * int(sizeof(T));
+        }
+        off = in ? off : kOutOfRange;
 #pragma unroll
         for (int ch = 0; ch < NCH; ++ch) {
-            const int col = cv * V + ch * CW;
-            const float* x0 = lds + G::uidx(0, pl, 0, 2 * i, col);
             float r0[CW], r1[CW];
-            lds_get<CW, G::al(0)>(x0, r0);
-            lds_get<CW, G::al(0)>(x0 + G::pitch(0), r1);
-            if constexpr (G::L >= 1) {
-                float cf[4][CW / 2];
-#pragma unroll
-                for (int sb = 0; sb < 4; ++sb)
-                    lds_get<CW / 2, G::al(1)>(lds + G::uidx(1, pl, sb, i, col / 2), cf[sb]);
-#pragma unroll
-                for (int m = 0; m < CW / 2; ++m) {
-                    float ll = cf[0][m];
-                    if constexpr (G::L >= 2) {
-                        constexpr int A2 = G::arr(2);
-                        const int j = col / 2 + m;
-                        const float* c2 = lds + G::uidx(2, pl, 0, i >> 1, j >> 1);
-                        const float sy2 = (i & 1) ? -1.f : 1.f, sx2 = (j & 1) ? -1.f : 1.f;
-                        const float e2 = fmaf(sy2, c2[2 * A2], c2[0]);
-                        const float f2 = fmaf(sy2, c2[3 * A2], c2[A2]);
-                        ll += fmaf(sx2, f2, e2);
-                    }
-                    const float lh = cf[1][m], hl = cf[2][m], hh = cf[3][m];
-                    const float e0 = ll + hl, f0 = lh + hh;  // row 2i   (row bit 0)
-                    const float e1 = ll - hl, f1 = lh - hh;  // row 2i+1 (row bit 1)
-                    r0[2 * m] += e0 + f0;
-                    r0[2 * m + 1] += e0 - f0;
-                    r1[2 * m] += e1 + f1;
-                    r1[2 * m + 1] += e1 - f1;
-                }
-            }
+            synth_rows<G, CW>(lds, pl, i, cv * V + ch * CW, r0, r1);
             union {
                 raw_t raw;
                 T e[CW];
@@ -917,49 +915,10 @@ __device__ __forceinline__ void final_store(const float* lds, T* __restrict__ ou
             store_vec<T, CW>(u1.e, r1);
             const int o = off + (in ? ch * BYTES : 0);
             buf_store(u0.raw, rs, o);
-            buf_store(u1.raw, rs, o + (in ? G::W * int(sizeof(T)) : 0));
+            buf_store(u1.raw, rs, o + (in ? row_elems * int(sizeof(T)) : 0));
         }
     }
 }
-
-// The finished group (y in the core of the level-0 array) -> HBM, ROWS x V
-// per item.  In tile mode the core sits at (y0, x0) of an Hp x Wp plane and
-// items outside the plane are skipped.
-template <class G, typename T>
-__device__ __forceinline__ void store_out(const float* lds, T* __restrict__ out, int b0, int B,
-                                          int C, int c, int tid, int y0 = 0, int x0 = 0,
-                                          int Hp = G::H, int Wp = G::W) {
-    using F = Fetch<G, T, false>;
-    constexpr int V = F::V, ROWS = F::ROWS, NV = F::NV, RB = F::RB, ITEMS = F::ITEMS;
-#pragma unroll
-    for (int it = 0; it < F::IT; ++it) {
-        const int item = tid + it * G::NT;
-        if (ITEMS % G::NT == 0 || item < ITEMS) {
-            const int cv = item % NV;
-            const int rb = (item / NV) % RB;
-            const int pl = item / (NV * RB);
-            const int b = b0 + pl;
-            const int yy = y0 + ROWS * rb, xx = x0 + cv * V;
-            bool in = b < B;
-            if constexpr (G::HT > 0) in = in && yy < Hp && xx < Wp;
-            if (in) {
-                const float* x0p = lds + G::uidx(0, pl, 0, ROWS * rb, cv * V);
-                T* o = out + ((size_t(b) * C + c) * Hp + yy) * Wp + xx;
-#pragma unroll
-                for (int k = 0; k < ROWS; ++k) {
-                    float v[V];
-                    lds_get<V, G::al(0)>(x0p + k * G::pitch(0), v);
-                    store_vec<T, V>(o + k * Wp, v);
-                }
-            }
-        }
-    }
-}
-
-// Wait for every outstanding vector-memory operation (the group's prefetched
-// input and stores issued a group earlier).  Stores are then issued only after
-// this point, so no later wait for prefetched data has to drain fresh stores.
-__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 // Folded filters into LDS: [0, KK) base, then (l, s) blocks, then the bias.
 template <class G, typename T, bool FLIP>
@@ -1097,7 +1056,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(
         }
         __syncthreads();
         // levels L..3 fold into the LL of the level above; level 2 folds into
-        // level 1 inside final_to_lds
+        // level 1 inside final_store
         static_for<0, L - 2>([&](auto lc) {
             cascade_level<G, L - decltype(lc)::value>(lds, tid);
             __syncthreads();
@@ -1519,7 +1478,7 @@ __global__ __launch_bounds__(NT) void k_tile_apply(
     if (q0 < q1) {
         int c, b, y0, x0;
         unit(q0, c, b, y0, x0);
-        fx.issue(in, b, B, C, c, tid, y0, x0, Hp, Wp);
+        fx.issue_tile_buf(in, b, B, C, c, tid, y0, x0, Hp, Wp);
     }
     for (int i = tid; i < G::side; i += NT) lds[i] = 0.f;
 
@@ -1536,7 +1495,7 @@ __global__ __launch_bounds__(NT) void k_tile_apply(
 
     float w[KK];
     float init = 0.f;
-    int cur = -1, pc = 0, pb = -1, py = 0, px = 0;
+    int cur = -1;
     for (long q = q0; q < q1; ++q) {
         int c, b, y0, x0;
         unit(q, c, b, y0, x0);
@@ -1547,11 +1506,6 @@ __global__ __launch_bounds__(NT) void k_tile_apply(
             for (int t = 0; t < KK; ++t) w[t] = wf[wsrc + t];
             init = job.lvl == 0 ? wf[G::NWF - 1] : 0.f;
             cur = c;
-        }
-        wait_vmem();
-        if (pb >= 0) {
-            store_out<G, T>(lds, out, pb, B, C, pc, tid, py, px, Hp, Wp);
-            __syncthreads();
         }
         fx.template commit<true, false>(lds, tid);
         __syncthreads();
@@ -1564,7 +1518,7 @@ __global__ __launch_bounds__(NT) void k_tile_apply(
         if (q + 1 < q1) {
             int cn, bn, yn, xn;
             unit(q + 1, cn, bn, yn, xn);
-            fx.issue(in, bn, B, C, cn, tid, yn, xn, Hp, Wp);
+            fx.issue_tile_buf(in, bn, B, C, cn, tid, yn, xn, Hp, Wp);
         }
         __syncthreads();
         if (job.on) {
@@ -1583,14 +1537,9 @@ __global__ __launch_bounds__(NT) void k_tile_apply(
             cascade_level<G, LT - decltype(lc)::value>(lds, tid);
             __syncthreads();
         });
-        final_to_lds<G, T>(lds, tid);
-        pc = c;
-        pb = b;
-        py = y0;
-        px = x0;
+        final_store<G, T>(lds, out, b, B, C, c, tid, y0, x0, Hp, Wp);
         __syncthreads();
     }
-    if (pb >= 0) store_out<G, T>(lds, out, pb, B, C, pc, tid, py, px, Hp, Wp);
 }
 
 // Weight-gradient partial sums of the base and levels 1..LT over the tiles of
@@ -1622,8 +1571,8 @@ __global__ __launch_bounds__(NT) void k_tile_bww(const T* __restrict__ x,
     if (u0 < u1) {
         int b, y0, x0;
         unit(u0, b, y0, x0);
-        fx.issue(x, b, B, C, c, tid, y0, x0, Hp, Wp);
-        fd.issue(dy, b, B, C, c, tid, y0, x0, Hp, Wp);
+        fx.issue_tile_buf(x, b, B, C, c, tid, y0, x0, Hp, Wp);
+        fd.issue_tile_buf(dy, b, B, C, c, tid, y0, x0, Hp, Wp);
     }
     for (int i = tid; i < G::side + G::vside; i += NT) lds[i] = 0.f;
     __syncthreads();
@@ -1653,14 +1602,13 @@ __global__ __launch_bounds__(NT) void k_tile_bww(const T* __restrict__ x,
     for (int u = u0; u < u1; ++u) {
         int b, y0, x0;
         unit(u, b, y0, x0);
-        wait_vmem();
         fx.template commit<true, false>(lds, tid);
         fd.template commit<false, true>(lds, tid);
         if (u + 1 < u1) {
             int bn, yn, xn;
             unit(u + 1, bn, yn, xn);
-            fx.issue(x, bn, B, C, c, tid, yn, xn, Hp, Wp);
-            fd.issue(dy, bn, B, C, c, tid, yn, xn, Hp, Wp);
+            fx.issue_tile_buf(x, bn, B, C, c, tid, yn, xn, Hp, Wp);
+            fd.issue_tile_buf(dy, bn, B, C, c, tid, yn, xn, Hp, Wp);
         }
         __syncthreads();
         static_for<Fetch<G, T, true>::LEVELS + 1, LT + 1>([&](auto lc) {

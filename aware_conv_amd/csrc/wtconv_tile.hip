@@ -361,6 +361,9 @@ bool tile_supported(const wtconv_shape& s) {
     const int vec = s.dtype == WTCONV_F32 ? 4 : 8;
     if ((s.H % 4) || (s.W % vec)) return false;
     if ((s.H % (1 << s.L)) || (s.W % (1 << s.L))) return false;
+    // buffer offsets within a plane are 32-bit
+    if (size_t(s.H) * size_t(s.W) * (s.dtype == WTCONV_F32 ? 4 : 2) >= (size_t(1) << 31))
+        return false;
     if (s.L > tile_lt(s) && deep_bww_lds(s) > kMaxLds) return false;
     return true;
 }
