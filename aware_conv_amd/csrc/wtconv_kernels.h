@@ -1200,6 +1200,14 @@ __global__ __launch_bounds__(NT) void k_plane_bww(
 // the same banks.
 template <class G>
 constexpr int bwd_dy_base() { return cdiv(G::side, 32) * 32; }
+// The fused tile backward keeps no filters in LDS.
+template <class G>
+constexpr size_t tile_bwd_lds_bytes() {
+    const size_t a = sizeof(float) * (bwd_dy_base<G>() + G::side);
+    const size_t b = sizeof(float) * G::NT * (G::KK + 1);
+    const size_t f = sizeof(float) * G::NWF;
+    return a > b ? (a > f ? a : f) : (b > f ? b : f);
+}
 template <class G>
 constexpr size_t bwd_lds_bytes() {
     const size_t a = sizeof(float) * (bwd_dy_base<G>() + G::side + G::NWF);
@@ -1648,5 +1656,135 @@ __global__ __launch_bounds__(NT) void k_tile_bww(const T* __restrict__ x,
 
     reduce_row<G>(lds, acc, sdy, part + (size_t(chunk) * C + c) * npart, npart, tid);
 }
+}  // namespace dev
+}  // namespace wtc
+
+namespace wtc {
+namespace dev {
+
+// Fused backward of a large plane's tiles: the input gradient of the base
+// conv and levels 1..LT (plus the deep levels' contribution `deep`, NULL if
+// none) and the weight-gradient partials of those levels, reading x and dy
+// once.  (channel, chunk) workgroups as in k_tile_bww.  dy and x are analysed
+// side by side, both with the tile's halos; each lane runs the
+// rotated-filter conv on its dy window, keeps the window's centre, masked to
+// its part of the core, and correlates it with its x window.  Two
+// workgroups per compute unit fit its LDS for k <= 5, which sets the
+// register budget; the 7 x 7 tiles need the LDS of one and take the
+// registers that leaves.
+template <int K, int LT, int TH, int TW, int NT, typename T>
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(K >= 7 ? 1 : 2))) void k_tile_bwd(
+    const T* __restrict__ x, const T* __restrict__ dy, const T* __restrict__ wb,
+    const T* __restrict__ sb, const T* __restrict__ ww, const T* __restrict__ sw,
+    const float* __restrict__ deep, T* __restrict__ dx, float* __restrict__ part, int B, int C,
+    int Hp, int Wp, int upw, int npart) {
+    using G = Geo<K, LT, TH, TW, 1, NT, LT>;
+    using F = Fetch<G, T, true>;
+    constexpr int KK = G::KK, Q = G::Q, R = G::R, DY = bwd_dy_base<G>();
+    extern __shared__ float lds[];
+    float* ldy = lds + DY;
+    const int tid = threadIdx.x;
+    const int c = blockIdx.x % C;
+    const int chunk = blockIdx.x / C;
+    const int ntx = cdiv(Wp, TW), nty = cdiv(Hp, TH);
+    const int units = B * nty * ntx;
+    const int u0 = chunk * upw;
+    const int u1 = min(u0 + upw, units);
+    auto unit = [&](int u, int& b, int& y0, int& x0) {
+        b = u / (nty * ntx);
+        const int t = u % (nty * ntx);
+        y0 = (t / ntx) * TH;
+        x0 = (t % ntx) * TW;
+    };
+    F fx, fd;
+    if (u0 < u1) {
+        int b, y0, x0;
+        unit(u0, b, y0, x0);
+        fx.issue_tile_buf(x, b, B, C, c, tid, y0, x0, Hp, Wp);
+        fd.issue_tile_buf(dy, b, B, C, c, tid, y0, x0, Hp, Wp);
+    }
+    const Job job = decode_job<G>(tid);
+    const int wsrc = job.lvl == 0 ? 0 : KK * (1 + (job.lvl - 1) * 4 + job.s);
+    const int win = window_index<G>(job);
+    const int pitch = level_pitch<G>(job.lvl);
+    const int hrows = by_level<G>(job.lvl, [](auto lc) { return G::hl(decltype(lc)::value); });
+    const int wcols = by_level<G>(job.lvl, [](auto lc) { return G::wl(decltype(lc)::value); });
+    const int nrows = min(Q, hrows - job.grp * Q);
+    const int ncols = min(R, wcols - job.strip * R);
+    const bool full = nrows == Q && ncols == R;
+    const int dst = win + G::p * pitch + G::p;
+    // the folded filters pass through the head of the x side on their way to
+    // registers, so that two workgroups fit a compute unit's LDS at k = 5
+    float w[KK];
+    fold_weights<G, T, true>(lds, wb, wb, sb, ww, sw, C, c, tid);
+    __syncthreads();
+#pragma unroll
+    for (int t = 0; t < KK; ++t) w[t] = lds[wsrc + t];
+    __syncthreads();
+    for (int i = tid; i < DY + G::side; i += NT) lds[i] = 0.f;
+    __syncthreads();
+    float gacc[KK];
+#pragma unroll
+    for (int t = 0; t < KK; ++t) gacc[t] = 0.f;
+    float sdy = 0.f;
+
+    for (int u = u0; u < u1; ++u) {
+        int b, y0, x0;
+        unit(u, b, y0, x0);
+        fx.template commit<true, false>(lds, tid);
+        fd.template commit<true, false>(ldy, tid);
+        __syncthreads();
+        static_for<F::LEVELS + 1, LT + 1>([&](auto lc) {
+            analysis_level<G, decltype(lc)::value, false>(lds, tid);
+            analysis_level<G, decltype(lc)::value, false>(ldy, tid);
+            __syncthreads();
+        });
+        float acc[Q][R];
+        if (job.on) {
+            float d[Q][R];
+            conv_tile<K, Q, R, true>(ldy + win, pitch, w, 0.f, acc, d);
+            // the centre past the job's part of the core is halo (real
+            // neighbours), and the core past the plane's edge reads zeros
+#pragma unroll
+            for (int qq = 0; qq < Q; ++qq)
+#pragma unroll
+                for (int j = 0; j < R; ++j)
+                    if (!full && !(qq < nrows && j < ncols)) d[qq][j] = 0.f;
+            if (job.lvl == 0)
+#pragma unroll
+                for (int qq = 0; qq < Q; ++qq)
+#pragma unroll
+                    for (int j = 0; j < R; ++j) sdy += d[qq][j];
+            corr_tile<K, Q, R>(d, lds + win, pitch, gacc);
+        }
+        if (u + 1 < u1) {
+            int bn, yn, xn;
+            unit(u + 1, bn, yn, xn);
+            fx.issue_tile_buf(x, bn, B, C, c, tid, yn, xn, Hp, Wp);
+            fd.issue_tile_buf(dy, bn, B, C, c, tid, yn, xn, Hp, Wp);
+        }
+        __syncthreads();
+        if (job.on) {
+#pragma unroll
+            for (int qq = 0; qq < Q; ++qq)
+#pragma unroll
+                for (int j = 0; j < R; ++j)
+                    if (full || (qq < nrows && j < ncols)) ldy[dst + qq * pitch + j] = acc[qq][j];
+        }
+        __syncthreads();
+        if (deep) {
+            add_deep<G>(ldy, deep, b, C, c, y0, x0, Hp, Wp, tid);
+            __syncthreads();
+        }
+        static_for<0, LT - 2>([&](auto lc) {
+            cascade_level<G, LT - decltype(lc)::value>(ldy, tid);
+            __syncthreads();
+        });
+        final_store<G, T>(ldy, dx, b, B, C, c, tid, y0, x0, Hp, Wp);
+        __syncthreads();
+    }
+    reduce_row<G>(lds, gacc, sdy, part + (size_t(chunk) * C + c) * npart, npart, tid);
+}
+
 }  // namespace dev
 }  // namespace wtc

@@ -368,8 +368,8 @@ bool tile_supported(const wtconv_shape& s) {
     return true;
 }
 
-// Workspace: [partial rows | deep contribution D] (used one after the other),
-// then the box sums P of x and of dy (levels deeper than the tile's).
+// Workspace: [partial rows | deep contribution D | box sums P of x | of dy]
+// (D and the box sums only with levels deeper than the tile's).
 namespace {
 constexpr size_t kAlign = 256;
 size_t align_up(size_t n) { return (n + kAlign - 1) / kAlign * kAlign; }
@@ -377,19 +377,20 @@ size_t p_bytes(const wtconv_shape& s) {
     const int LT = tile_lt(s);
     return size_t(s.B) * s.C * (s.H >> LT) * (s.W >> LT) * sizeof(float);
 }
-size_t head_bytes(const wtconv_shape& s) {
+size_t rows_bytes(const wtconv_shape& s) {
     const int LT = tile_lt(s);
     const size_t KK = size_t(s.k) * s.k, npart = KK + 1 + 4 * size_t(s.L) * KK;
     const int units = tile_units_per_channel(s);
     const size_t chunks = size_t(units < kMaxTileChunks ? units : kMaxTileChunks) +
                           (s.L > LT ? size_t(s.B) : 0);
-    const size_t bww = chunks * s.C * npart * sizeof(float);
-    const size_t deep = s.L > LT ? p_bytes(s) : 0;
-    return align_up(bww > deep ? bww : deep);
+    return align_up(chunks * s.C * npart * sizeof(float));
+}
+float* d_of(const wtconv_shape& s, void* workspace) {
+    return reinterpret_cast<float*>(static_cast<char*>(workspace) + rows_bytes(s));
 }
 float* p_of(const wtconv_shape& s, void* workspace, int which) {
-    return reinterpret_cast<float*>(static_cast<char*>(workspace) + head_bytes(s) +
-                                    which * align_up(p_bytes(s)));
+    return reinterpret_cast<float*>(static_cast<char*>(workspace) + rows_bytes(s) +
+                                    (1 + which) * align_up(p_bytes(s)));
 }
 
 hipError_t launch_box_sums(const wtconv_shape& s, const void* src, float* P,
@@ -405,7 +406,7 @@ hipError_t launch_box_sums(const wtconv_shape& s, const void* src, float* P,
     return hipGetLastError();
 }
 
-// Deep levels' contribution D (head of the workspace) from the box sums P.
+// Deep levels' contribution D from the box sums P.
 hipError_t launch_deep_apply(const wtconv_shape& s, const float* P, const Params& p, bool flip,
                              float* deep, hipStream_t stream) {
     const int LT = tile_lt(s);
@@ -486,7 +487,7 @@ hipError_t launch_weight_grads(const wtconv_shape& s, const TileVariant* v, cons
 size_t tile_workspace_bytes(const wtconv_shape& s) {
     if (!tile_supported(s) || s.B == 0 || s.C == 0) return 0;
     const int LT = tile_lt(s);
-    return head_bytes(s) + (s.L > LT ? 2 * align_up(p_bytes(s)) : 0);
+    return rows_bytes(s) + (s.L > LT ? 3 * align_up(p_bytes(s)) : 0);
 }
 
 hipError_t tile_apply(const wtconv_shape& s, const void* in, const Params& p, void* out,
@@ -495,7 +496,7 @@ hipError_t tile_apply(const wtconv_shape& s, const void* in, const Params& p, vo
     if (!v) return hipErrorInvalidValue;
     float* deep = nullptr;
     if (s.L > tile_lt(s)) {
-        deep = static_cast<float*>(workspace);
+        deep = d_of(s, workspace);
         float* P = p_of(s, workspace, 0);
         hipError_t e = launch_box_sums(s, in, P, stream);
         if (e == hipSuccess) e = launch_deep_apply(s, P, p, flip, deep, stream);
@@ -521,21 +522,59 @@ hipError_t tile_bwd_weight(const wtconv_shape& s, const void* x, const void* dy,
     return launch_weight_grads(s, v, x, dy, Px, Pdy, p, g, workspace, stream);
 }
 
+// Fused: box sums of x and dy and the deep input gradient D (deeper levels
+// only), then one pass over the tiles for dx and the tiles' weight partials,
+// the deep levels' partials, and the finalize.
 hipError_t tile_bwd(const wtconv_shape& s, const void* x, const void* dy, const Params& p,
                     void* dx, const Grads& g, void* workspace, hipStream_t stream) {
     const TileVariant* v = find_tile(s);
     if (!v) return hipErrorInvalidValue;
-    // the weight gradient first (its rows share the head of the workspace
-    // with D), keeping the box sums of dy for the input gradient's deep levels
-    hipError_t e = tile_bwd_weight(s, x, dy, p, g, workspace, stream);
-    if (e != hipSuccess) return e;
+    const int LT = tile_lt(s);
+    hipError_t e;
     float* deep = nullptr;
-    if (s.L > tile_lt(s)) {
-        deep = static_cast<float*>(workspace);
-        e = launch_deep_apply(s, p_of(s, workspace, 1), p, true, deep, stream);
+    float* Px = nullptr;
+    float* Pdy = nullptr;
+    if (s.L > LT) {
+        deep = d_of(s, workspace);
+        Px = p_of(s, workspace, 0);
+        Pdy = p_of(s, workspace, 1);
+        if ((e = launch_box_sums(s, x, Px, stream)) != hipSuccess) return e;
+        if ((e = launch_box_sums(s, dy, Pdy, stream)) != hipSuccess) return e;
+        if ((e = launch_deep_apply(s, Pdy, p, true, deep, stream)) != hipSuccess) return e;
+    }
+    if ((e = set_lds(v->bwd, v->lds_bwd)) != hipSuccess) return e;
+    const int nchunk = tile_chunks(s, resident(v->bwd, v->NT, v->lds_bwd));
+    const int units = tile_units_per_channel(s);
+    int upw = (units + nchunk - 1) / nchunk;
+    int B = s.B, C = s.C, H = s.H, W = s.W, L = s.L, LTv = LT;
+    int npart = s.k * s.k * (1 + 4 * s.L) + 1;
+    float* part = static_cast<float*>(workspace);
+    const void* wb = p.w_base;
+    const void* sb = p.s_base;
+    const void* ww = p.w_wav;
+    const void* sw = p.s_wav;
+    const float* dp = deep;
+    {
+        void* args[] = {&x, &dy, &wb, &sb, &ww, &sw, &dp, &dx, &part, &B, &C, &H, &W, &upw,
+                        &npart};
+        e = hipLaunchKernel(v->bwd, dim3(unsigned(nchunk) * unsigned(s.C)), dim3(v->NT), args,
+                            v->lds_bwd, stream);
+        if (e == hipSuccess) e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
-    return launch_tiles(s, v, dy, p, dx, true, deep, stream);
+    int rows = nchunk;
+    if (s.L > LT) {
+        const void* fn = deep_bww_fn(s.k);
+        const size_t lds = deep_bww_lds(s);
+        if ((e = set_lds(fn, lds)) != hipSuccess) return e;
+        int row0 = nchunk;
+        void* args[] = {&Px, &Pdy, &part, &B, &C, &H, &W, &L, &LTv, &row0, &npart};
+        e = hipLaunchKernel(fn, dim3(unsigned(B) * unsigned(C)), dim3(256), args, lds, stream);
+        if (e == hipSuccess) e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        rows += s.B;
+    }
+    return finalize_grads(s, part, rows, p, g, stream);
 }
 
 }  // namespace wtc

@@ -11,7 +11,8 @@ struct TileVariant {
     const void* fwd;
     const void* bwi;
     const void* bww;
-    size_t lds_apply, lds_bww;
+    const void* bwd;  // fused backward: input gradient and weight partials
+    size_t lds_apply, lds_bww, lds_bwd;
 };
 
 constexpr int kTileH = 32, kTileW = 32, kTileNT = 256;
@@ -24,7 +25,8 @@ TileVariant make_tile_variant(int dtype) {
         reinterpret_cast<const void*>(&dev::k_tile_apply<K, LT, kTileH, kTileW, kTileNT, T, false>),
         reinterpret_cast<const void*>(&dev::k_tile_apply<K, LT, kTileH, kTileW, kTileNT, T, true>),
         reinterpret_cast<const void*>(&dev::k_tile_bww<K, LT, kTileH, kTileW, kTileNT, T>),
-        dev::apply_lds_bytes<G>(), dev::bww_lds_bytes<G>()};
+        reinterpret_cast<const void*>(&dev::k_tile_bwd<K, LT, kTileH, kTileW, kTileNT, T>),
+        dev::apply_lds_bytes<G>(), dev::bww_lds_bytes<G>(), dev::tile_bwd_lds_bytes<G>()};
 }
 
 // Tables of the per-k translation units (LT = 1, 2, 3; fp32 and fp16).

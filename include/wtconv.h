@@ -142,8 +142,7 @@ int wtconv_bwd_weight(const wtconv_shape* s, const void* x, const void* dy,
  * [B][C][H][W] must overlap neither x nor dy; the gradients are overwritten.
  * Results equal the two separate calls up to floating-point evaluation
  * order, and the parameter gradients are bitwise reproducible for a given
- * shape.  Planes handled as tiles (the largest ones) run the two passes one
- * after the other.  Needs wtconv_workspace_size() bytes of workspace.
+ * shape.  Needs wtconv_workspace_size() bytes of workspace.
  */
 int wtconv_bwd(const wtconv_shape* s, const void* x, const void* dy,
                const void* w_base, const void* b_base, const void* s_base,
