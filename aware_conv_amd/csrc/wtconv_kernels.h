@@ -1665,7 +1665,7 @@ namespace dev {
 // Fused backward of a large plane's tiles: the input gradient of the base
 // conv and levels 1..LT (plus the deep levels' contribution `deep`, NULL if
 // none) and the weight-gradient partials of those levels, reading x and dy
-// once.  (channel, chunk) workgroups as in k_tile_bww.  dy and x are analysed
+// once; with `px` (NULL: none) also the box sums U^LT_LL(x) of the planes.  (channel, chunk) workgroups as in k_tile_bww.  dy and x are analysed
 // side by side, both with the tile's halos; each lane runs the
 // rotated-filter conv on its dy window, keeps the window's centre, masked to
 // its part of the core, and correlates it with its x window.  Two
@@ -1676,8 +1676,8 @@ template <int K, int LT, int TH, int TW, int NT, typename T>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(K >= 7 ? 1 : 2))) void k_tile_bwd(
     const T* __restrict__ x, const T* __restrict__ dy, const T* __restrict__ wb,
     const T* __restrict__ sb, const T* __restrict__ ww, const T* __restrict__ sw,
-    const float* __restrict__ deep, T* __restrict__ dx, float* __restrict__ part, int B, int C,
-    int Hp, int Wp, int upw, int npart) {
+    const float* __restrict__ deep, T* __restrict__ dx, float* __restrict__ part,
+    float* __restrict__ px, int B, int C, int Hp, int Wp, int upw, int npart) {
     using G = Geo<K, LT, TH, TW, 1, NT, LT>;
     using F = Fetch<G, T, true>;
     constexpr int KK = G::KK, Q = G::Q, R = G::R, DY = bwd_dy_base<G>();
@@ -1756,6 +1756,19 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(K >= 7 ? 1 :
 #pragma unroll
                     for (int j = 0; j < R; ++j) sdy += d[qq][j];
             corr_tile<K, Q, R>(d, lds + win, pitch, gacc);
+        }
+        if (px) {
+            // the core of U^LT_LL(x): the tile's share of the box sums that
+            // the deeper levels' weight gradient starts from
+            constexpr int h = G::hl(LT), w = G::wl(LT);
+            const int hd = Hp >> LT, wd = Wp >> LT;
+            if (tid < h * w) {
+                const int i = tid / w, j = tid % w;
+                const int gy = (y0 >> LT) + i, gx = (x0 >> LT) + j;
+                if (gy < hd && gx < wd)
+                    px[(size_t(b) * C + c) * hd * wd + size_t(gy) * wd + gx] =
+                        lds[G::uidx(LT, 0, 0, i, j)];
+            }
         }
         if (u + 1 < u1) {
             int bn, yn, xn;

@@ -522,9 +522,10 @@ hipError_t tile_bwd_weight(const wtconv_shape& s, const void* x, const void* dy,
     return launch_weight_grads(s, v, x, dy, Px, Pdy, p, g, workspace, stream);
 }
 
-// Fused: box sums of x and dy and the deep input gradient D (deeper levels
-// only), then one pass over the tiles for dx and the tiles' weight partials,
-// the deep levels' partials, and the finalize.
+// Fused: with deeper levels, the box sums of dy and from them the deep input
+// gradient D; then one pass over the tiles for dx, the tiles' weight
+// partials and (deeper levels) the box sums of x; the deep levels' partials;
+// the finalize.
 hipError_t tile_bwd(const wtconv_shape& s, const void* x, const void* dy, const Params& p,
                     void* dx, const Grads& g, void* workspace, hipStream_t stream) {
     const TileVariant* v = find_tile(s);
@@ -538,7 +539,6 @@ hipError_t tile_bwd(const wtconv_shape& s, const void* x, const void* dy, const 
         deep = d_of(s, workspace);
         Px = p_of(s, workspace, 0);
         Pdy = p_of(s, workspace, 1);
-        if ((e = launch_box_sums(s, x, Px, stream)) != hipSuccess) return e;
         if ((e = launch_box_sums(s, dy, Pdy, stream)) != hipSuccess) return e;
         if ((e = launch_deep_apply(s, Pdy, p, true, deep, stream)) != hipSuccess) return e;
     }
@@ -555,8 +555,8 @@ hipError_t tile_bwd(const wtconv_shape& s, const void* x, const void* dy, const 
     const void* sw = p.s_wav;
     const float* dp = deep;
     {
-        void* args[] = {&x, &dy, &wb, &sb, &ww, &sw, &dp, &dx, &part, &B, &C, &H, &W, &upw,
-                        &npart};
+        void* args[] = {&x,    &dy, &wb, &sb, &ww, &sw, &dp,  &dx,
+                        &part, &Px, &B,  &C,  &H,  &W,  &upw, &npart};
         e = hipLaunchKernel(v->bwd, dim3(unsigned(nchunk) * unsigned(s.C)), dim3(v->NT), args,
                             v->lds_bwd, stream);
         if (e == hipSuccess) e = hipGetLastError();
