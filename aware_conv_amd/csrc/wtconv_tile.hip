@@ -433,7 +433,8 @@ hipError_t launch_tiles(const wtconv_shape& s, const TileVariant* v, const void*
     const void* fn = flip ? v->bwi : v->fwd;
     hipError_t e;
     if ((e = set_lds(fn, v->lds_apply)) != hipSuccess) return e;
-    const long total = long(s.C) * tile_units_per_channel(s);
+    const long units = long(s.B) * ((s.H + v->ATH - 1) / v->ATH) * ((s.W + v->ATW - 1) / v->ATW);
+    const long total = long(s.C) * units;
     long nwg = resident(fn, v->NT, v->lds_apply);
     if (nwg > total) nwg = total;
     const void* bb = flip ? p.w_base : p.b_base;  // unread when flipped

@@ -115,9 +115,12 @@ def test_small_shapes_ragged_batch(k, L, H, W, dtype):
     assert_parity(d, dtype, "k%d L%d %dx%d %s" % (k, L, H, W, dtype))
 
 
-TILED = [  # k, L, H, W, dtype: planes handled as 32 x 32 tiles (+ deep levels)
+TILED = [  # k, L, H, W, dtype: planes handled as tiles (+ deep levels); the
+    # forward and input gradient use 32 x 64 tiles for k <= 5, the rest 32 x 32
     (3, 3, 64, 64, "f32"),    # three levels in the tile, no deep levels
     (5, 2, 48, 80, "f32"),    # partial edge tiles
+    (5, 3, 40, 136, "f32"),   # two full 64-wide tiles and an 8-wide one per row
+    (5, 1, 24, 72, "f16"),    # partial tiles, fp16
     (3, 2, 36, 40, "f32"),    # partial tiles, H != W
     (1, 1, 40, 40, "f32"),    # k = 1: no halo
     (5, 4, 96, 64, "f32"),    # one deep level
