@@ -9,8 +9,9 @@ the fused wtconv_bwd (input and parameter gradients reading x and dy once),
 with --backward split the two calls wtconv_bwd_input and wtconv_bwd_weight.
 By default the step's kernels are replayed from a HIP graph (one per buffer
 set), as a training loop that captures its step would run them; --launch
-eager times the calls as issued (also reported as eager_ms_per_step).  W untimed steps, then exactly K timed steps bracketed by
-device synchronisation; value = images per second over the K steps.  Each
+eager times the calls as issued (also reported as eager_ms_per_step).
+W untimed steps, then exactly K timed steps bracketed by device
+synchronisation; value = images per second over the K steps.  Each
 step reads its own set of buffers, rotating over enough sets that no step
 finds the previous step's tensors in the 256 MB last-level cache.
 
@@ -57,7 +58,7 @@ def conv_flops_per_pixel(L, k):
 def io_model_reference(L):
     """Elements moved through device memory per input element by the unfused
     reference forward: 7 for the base path and the final add, 10.75 per level
-    on a grid 4^(l-1) times smaller (see the design doc for the op-by-op count)."""
+    on a grid 4^(l-1) times smaller."""
     return 7.0 + 10.75 * sum(4.0 ** (-j) for j in range(L))
 
 
@@ -80,7 +81,7 @@ def call_of(kernel_name, fused):
         c = "wtconv_bwd_input" if head.rstrip("> ").endswith("true") else "wtconv_fwd"
     elif "k_plane_bww" in n or "k_tile_bww" in n or "k_deep_bww" in n or "k_bww_final" in n:
         c = "wtconv_bwd_weight"
-    elif "k_plane_bwd" in n:
+    elif "k_plane_bwd" in n or "k_tile_bwd" in n:
         c = "wtconv_bwd"
     if fused and c in ("wtconv_bwd_input", "wtconv_bwd_weight"):
         c = "wtconv_bwd"
