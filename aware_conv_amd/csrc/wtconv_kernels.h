@@ -1441,6 +1441,33 @@ __global__ __launch_bounds__(256) void k_bww_final(
 // Contribution of the levels deeper than the tile's (computed per plane by
 // the deep kernels, fp32 at level-LT resolution) added to the level-LT LL
 // coefficients of the tile's core.
+// Position of a tile-kernel unit: channel, image, tile row and column, the
+// column fastest.  Decoded from a unit index once per workgroup and then
+// stepped, so the loop carries no divisions.
+struct TileCursor {
+    int c, b, ty, tx;
+    __device__ static TileCursor at(long q, int B, int nty, int ntx) {
+        const long per_c = long(B) * nty * ntx;
+        const long r = q % per_c;
+        const int t = int(r % (long(nty) * ntx));
+        return TileCursor{int(q / per_c), int(r / (long(nty) * ntx)), t / ntx, t % ntx};
+    }
+    __device__ TileCursor next(int B, int nty, int ntx) const {
+        TileCursor n = *this;
+        if (++n.tx == ntx) {
+            n.tx = 0;
+            if (++n.ty == nty) {
+                n.ty = 0;
+                if (++n.b == B) {
+                    n.b = 0;
+                    ++n.c;
+                }
+            }
+        }
+        return n;
+    }
+};
+
 template <class G>
 __device__ __forceinline__ void add_deep(float* lds, const float* __restrict__ deep, int b,
                                          int C, int c, int y0, int x0, int Hp, int Wp, int tid) {
@@ -1474,20 +1501,9 @@ __global__ __launch_bounds__(NT) void k_tile_apply(
     const long total = long(C) * per_c;
     const long q0 = total * blockIdx.x / gridDim.x;
     const long q1 = total * (blockIdx.x + 1) / gridDim.x;
-    auto unit = [&](long q, int& c, int& b, int& y0, int& x0) {
-        c = int(q / per_c);
-        long r = q % per_c;
-        b = int(r / (long(nty) * ntx));
-        const int t = int(r % (long(nty) * ntx));
-        y0 = (t / ntx) * TH;
-        x0 = (t % ntx) * TW;
-    };
+    TileCursor cu = TileCursor::at(q0, B, nty, ntx);
     F fx;
-    if (q0 < q1) {
-        int c, b, y0, x0;
-        unit(q0, c, b, y0, x0);
-        fx.issue_tile_buf(in, b, B, C, c, tid, y0, x0, Hp, Wp);
-    }
+    if (q0 < q1) fx.issue_tile_buf(in, cu.b, B, C, cu.c, tid, cu.ty * TH, cu.tx * TW, Hp, Wp);
     for (int i = tid; i < G::side; i += NT) lds[i] = 0.f;
 
     const Job job = decode_job<G>(tid);
@@ -1505,8 +1521,8 @@ __global__ __launch_bounds__(NT) void k_tile_apply(
     float init = 0.f;
     int cur = -1;
     for (long q = q0; q < q1; ++q) {
-        int c, b, y0, x0;
-        unit(q, c, b, y0, x0);
+        const int c = cu.c, b = cu.b, y0 = cu.ty * TH, x0 = cu.tx * TW;
+        const TileCursor nx = cu.next(B, nty, ntx);
         if (c != cur) {
             fold_weights<G, T, FLIP>(wf, wb, bb, sb, ww, sw, C, c, tid);
             __syncthreads();
@@ -1523,11 +1539,7 @@ __global__ __launch_bounds__(NT) void k_tile_apply(
         });
         float acc[Q][R];
         if (job.on) conv_tile<K, Q, R>(lds + win, pitch, w, init, acc);
-        if (q + 1 < q1) {
-            int cn, bn, yn, xn;
-            unit(q + 1, cn, bn, yn, xn);
-            fx.issue_tile_buf(in, bn, B, C, cn, tid, yn, xn, Hp, Wp);
-        }
+        if (q + 1 < q1) fx.issue_tile_buf(in, nx.b, B, C, nx.c, tid, nx.ty * TH, nx.tx * TW, Hp, Wp);
         __syncthreads();
         if (job.on) {
 #pragma unroll
@@ -1546,6 +1558,7 @@ __global__ __launch_bounds__(NT) void k_tile_apply(
             __syncthreads();
         });
         final_store<G, T>(lds, out, b, B, C, c, tid, y0, x0, Hp, Wp);
+        cu = nx;
         __syncthreads();
     }
 }
@@ -1568,19 +1581,12 @@ __global__ __launch_bounds__(NT) void k_tile_bww(const T* __restrict__ x,
     const int units = B * nty * ntx;
     const int u0 = chunk * upw;
     const int u1 = min(u0 + upw, units);
-    auto unit = [&](int u, int& b, int& y0, int& x0) {
-        b = u / (nty * ntx);
-        const int t = u % (nty * ntx);
-        y0 = (t / ntx) * TH;
-        x0 = (t % ntx) * TW;
-    };
+    TileCursor cu = TileCursor::at(u0, B, nty, ntx);  // c stays 0: one channel
     Fetch<G, T, true> fx;
     Fetch<G, T, false> fd;
     if (u0 < u1) {
-        int b, y0, x0;
-        unit(u0, b, y0, x0);
-        fx.issue_tile_buf(x, b, B, C, c, tid, y0, x0, Hp, Wp);
-        fd.issue_tile_buf(dy, b, B, C, c, tid, y0, x0, Hp, Wp);
+        fx.issue_tile_buf(x, cu.b, B, C, c, tid, cu.ty * TH, cu.tx * TW, Hp, Wp);
+        fd.issue_tile_buf(dy, cu.b, B, C, c, tid, cu.ty * TH, cu.tx * TW, Hp, Wp);
     }
     for (int i = tid; i < G::side + G::vside; i += NT) lds[i] = 0.f;
     __syncthreads();
@@ -1608,15 +1614,13 @@ __global__ __launch_bounds__(NT) void k_tile_bww(const T* __restrict__ x,
     float sdy = 0.f;
 
     for (int u = u0; u < u1; ++u) {
-        int b, y0, x0;
-        unit(u, b, y0, x0);
+        const int b = cu.b, y0 = cu.ty * TH, x0 = cu.tx * TW;
+        const TileCursor nx = cu.next(B, nty, ntx);
         fx.template commit<true, false>(lds, tid);
         fd.template commit<false, true>(lds, tid);
         if (u + 1 < u1) {
-            int bn, yn, xn;
-            unit(u + 1, bn, yn, xn);
-            fx.issue_tile_buf(x, bn, B, C, c, tid, yn, xn, Hp, Wp);
-            fd.issue_tile_buf(dy, bn, B, C, c, tid, yn, xn, Hp, Wp);
+            fx.issue_tile_buf(x, nx.b, B, C, c, tid, nx.ty * TH, nx.tx * TW, Hp, Wp);
+            fd.issue_tile_buf(dy, nx.b, B, C, c, tid, nx.ty * TH, nx.tx * TW, Hp, Wp);
         }
         __syncthreads();
         static_for<Fetch<G, T, true>::LEVELS + 1, LT + 1>([&](auto lc) {
@@ -1651,6 +1655,7 @@ __global__ __launch_bounds__(NT) void k_tile_bww(const T* __restrict__ x,
             }
             corr_tile<K, Q, R>(d, lds + win, pitch, acc);
         }
+        cu = nx;
         __syncthreads();
     }
 
@@ -1690,18 +1695,11 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(K >= 7 ? 1 :
     const int units = B * nty * ntx;
     const int u0 = chunk * upw;
     const int u1 = min(u0 + upw, units);
-    auto unit = [&](int u, int& b, int& y0, int& x0) {
-        b = u / (nty * ntx);
-        const int t = u % (nty * ntx);
-        y0 = (t / ntx) * TH;
-        x0 = (t % ntx) * TW;
-    };
+    TileCursor cu = TileCursor::at(u0, B, nty, ntx);  // c stays 0: one channel
     F fx, fd;
     if (u0 < u1) {
-        int b, y0, x0;
-        unit(u0, b, y0, x0);
-        fx.issue_tile_buf(x, b, B, C, c, tid, y0, x0, Hp, Wp);
-        fd.issue_tile_buf(dy, b, B, C, c, tid, y0, x0, Hp, Wp);
+        fx.issue_tile_buf(x, cu.b, B, C, c, tid, cu.ty * TH, cu.tx * TW, Hp, Wp);
+        fd.issue_tile_buf(dy, cu.b, B, C, c, tid, cu.ty * TH, cu.tx * TW, Hp, Wp);
     }
     const Job job = decode_job<G>(tid);
     const int wsrc = job.lvl == 0 ? 0 : KK * (1 + (job.lvl - 1) * 4 + job.s);
@@ -1729,8 +1727,8 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(K >= 7 ? 1 :
     float sdy = 0.f;
 
     for (int u = u0; u < u1; ++u) {
-        int b, y0, x0;
-        unit(u, b, y0, x0);
+        const int b = cu.b, y0 = cu.ty * TH, x0 = cu.tx * TW;
+        const TileCursor nx = cu.next(B, nty, ntx);
         fx.template commit<true, false>(lds, tid);
         fd.template commit<true, false>(ldy, tid);
         __syncthreads();
@@ -1771,10 +1769,8 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(K >= 7 ? 1 :
             }
         }
         if (u + 1 < u1) {
-            int bn, yn, xn;
-            unit(u + 1, bn, yn, xn);
-            fx.issue_tile_buf(x, bn, B, C, c, tid, yn, xn, Hp, Wp);
-            fd.issue_tile_buf(dy, bn, B, C, c, tid, yn, xn, Hp, Wp);
+            fx.issue_tile_buf(x, nx.b, B, C, c, tid, nx.ty * TH, nx.tx * TW, Hp, Wp);
+            fd.issue_tile_buf(dy, nx.b, B, C, c, tid, nx.ty * TH, nx.tx * TW, Hp, Wp);
         }
         __syncthreads();
         if (job.on) {
@@ -1794,6 +1790,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(K >= 7 ? 1 :
             __syncthreads();
         });
         final_store<G, T>(ldy, dx, b, B, C, c, tid, y0, x0, Hp, Wp);
+        cu = nx;
         __syncthreads();
     }
     reduce_row<G>(lds, gacc, sdy, part + (size_t(chunk) * C + c) * npart, npart, tid);
