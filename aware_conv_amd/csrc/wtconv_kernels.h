@@ -1468,16 +1468,41 @@ struct TileCursor {
     }
 };
 
+// The deeper levels' contribution to a tile's level-LT LL core, in two
+// halves: fetch_deep loads it into registers when a tile starts (so the load
+// is in flight during the conv), add_deep adds it to LDS after the conv
+// results are written.
 template <class G>
-__device__ __forceinline__ void add_deep(float* lds, const float* __restrict__ deep, int b,
-                                         int C, int c, int y0, int x0, int Hp, int Wp, int tid) {
-    constexpr int LT = G::L, h = G::hl(LT), w = G::wl(LT), ITEMS = h * w;
+struct DeepRegs {
+    static constexpr int LT = G::L, h = G::hl(LT), w = G::wl(LT), ITEMS = h * w;
+    static constexpr int N = cdiv(ITEMS, G::NT);
+    float v[N];
+};
+
+template <class G>
+__device__ __forceinline__ void fetch_deep(DeepRegs<G>& r, const float* __restrict__ deep, int b,
+                                           int C, int c, int y0, int x0, int Hp, int Wp,
+                                           int tid) {
+    using D = DeepRegs<G>;
+    constexpr int LT = D::LT;
     const int hd = Hp >> LT, wd = Wp >> LT;
     const float* dp = deep + (size_t(b) * C + c) * hd * wd;
-    for (int item = tid; item < ITEMS; item += G::NT) {
-        const int i = item / w, j = item % w;
+#pragma unroll
+    for (int n = 0; n < D::N; ++n) {
+        const int item = tid + n * G::NT;
+        const int i = item / D::w, j = item % D::w;
         const int gy = (y0 >> LT) + i, gx = (x0 >> LT) + j;
-        if (gy < hd && gx < wd) lds[G::uidx(LT, 0, 0, i, j)] += dp[gy * wd + gx];
+        r.v[n] = item < D::ITEMS && gy < hd && gx < wd ? dp[gy * wd + gx] : 0.f;
+    }
+}
+
+template <class G>
+__device__ __forceinline__ void add_deep(float* lds, const DeepRegs<G>& r, int tid) {
+    using D = DeepRegs<G>;
+#pragma unroll
+    for (int n = 0; n < D::N; ++n) {
+        const int item = tid + n * G::NT;
+        if (item < D::ITEMS) lds[G::uidx(D::LT, 0, 0, item / D::w, item % D::w)] += r.v[n];
     }
 }
 
@@ -1537,6 +1562,8 @@ __global__ __launch_bounds__(NT) void k_tile_apply(
             analysis_level<G, decltype(lc)::value, false>(lds, tid);
             __syncthreads();
         });
+        DeepRegs<G> dr;
+        if (deep) fetch_deep<G>(dr, deep, b, C, c, y0, x0, Hp, Wp, tid);
         float acc[Q][R];
         if (job.on) conv_tile<K, Q, R>(lds + win, pitch, w, init, acc);
         if (q + 1 < q1) fx.issue_tile_buf(in, nx.b, B, C, nx.c, tid, nx.ty * TH, nx.tx * TW, Hp, Wp);
@@ -1550,7 +1577,7 @@ __global__ __launch_bounds__(NT) void k_tile_apply(
         }
         __syncthreads();
         if (deep) {
-            add_deep<G>(lds, deep, b, C, c, y0, x0, Hp, Wp, tid);
+            add_deep<G>(lds, dr, tid);
             __syncthreads();
         }
         static_for<0, LT - 2>([&](auto lc) {
@@ -1737,6 +1764,8 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(K >= 7 ? 1 :
             analysis_level<G, decltype(lc)::value, false>(ldy, tid);
             __syncthreads();
         });
+        DeepRegs<G> dr;
+        if (deep) fetch_deep<G>(dr, deep, b, C, c, y0, x0, Hp, Wp, tid);
         float acc[Q][R];
         if (job.on) {
             float d[Q][R];
@@ -1782,7 +1811,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(K >= 7 ? 1 :
         }
         __syncthreads();
         if (deep) {
-            add_deep<G>(ldy, deep, b, C, c, y0, x0, Hp, Wp, tid);
+            add_deep<G>(ldy, dr, tid);
             __syncthreads();
         }
         static_for<0, LT - 2>([&](auto lc) {
