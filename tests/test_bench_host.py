@@ -1,0 +1,50 @@
+"""Host logic of bench.py: attribution of profiled kernels to entry points,
+the per-pass FLOP count, and the --gpus guard.  CPU only."""
+import os
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+
+import bench  # noqa: E402
+
+
+@pytest.mark.parametrize("name,fused,call", [
+    ("void wtc::dev::k_plane_apply<5, 2, 56, 56, 1, 256, float, false>(...)", True, "wtconv_fwd"),
+    ("void wtc::dev::k_plane_apply<5, 2, 56, 56, 1, 256, float, true>(...)", False, "wtconv_bwd_input"),
+    ("void wtc::dev::k_tile_apply<5, 3, 32, 64, 256, float, true>(...)", True, "wtconv_bwd"),
+    ("void wtc::dev::k_deep_apply<float, 5, false>(...)", True, "wtconv_fwd"),
+    ("void wtc::dev::k_plane_bww<5, 2, 56, 56, 1, 256, float>(...)", False, "wtconv_bwd_weight"),
+    ("void wtc::dev::k_deep_bww<5>(...)", True, "wtconv_bwd"),
+    ("void wtc::dev::k_bww_final<float>(...)", False, "wtconv_bwd_weight"),
+    ("void wtc::dev::k_plane_bwd<5, 2, 56, 56, 1, 256, float, false>(...)", True, "wtconv_bwd"),
+    ("void wtc::dev::k_tile_bwd<5, 3, 32, 32, 256, float>(...)", True, "wtconv_bwd"),
+    ("__amd_rocclr_copyBuffer", True, None),
+    ("void at::native::roll_cuda_kernel<float>(...)", True, None),
+])
+def test_kernels_map_to_their_entry_point(name, fused, call):
+    assert bench.call_of(name, fused) == call
+
+
+def test_step_marker_is_the_forward_main_kernel():
+    assert bench.is_step_marker("void wtc::dev::k_plane_apply<5, 2, 56, 56, 1, 256, float, false>(x)")
+    assert bench.is_step_marker("void wtc::dev::k_tile_apply<5, 3, 32, 64, 256, float, false>(x)")
+    assert not bench.is_step_marker("void wtc::dev::k_plane_apply<5, 2, 56, 56, 1, 256, float, true>(x)")
+    assert not bench.is_step_marker("void wtc::dev::k_deep_apply<float, 5, false>(x)")
+
+
+def test_flops_per_pixel():
+    # 2 k^2 for the base conv plus 4 subbands of 2 k^2 on grids 4^l smaller:
+    # 2 * 25 * (1 + 1 + 1/4) = 112.5 at k = 5, L = 2
+    assert bench.conv_flops_per_pixel(2, 5) == pytest.approx(112.5)
+    assert bench.conv_flops_per_pixel(1, 3) == pytest.approx(2 * 9 * 2)
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode != 0
+    assert "one GPU" in (r.stdout + r.stderr)

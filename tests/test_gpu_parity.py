@@ -143,6 +143,24 @@ def test_tiled_planes(k, L, H, W, dtype):
     assert_parity(d, dtype, "tiled k%d L%d %dx%d %s" % (k, L, H, W, dtype))
 
 
+@pytest.mark.parametrize("B,C,k,L,H,W,dtype", [
+    (16, 7, 5, 4, 128, 192, "f32"),
+    (32, 5, 5, 5, 96, 160, "f16"),
+])
+def test_tiled_ranges_span_images_and_channels(B, C, k, L, H, W, dtype):
+    # more tiles than resident workgroups: each workgroup of the forward and
+    # input gradient walks a range of tiles that runs past image and channel
+    # ends, and each workgroup of the backward walks several tiles and images
+    # of its channel
+    d = wi.make_inputs(B, C, H, W, L, k, dtype, seed=B * 100 + C)
+    g = torch.Generator().manual_seed(13)
+    td = d["x"].dtype
+    d["s_base"] = (1 + 0.5 * torch.randn(C, generator=g)).to(td)
+    d["s_wav"] = (0.3 + 0.5 * torch.randn(L, C, 4, generator=g)).to(td)
+    d["b_base"] = (0.5 * torch.randn(C, generator=g)).to(td)
+    assert_parity(d, dtype, "tile ranges B%d C%d k%d L%d %dx%d %s" % (B, C, k, L, H, W, dtype))
+
+
 ANY_SIZE = [  # k, L, H, W, dtype: sides the kernels do not take directly
     (5, 2, 55, 55, "f32"),    # zero-extended to 56 x 56 (whole planes)
     (5, 2, 27, 27, "f16"),    # to 28 x 28, fp16
