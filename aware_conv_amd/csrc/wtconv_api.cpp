@@ -243,8 +243,8 @@ int backward(const wtconv_shape* s, const void* x, const void* dy, const void* w
         err = fused ? wtc::plane_bwd(r, xr, dyr, p, dxr, g, workspace, st)
                     : wtc::plane_bwd_weight(r, xr, dyr, p, g, workspace, st);
     } else {
-        // tiles of large planes: both passes one after the other on the
-        // stream, sharing the box sums of dy
+        // tiles of large planes: one pass over x and dy for both gradients,
+        // or the weight taps alone
         err = fused ? wtc::tile_bwd(r, xr, dyr, p, dxr, g, workspace, st)
                     : wtc::tile_bwd_weight(r, xr, dyr, p, g, workspace, st);
     }
