@@ -260,6 +260,157 @@ __global__ __launch_bounds__(256) void k_deep_bww(const float* __restrict__ px,
     }
 }
 
+// Deep levels of planes whose box sums do not fit one workgroup's LDS: the
+// same arithmetic as k_deep_apply / k_deep_bww, staged through device memory
+// one level at a time (the box sums are 1/4^LT of the input, so these passes
+// are small next to the tiles).  Level m of every plane is one array
+// [plane][subband][h(m)][w(m)] of fp32.
+struct DeepGlobal {
+    int planes, hp, wp, LD;
+    __host__ __device__ int h(int m) const { return hp >> m; }
+    __host__ __device__ int w(int m) const { return wp >> m; }
+    __host__ __device__ size_t level_size(int m) const { return size_t(4) * planes * h(m) * w(m); }
+    __host__ __device__ size_t level_off(int m) const {  // floats, m = 1..LD + 1
+        size_t o = 0;
+        for (int k = 1; k < m; ++k) o += level_size(k);
+        return o;
+    }
+};
+
+// One unnormalised Haar level of every plane: the 2 x 2 blocks of the source
+// LL (plane stride `sps`, row pitch `sp`) into the four subbands of `dst`.
+__global__ __launch_bounds__(256) void k_gdeep_analysis(const float* __restrict__ src,
+                                                        size_t sps, int sp,
+                                                        float* __restrict__ dst, int planes,
+                                                        int h, int w) {
+    const size_t n = size_t(planes) * h * w, A = size_t(h) * w;
+    for (size_t e = size_t(blockIdx.x) * blockDim.x + threadIdx.x; e < n;
+         e += size_t(gridDim.x) * blockDim.x) {
+        const int j = int(e % w);
+        const size_t r = e / w;
+        const int i = int(r % h);
+        const size_t pl = r / h;
+        const float* s0 = src + pl * sps + size_t(2 * i) * sp + 2 * j;
+        const float a = s0[0], b = s0[1], c = s0[sp], d = s0[sp + 1];
+        const float x0 = a + b, d0 = a - b, x1 = c + d, d1 = c - d;
+        float* o = dst + pl * 4 * A + size_t(i) * w + j;
+        o[0] = x0 + x1;
+        o[A] = d0 + d1;
+        o[2 * A] = x0 - x1;
+        o[3 * A] = d0 - d1;
+    }
+}
+
+// Folded-filter conv of one (plane, subband) of absolute level `la` per
+// workgroup, 'same' zero padding, taps in the order of k_deep_apply.
+template <typename T, int K, bool FLIP>
+__global__ __launch_bounds__(256) void k_gdeep_conv(const float* __restrict__ U,
+                                                    float* __restrict__ out,
+                                                    const T* __restrict__ ww,
+                                                    const T* __restrict__ sw, int C, int h,
+                                                    int w, int la) {
+    constexpr int KK = K * K, p = K / 2;
+    __shared__ float wk[KK];
+    const int ps = blockIdx.x, s = ps % 4, c = (ps / 4) % C;
+    if (threadIdx.x < KK) {
+        const int t = threadIdx.x, tt = FLIP ? KK - 1 - t : t;
+        const size_t gi = (size_t(la - 1) * C + c) * 4 + s;
+        wk[t] = to_f(sw[gi]) * ldexpf(1.f, -2 * la) * to_f(ww[gi * KK + tt]);
+    }
+    __syncthreads();
+    const float* u = U + size_t(ps) * h * w;
+    float* o = out + size_t(ps) * h * w;
+    for (int e = threadIdx.x; e < h * w; e += blockDim.x) {
+        const int i = e / w, j = e % w;
+        float acc = 0.f;
+#pragma unroll
+        for (int uu = 0; uu < K; ++uu) {
+            const int y = i + uu - p;
+            if (y < 0 || y >= h) continue;
+#pragma unroll
+            for (int vv = 0; vv < K; ++vv) {
+                const int x = j + vv - p;
+                if (x >= 0 && x < w) acc = fmaf(wk[uu * K + vv], u[y * w + x], acc);
+            }
+        }
+        o[e] = acc;
+    }
+}
+
+// The conv outputs of one level synthesised one level down, with the signs
+// of k_deep_apply: added to the next finer LL (`accumulate`), or written as
+// the level-LT contribution D.
+__global__ __launch_bounds__(256) void k_gdeep_synth(const float* __restrict__ cm, int hc,
+                                                     int wc, float* __restrict__ dst,
+                                                     size_t dps, int dp, int planes,
+                                                     bool accumulate) {
+    const int h = 2 * hc, w = 2 * wc;
+    const size_t n = size_t(planes) * h * w, A = size_t(hc) * wc;
+    for (size_t e = size_t(blockIdx.x) * blockDim.x + threadIdx.x; e < n;
+         e += size_t(gridDim.x) * blockDim.x) {
+        const int j = int(e % w);
+        const size_t r = e / w;
+        const int i = int(r % h);
+        const size_t pl = r / h;
+        const float* cs = cm + pl * 4 * A + size_t(i >> 1) * wc + (j >> 1);
+        const float sy = (i & 1) ? -1.f : 1.f, sx = (j & 1) ? -1.f : 1.f;
+        const float e0 = fmaf(sy, cs[2 * A], cs[0]), f0 = fmaf(sy, cs[3 * A], cs[A]);
+        const float v = fmaf(sx, f0, e0);
+        float* d = dst + pl * dps + size_t(i) * dp + j;
+        *d = accumulate ? *d + v : v;
+    }
+}
+
+// Correlation taps of one (plane, level, subband) per workgroup: V (dy side)
+// against the shifted U (x side), each lane over a strided share of the
+// positions, then summed over the lanes in order into the plane's partial
+// row (row0 + b) * C + c.  The workgroup of the first subband of the first
+// level also zeroes the row's slots below the deep levels.
+template <int K>
+__global__ __launch_bounds__(256) void k_gdeep_corr(const float* __restrict__ ux,
+                                                    const float* __restrict__ vdy,
+                                                    DeepGlobal G, float* __restrict__ part,
+                                                    int C, int LT, int row0, int npart) {
+    constexpr int KK = K * K, p = K / 2, NT = 256;
+    __shared__ float red[NT * KK];
+    const int tid = threadIdx.x;
+    const int ms = blockIdx.x % (G.LD * 4), pl = blockIdx.x / (G.LD * 4);
+    const int m = ms / 4 + 1, s = ms % 4, h = G.h(m), w = G.w(m);
+    const size_t off = G.level_off(m) + (size_t(pl) * 4 + s) * h * w;
+    const float* u = ux + off;
+    const float* v = vdy + off;
+    float acc[KK];
+#pragma unroll
+    for (int t = 0; t < KK; ++t) acc[t] = 0.f;
+    for (int e = tid; e < h * w; e += NT) {
+        const int i = e / w, j = e % w;
+        const float dv = v[e];
+#pragma unroll
+        for (int uu = 0; uu < K; ++uu) {
+            const int y = i + uu - p;
+            if (y < 0 || y >= h) continue;
+#pragma unroll
+            for (int vv = 0; vv < K; ++vv) {
+                const int x = j + vv - p;
+                if (x >= 0 && x < w) acc[uu * K + vv] = fmaf(dv, u[y * w + x], acc[uu * K + vv]);
+            }
+        }
+    }
+#pragma unroll
+    for (int t = 0; t < KK; ++t) red[tid * KK + t] = acc[t];
+    __syncthreads();
+    const int b = pl / C, c = pl % C;
+    float* row = part + (size_t(row0 + b) * C + c) * npart;
+    const int first = KK + 1 + LT * 4 * KK;
+    for (int t = tid; t < KK; t += NT) {
+        float sum = 0.f;
+        for (int q = 0; q < NT; ++q) sum += red[q * KK + t];
+        row[first + ms * KK + t] = sum;
+    }
+    if (ms == 0)
+        for (int o = tid; o < first; o += NT) row[o] = 0.f;
+}
+
 }  // namespace dev
 
 namespace {
@@ -364,12 +515,13 @@ bool tile_supported(const wtconv_shape& s) {
     // buffer offsets within a plane are 32-bit
     if (size_t(s.H) * size_t(s.W) * (s.dtype == WTCONV_F32 ? 4 : 2) >= (size_t(1) << 31))
         return false;
-    if (s.L > tile_lt(s) && deep_bww_lds(s) > kMaxLds) return false;
     return true;
 }
 
 // Workspace: [partial rows | deep contribution D | box sums P of x | of dy]
-// (D and the box sums only with levels deeper than the tile's).
+// (D and the box sums only with levels deeper than the tile's), then, when
+// the deep levels run through device memory, [levels of x | of dy | conv
+// outputs].
 namespace {
 constexpr size_t kAlign = 256;
 size_t align_up(size_t n) { return (n + kAlign - 1) / kAlign * kAlign; }
@@ -391,6 +543,110 @@ float* d_of(const wtconv_shape& s, void* workspace) {
 float* p_of(const wtconv_shape& s, void* workspace, int which) {
     return reinterpret_cast<float*>(static_cast<char*>(workspace) + rows_bytes(s) +
                                     (1 + which) * align_up(p_bytes(s)));
+}
+
+// The deep levels stay in one workgroup's LDS when both deep kernels fit.
+bool deep_in_lds(const wtconv_shape& s) {
+    return deep_apply_lds(s) <= kMaxLds && deep_bww_lds(s) <= kMaxLds;
+}
+DeepGlobal deep_global(const wtconv_shape& s) {
+    const int LT = tile_lt(s);
+    return DeepGlobal{s.B * s.C, s.H >> LT, s.W >> LT, s.L - LT};
+}
+size_t g_bytes(const wtconv_shape& s) {
+    const DeepGlobal G = deep_global(s);
+    return align_up(G.level_off(G.LD + 1) * sizeof(float));
+}
+// 0: levels of P(x), 1: levels of P(dy), 2: conv outputs
+float* g_of(const wtconv_shape& s, void* workspace, int which) {
+    return reinterpret_cast<float*>(static_cast<char*>(workspace) + rows_bytes(s) +
+                                    3 * align_up(p_bytes(s)) + which * g_bytes(s));
+}
+unsigned grid_for(size_t n) {
+    const size_t g = (n + 255) / 256;
+    return unsigned(g < 65536 ? g : 65536);
+}
+
+// Levels 1..LD of the box sums P into A (device-memory deep path).
+hipError_t gdeep_analysis(const wtconv_shape& s, const float* P, float* A, hipStream_t stream) {
+    const DeepGlobal G = deep_global(s);
+    for (int m = 1; m <= G.LD; ++m) {
+        const float* src = m == 1 ? P : A + G.level_off(m - 1);
+        const size_t sps = m == 1 ? size_t(G.hp) * G.wp : size_t(4) * G.h(m - 1) * G.w(m - 1);
+        const int sp = m == 1 ? G.wp : G.w(m - 1);
+        const size_t n = size_t(G.planes) * G.h(m) * G.w(m);
+        hipLaunchKernelGGL(k_gdeep_analysis, dim3(grid_for(n)), dim3(256), 0, stream, src, sps,
+                           sp, A + G.level_off(m), G.planes, G.h(m), G.w(m));
+    }
+    return hipGetLastError();
+}
+
+template <typename T, int K>
+const void* gdeep_conv_fn_k(bool flip) {
+    return flip ? reinterpret_cast<const void*>(&k_gdeep_conv<T, K, true>)
+                : reinterpret_cast<const void*>(&k_gdeep_conv<T, K, false>);
+}
+template <typename T>
+const void* gdeep_conv_fn(bool flip, int k) {
+    switch (k) {
+        case 1: return gdeep_conv_fn_k<T, 1>(flip);
+        case 3: return gdeep_conv_fn_k<T, 3>(flip);
+        case 5: return gdeep_conv_fn_k<T, 5>(flip);
+        default: return gdeep_conv_fn_k<T, 7>(flip);
+    }
+}
+const void* gdeep_corr_fn(int k) {
+    switch (k) {
+        case 1: return reinterpret_cast<const void*>(&k_gdeep_corr<1>);
+        case 3: return reinterpret_cast<const void*>(&k_gdeep_corr<3>);
+        case 5: return reinterpret_cast<const void*>(&k_gdeep_corr<5>);
+        default: return reinterpret_cast<const void*>(&k_gdeep_corr<7>);
+    }
+}
+
+// D from the levels A of the box sums: the convs of every level into Cb,
+// each level folded into the LL below it, level 1 expanded over P's grid.
+hipError_t gdeep_apply(const wtconv_shape& s, const float* A, const Params& p, bool flip,
+                       float* Cb, float* deep, hipStream_t stream) {
+    const DeepGlobal G = deep_global(s);
+    const int LT = tile_lt(s);
+    const void* fn = s.dtype == WTCONV_F32 ? gdeep_conv_fn<float>(flip, s.k)
+                                           : gdeep_conv_fn<__half>(flip, s.k);
+    int C = s.C;
+    const void* ww = p.w_wav;
+    const void* sw = p.s_wav;
+    for (int m = 1; m <= G.LD; ++m) {
+        const float* u = A + G.level_off(m);
+        float* o = Cb + G.level_off(m);
+        int h = G.h(m), w = G.w(m), la = LT + m;
+        void* args[] = {&u, &o, &ww, &sw, &C, &h, &w, &la};
+        hipError_t e = hipLaunchKernel(fn, dim3(unsigned(G.planes) * 4u), dim3(256), args, 0,
+                                       stream);
+        if (e != hipSuccess) return e;
+    }
+    for (int m = G.LD; m >= 1; --m) {
+        const size_t n = size_t(G.planes) * G.h(m - 1) * G.w(m - 1);
+        float* dst = m > 1 ? Cb + G.level_off(m - 1) : deep;
+        const size_t dps =
+            m > 1 ? size_t(4) * G.h(m - 1) * G.w(m - 1) : size_t(G.hp) * G.wp;
+        hipLaunchKernelGGL(k_gdeep_synth, dim3(grid_for(n)), dim3(256), 0, stream,
+                           Cb + G.level_off(m), G.h(m), G.w(m), dst, dps, G.w(m - 1), G.planes,
+                           m > 1);
+    }
+    return hipGetLastError();
+}
+
+// Deep partial rows (row0 + b) from the levels of both box sums.
+hipError_t gdeep_rows(const wtconv_shape& s, const float* Ax, const float* Ady, float* part,
+                      int row0, hipStream_t stream) {
+    DeepGlobal G = deep_global(s);
+    int C = s.C, LT = tile_lt(s), npart = s.k * s.k * (1 + 4 * s.L) + 1;
+    void* args[] = {&Ax, &Ady, &G, &part, &C, &LT, &row0, &npart};
+    const hipError_t e = hipLaunchKernel(gdeep_corr_fn(s.k),
+                                         dim3(unsigned(G.planes) * unsigned(G.LD) * 4u),
+                                         dim3(256), args, 0, stream);
+    if (e != hipSuccess) return e;
+    return hipGetLastError();
 }
 
 hipError_t launch_box_sums(const wtconv_shape& s, const void* src, float* P,
@@ -422,6 +678,39 @@ hipError_t launch_deep_apply(const wtconv_shape& s, const float* P, const Params
     e = hipLaunchKernel(fn, dim3(unsigned(B) * unsigned(C)), dim3(256), args, lds, stream);
     if (e != hipSuccess) return e;
     return hipGetLastError();
+}
+
+// D from the box sums P on either deep path; on the device-memory path the
+// levels of P are left in A.
+hipError_t deep_contribution(const wtconv_shape& s, const float* P, const Params& p, bool flip,
+                             float* deep, float* A, float* Cb, hipStream_t stream) {
+    if (deep_in_lds(s)) return launch_deep_apply(s, P, p, flip, deep, stream);
+    const hipError_t e = gdeep_analysis(s, P, A, stream);
+    if (e != hipSuccess) return e;
+    return gdeep_apply(s, A, p, flip, Cb, deep, stream);
+}
+
+// Deep partial rows from the box sums of x and dy on either path; Ady holds
+// the levels of P(dy) already when `dy_levels`.
+hipError_t deep_rows(const wtconv_shape& s, const float* Px, const float* Pdy, float* part,
+                     int row0, void* workspace, bool dy_levels, hipStream_t stream) {
+    hipError_t e;
+    if (deep_in_lds(s)) {
+        int B = s.B, C = s.C, H = s.H, W = s.W, L = s.L, LTv = tile_lt(s);
+        int npart = s.k * s.k * (1 + 4 * s.L) + 1;
+        const void* fn = deep_bww_fn(s.k);
+        const size_t lds = deep_bww_lds(s);
+        if ((e = set_lds(fn, lds)) != hipSuccess) return e;
+        void* args[] = {&Px, &Pdy, &part, &B, &C, &H, &W, &L, &LTv, &row0, &npart};
+        e = hipLaunchKernel(fn, dim3(unsigned(B) * unsigned(C)), dim3(256), args, lds, stream);
+        if (e != hipSuccess) return e;
+        return hipGetLastError();
+    }
+    float* Ax = g_of(s, workspace, 0);
+    float* Ady = g_of(s, workspace, 1);
+    if ((e = gdeep_analysis(s, Px, Ax, stream)) != hipSuccess) return e;
+    if (!dy_levels && (e = gdeep_analysis(s, Pdy, Ady, stream)) != hipSuccess) return e;
+    return gdeep_rows(s, Ax, Ady, part, row0, stream);
 }
 
 // The tile kernels of the forward (flip = false) or input gradient, with the
@@ -461,7 +750,7 @@ hipError_t launch_weight_grads(const wtconv_shape& s, const TileVariant* v, cons
     const int nchunk = tile_chunks(s, resident(v->bww, v->NT, v->lds_bww));
     const int units = tile_units_per_channel(s);
     int upw = (units + nchunk - 1) / nchunk;
-    int B = s.B, C = s.C, H = s.H, W = s.W, L = s.L, LTv = LT;
+    int B = s.B, C = s.C, H = s.H, W = s.W;
     int npart = s.k * s.k * (1 + 4 * s.L) + 1;
     float* part = static_cast<float*>(workspace);
     {
@@ -472,13 +761,8 @@ hipError_t launch_weight_grads(const wtconv_shape& s, const TileVariant* v, cons
     }
     int rows = nchunk;
     if (s.L > LT) {
-        const void* fn = deep_bww_fn(s.k);
-        const size_t lds = deep_bww_lds(s);
-        if ((e = set_lds(fn, lds)) != hipSuccess) return e;
-        int row0 = nchunk;
-        void* args[] = {&Px, &Pdy, &part, &B, &C, &H, &W, &L, &LTv, &row0, &npart};
-        e = hipLaunchKernel(fn, dim3(unsigned(B) * unsigned(C)), dim3(256), args, lds, stream);
-        if (e != hipSuccess) return e;
+        if ((e = deep_rows(s, Px, Pdy, part, nchunk, workspace, false, stream)) != hipSuccess)
+            return e;
         rows += s.B;
     }
     return finalize_grads(s, part, rows, p, g, stream);
@@ -487,8 +771,8 @@ hipError_t launch_weight_grads(const wtconv_shape& s, const TileVariant* v, cons
 
 size_t tile_workspace_bytes(const wtconv_shape& s) {
     if (!tile_supported(s) || s.B == 0 || s.C == 0) return 0;
-    const int LT = tile_lt(s);
-    return rows_bytes(s) + (s.L > LT ? 3 * align_up(p_bytes(s)) : 0);
+    if (s.L <= tile_lt(s)) return rows_bytes(s);
+    return rows_bytes(s) + 3 * align_up(p_bytes(s)) + (deep_in_lds(s) ? 0 : 3 * g_bytes(s));
 }
 
 hipError_t tile_apply(const wtconv_shape& s, const void* in, const Params& p, void* out,
@@ -500,7 +784,9 @@ hipError_t tile_apply(const wtconv_shape& s, const void* in, const Params& p, vo
         deep = d_of(s, workspace);
         float* P = p_of(s, workspace, 0);
         hipError_t e = launch_box_sums(s, in, P, stream);
-        if (e == hipSuccess) e = launch_deep_apply(s, P, p, flip, deep, stream);
+        if (e == hipSuccess)
+            e = deep_contribution(s, P, p, flip, deep, g_of(s, workspace, 0),
+                                  g_of(s, workspace, 2), stream);
         if (e != hipSuccess) return e;
     }
     return launch_tiles(s, v, in, p, out, flip, deep, stream);
@@ -541,13 +827,15 @@ hipError_t tile_bwd(const wtconv_shape& s, const void* x, const void* dy, const 
         Px = p_of(s, workspace, 0);
         Pdy = p_of(s, workspace, 1);
         if ((e = launch_box_sums(s, dy, Pdy, stream)) != hipSuccess) return e;
-        if ((e = launch_deep_apply(s, Pdy, p, true, deep, stream)) != hipSuccess) return e;
+        if ((e = deep_contribution(s, Pdy, p, true, deep, g_of(s, workspace, 1),
+                                   g_of(s, workspace, 2), stream)) != hipSuccess)
+            return e;
     }
     if ((e = set_lds(v->bwd, v->lds_bwd)) != hipSuccess) return e;
     const int nchunk = tile_chunks(s, resident(v->bwd, v->NT, v->lds_bwd));
     const int units = tile_units_per_channel(s);
     int upw = (units + nchunk - 1) / nchunk;
-    int B = s.B, C = s.C, H = s.H, W = s.W, L = s.L, LTv = LT;
+    int B = s.B, C = s.C, H = s.H, W = s.W;
     int npart = s.k * s.k * (1 + 4 * s.L) + 1;
     float* part = static_cast<float*>(workspace);
     const void* wb = p.w_base;
@@ -565,14 +853,10 @@ hipError_t tile_bwd(const wtconv_shape& s, const void* x, const void* dy, const 
     }
     int rows = nchunk;
     if (s.L > LT) {
-        const void* fn = deep_bww_fn(s.k);
-        const size_t lds = deep_bww_lds(s);
-        if ((e = set_lds(fn, lds)) != hipSuccess) return e;
-        int row0 = nchunk;
-        void* args[] = {&Px, &Pdy, &part, &B, &C, &H, &W, &L, &LTv, &row0, &npart};
-        e = hipLaunchKernel(fn, dim3(unsigned(B) * unsigned(C)), dim3(256), args, lds, stream);
-        if (e == hipSuccess) e = hipGetLastError();
-        if (e != hipSuccess) return e;
+        // the levels of P(dy) are in the workspace already on the device-memory
+        // deep path (from the deep input gradient)
+        if ((e = deep_rows(s, Px, Pdy, part, nchunk, workspace, true, stream)) != hipSuccess)
+            return e;
         rows += s.B;
     }
     return finalize_grads(s, part, rows, p, g, stream);

@@ -81,7 +81,8 @@ typedef struct {
 #define WTCONV_ERR_ALIGN (-6)       /* activation/workspace pointer not 16-byte aligned,
                                        or parameter pointer not element aligned */
 #define WTCONV_ERR_WORKSPACE (-7)   /* ws_bytes below wtconv_workspace_size() */
-#define WTCONV_ERR_UNSUPPORTED (-8) /* valid shape this build has no kernel for */
+#define WTCONV_ERR_UNSUPPORTED (-8) /* valid shape this build has no kernel for
+                                       (a plane of 2^31 bytes or more) */
 #define WTCONV_ERR_ALIAS (-9)       /* an output overlaps an input */
 #define WTCONV_ERR_HIP (-100)       /* a kernel launch failed */
 
@@ -96,10 +97,11 @@ int wtconv_workspace_size(const wtconv_shape* s, size_t* bytes);
  * Forward: y = WTConv(x) as defined above (gist.science/pt, "Metodologia":
  * fused Haar analysis, closed-form synthesis, folded scales).  x and y are
  * [B][C][H][W]; y must not overlap x.  Planes too large for on-chip staging
- * with more than three levels use the workspace for the deeper levels'
- * contribution (1/64 of the input), and shapes run on zero-extended planes
- * keep those planes there; pass wtconv_workspace_size() bytes, or NULL when
- * it reported 0.
+ * with more than three levels use the workspace for the deeper levels (the
+ * 8 x 8 box sums of the input, their contribution, and for the largest
+ * planes their Haar levels: a few 1/64 of the input), and shapes run on
+ * zero-extended planes keep those planes there; pass wtconv_workspace_size()
+ * bytes, or NULL when it reported 0.
  */
 int wtconv_fwd(const wtconv_shape* s, const void* x, const void* w_base,
                const void* b_base, const void* s_base, const void* w_wav,

@@ -114,7 +114,7 @@ def test_bwd_weight_workspace_checks(lb):
 
 def test_workspace_size_queries(lb):
     n = ctypes.c_size_t(7)
-    huge = good(lb, H=8192, W=8192, L=4)  # deep levels too large for one workgroup
+    huge = good(lb, H=32768, W=32768, L=4)  # 4 GiB planes: beyond 32-bit plane offsets
     assert lb.lib.wtconv_workspace_size(ctypes.byref(huge), ctypes.byref(n)) == -8
     assert n.value == 7  # untouched on error
     assert lb.lib.wtconv_workspace_size(ctypes.byref(good(lb)), None) == -1
@@ -151,7 +151,7 @@ def test_fused_bwd_checks(lb):
     assert call(dx=FAKE2) == -9             # dx aliases dy
     assert call(shape=good(lb, k=2)) == -3
     far = [ctypes.c_void_p(n << 40) for n in (1, 2, 3)]  # 1 TiB apart: no overlap
-    assert call(shape=good(lb, H=8192, W=8192, L=4), x=far[0], dy=far[1], dx=far[2]) == -8
+    assert call(shape=good(lb, H=32768, W=32768, L=4), x=far[0], dy=far[1], dx=far[2]) == -8
 
 
 def test_dwconv_checks(lb):
@@ -176,3 +176,15 @@ def test_huge_channel_counts_leave_the_whole_plane_path(lb):
     # library still sizes a workspace (the tile path takes the shape)
     s = good(lb, B=1, C=1 << 22)
     assert lb.wtconv_workspace_size(s) > 0
+
+
+def test_large_planes_with_deep_levels_are_supported(lb):
+    # box sums too large for one workgroup's LDS: the deep levels run through
+    # device memory, which the workspace holds (three level sets of the box
+    # sums on top of the partial rows, D and both box sums)
+    for H, W, L, k in ((8192, 8192, 4, 5), (1024, 1024, 5, 5), (768, 768, 6, 7)):
+        s = good(lb, B=1, C=2, H=H, W=W, L=L, k=k)
+        p = 2 * (H >> 3) * (W >> 3) * 4  # bytes of one box-sum tensor
+        levels = 4 * p * (1 - 4.0 ** -(L - 3)) / 3  # levels 4..L of one box-sum tensor
+        assert lb.wtconv_workspace_size(s) >= 3 * p + 3 * levels
+

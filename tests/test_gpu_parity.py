@@ -161,6 +161,24 @@ def test_tiled_ranges_span_images_and_channels(B, C, k, L, H, W, dtype):
     assert_parity(d, dtype, "tile ranges B%d C%d k%d L%d %dx%d %s" % (B, C, k, L, H, W, dtype))
 
 
+@pytest.mark.parametrize("B,C,k,L,H,W,dtype", [
+    (2, 3, 5, 5, 1024, 1024, "f32"),
+    (1, 2, 7, 6, 768, 768, "f16"),
+    (3, 2, 3, 4, 512, 1536, "f32"),
+    (2, 2, 1, 4, 832, 832, "f32"),
+])
+def test_deep_levels_through_device_memory(B, C, k, L, H, W, dtype):
+    # box sums too large for one workgroup's LDS: the deep levels run level by
+    # level through the workspace (analysis, convs, synthesis, correlations)
+    d = wi.make_inputs(B, C, H, W, L, k, dtype, seed=H + W + L)
+    g = torch.Generator().manual_seed(17)
+    td = d["x"].dtype
+    d["s_base"] = (1 + 0.5 * torch.randn(C, generator=g)).to(td)
+    d["s_wav"] = (0.3 + 0.5 * torch.randn(L, C, 4, generator=g)).to(td)
+    d["b_base"] = (0.5 * torch.randn(C, generator=g)).to(td)
+    assert_parity(d, dtype, "deep in memory B%d C%d k%d L%d %dx%d %s" % (B, C, k, L, H, W, dtype))
+
+
 ANY_SIZE = [  # k, L, H, W, dtype: sides the kernels do not take directly
     (5, 2, 55, 55, "f32"),    # zero-extended to 56 x 56 (whole planes)
     (5, 2, 27, 27, "f16"),    # to 28 x 28, fp16
