@@ -73,6 +73,16 @@ def make_inputs(B, C, H, W, L, k, dtype="f32", seed=0, s_base=1.0,
     return {n: t.to(td).contiguous().to(device) for n, t in out.items()}
 
 
+def make_device_activations(B, C, H, W, seed, device="cuda"):
+    """x and dy ~ N(0,1) in fp32, drawn on `device` with a generator of its
+    own seeded with `seed` (for tensors too large to draw on the host)."""
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    x = torch.randn((B, C, H, W), generator=g, device=device)
+    dy = torch.randn((B, C, H, W), generator=g, device=device)
+    return x, dy
+
+
 def workload_inputs(wl, seed=0, device="cpu", batch=None):
     """Inputs for a named workload; ``batch`` truncates B (same draws)."""
     d = make_inputs(wl.B, wl.C, wl.H, wl.W, wl.L, wl.k, wl.dtype, seed,
