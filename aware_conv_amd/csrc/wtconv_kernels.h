@@ -1388,9 +1388,20 @@ __global__ __launch_bounds__(256) void k_bww_final(
     const T* __restrict__ wb, const T* __restrict__ bb, const T* __restrict__ sb,
     const T* __restrict__ ww, const T* __restrict__ sw, T* __restrict__ dwb,
     T* __restrict__ dbb, T* __restrict__ dsb, T* __restrict__ dww, T* __restrict__ dsw) {
-    extern __shared__ float g[];
+    extern __shared__ float g[];  // [NPART] summed rows, then Kb [KK] and K [4 L KK]
     const int KK = K * K, NPART = KK + 1 + 4 * L * KK;
     const int c = blockIdx.x, tid = threadIdx.x, nt = blockDim.x;
+    float* kf = g + NPART;
+    // the filters go to LDS alongside the row sums, so the products below
+    // wait on no further device-memory round trip
+    for (int i = tid; i < KK + 4 * L * KK; i += nt) {
+        if (i < KK) {
+            kf[i] = to_f(wb[size_t(c) * KK + i]);
+        } else {
+            const int j = i - KK, ls = j / KK, t = j % KK, l = ls >> 2, s = ls & 3;
+            kf[i] = to_f(ww[((size_t(l) * C + c) * 4 + s) * KK + t]);
+        }
+    }
     const bool lin = rows.nwg > 0;
     const int nrow = lin ? rows.count(c) : nchunk;
     const size_t base = lin ? size_t(c) * rows.rmax : size_t(c);
@@ -1415,7 +1426,7 @@ __global__ __launch_bounds__(256) void k_bww_final(
         dbb[c] = from_f<T>(beta * g[KK]);
         if (dsb) {
             float dot = 0.f;
-            for (int t = 0; t < KK; ++t) dot = fmaf(to_f(wb[size_t(c) * KK + t]), g[t], dot);
+            for (int t = 0; t < KK; ++t) dot = fmaf(kf[t], g[t], dot);
             dsb[c] = from_f<T>(fmaf(to_f(bb[c]), g[KK], dot));
         }
     }
@@ -1428,7 +1439,7 @@ __global__ __launch_bounds__(256) void k_bww_final(
         const int l = i >> 2, s = i & 3;
         const size_t gi = (size_t(l) * C + c) * 4 + s;
         float dot = 0.f;
-        for (int t = 0; t < KK; ++t) dot = fmaf(to_f(ww[gi * KK + t]), g[KK + 1 + i * KK + t], dot);
+        for (int t = 0; t < KK; ++t) dot = fmaf(kf[KK + i * KK + t], g[KK + 1 + i * KK + t], dot);
         dsw[gi] = from_f<T>(ldexpf(1.f, -2 * (l + 1)) * dot);
     }
 }

@@ -119,7 +119,7 @@ hipError_t launch_final(const wtconv_shape& s, const float* part, int nchunk,
                         const LinearRows& rows, const Params& p, const Grads& g,
                         hipStream_t stream) {
     const int KK = s.k * s.k;
-    const size_t lds = sizeof(float) * (size_t(KK) + 1 + size_t(4) * s.L * KK);
+    const size_t lds = sizeof(float) * (size_t(2) * KK + 1 + size_t(8) * s.L * KK);
     hipLaunchKernelGGL(k_bww_final<T>, dim3(s.C), dim3(256), lds, stream, part, nchunk, rows, s.C,
                        s.k, s.L, (const T*)p.w_base, (const T*)p.b_base, (const T*)p.s_base,
                        (const T*)p.w_wav, (const T*)p.s_wav, (T*)g.dw_base, (T*)g.db_base,
