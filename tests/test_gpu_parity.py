@@ -189,6 +189,9 @@ ANY_SIZE = [  # k, L, H, W, dtype: sides the kernels do not take directly
     (5, 5, 100, 90, "f32"),   # to 128 x 96, tiles plus two deep levels
     (3, 2, 9, 7, "f16"),      # to 12 x 8, fp16 tiles
     (1, 1, 5, 3, "f32"),
+    (3, 1, 1, 1, "f32"),      # one pixel: a single 1 x 1 coefficient per subband
+    (5, 2, 1, 7, "f16"),      # one row: every level's grid one row high
+    (7, 3, 3, 2, "f32"),      # a plane smaller than the kernel at every level
 ]
 
 
