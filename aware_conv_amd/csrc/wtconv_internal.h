@@ -59,8 +59,9 @@ hipError_t tile_apply(const wtconv_shape& s, const void* in, const Params& p, vo
 hipError_t tile_bwd_weight(const wtconv_shape& s, const void* x, const void* dy,
                            const Params& p, const Grads& g, void* workspace,
                            hipStream_t stream);
-// Both gradients: the weight gradient, then the input gradient (the box sums
-// of dy computed for the first serve the deep levels of the second).
+// Both gradients from one pass over the tiles of x and dy (with deeper
+// levels: their input gradient from the box sums of dy before the pass,
+// their weight taps after it).
 hipError_t tile_bwd(const wtconv_shape& s, const void* x, const void* dy, const Params& p,
                     void* dx, const Grads& g, void* workspace, hipStream_t stream);
 

@@ -1708,7 +1708,8 @@ namespace dev {
 // Fused backward of a large plane's tiles: the input gradient of the base
 // conv and levels 1..LT (plus the deep levels' contribution `deep`, NULL if
 // none) and the weight-gradient partials of those levels, reading x and dy
-// once; with `px` (NULL: none) also the box sums U^LT_LL(x) of the planes.  (channel, chunk) workgroups as in k_tile_bww.  dy and x are analysed
+// once; with `px` (NULL: none) also the box sums U^LT_LL(x) of the planes.
+// (channel, chunk) workgroups as in k_tile_bww.  dy and x are analysed
 // side by side, both with the tile's halos; each lane runs the
 // rotated-filter conv on its dy window, keeps the window's centre, masked to
 // its part of the core, and correlates it with its x window.  Two

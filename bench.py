@@ -63,11 +63,16 @@ def io_model_reference(L):
 
 
 def source_hash():
+    """Hash of the kernel sources' code: comments and blank lines are left
+    out, so that a comment edit does not mark the counters stale."""
+    import re
     h = hashlib.sha256()
     for name in sorted(os.listdir(KERNEL_SOURCES)):
         if name.endswith((".hip", ".h", ".cpp")):
-            with open(os.path.join(KERNEL_SOURCES, name), "rb") as f:
-                h.update(name.encode() + b"\0" + f.read())
+            with open(os.path.join(KERNEL_SOURCES, name)) as f:
+                text = re.sub(r"/\*.*?\*/", "", f.read(), flags=re.S)
+            code = [ln.split("//")[0].strip() for ln in text.splitlines()]
+            h.update(name.encode() + b"\0" + "\n".join(c for c in code if c).encode())
     return h.hexdigest()[:16]
 
 

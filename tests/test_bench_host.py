@@ -48,3 +48,14 @@ def test_more_than_one_gpu_is_refused():
                        capture_output=True, text=True, timeout=120)
     assert r.returncode != 0
     assert "one GPU" in (r.stdout + r.stderr)
+
+
+def test_source_hash_ignores_comments(tmp_path, monkeypatch):
+    src = tmp_path / "k.hip"
+    src.write_text("// a kernel\n__global__ void k(float* p) { p[0] = 1.f; }  // one\n")
+    monkeypatch.setattr(bench, "KERNEL_SOURCES", str(tmp_path))
+    h0 = bench.source_hash()
+    src.write_text("/* reworded\n   comment */\n\n__global__ void k(float* p) { p[0] = 1.f; }\n")
+    assert bench.source_hash() == h0
+    src.write_text("__global__ void k(float* p) { p[0] = 2.f; }\n")
+    assert bench.source_hash() != h0
