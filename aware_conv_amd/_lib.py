@@ -96,6 +96,60 @@ def _ptr(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
 
+def _layer_dims(x, w_wav):
+    """(B, C, H, W, L, k) from the activation and the wavelet filters."""
+    if x.dim() != 4:
+        raise ValueError("activations must be 4-D [B, C, H, W], got shape %s" % (tuple(x.shape),))
+    if w_wav.dim() != 5 or w_wav.shape[2] != 4 or w_wav.shape[3] != w_wav.shape[4]:
+        raise ValueError("w_wav must be [L, C, 4, k, k], got shape %s" % (tuple(w_wav.shape),))
+    B, C, H, W = x.shape
+    return B, C, H, W, w_wav.shape[0], w_wav.shape[-1]
+
+
+def _expect(dtype, tensors):
+    """Every (name, tensor, shape) of `tensors` (tensor None: skipped; the
+    library reports a missing pointer): of that shape, of `dtype` (None: any)
+    and contiguous.  The library sees only pointers and sizes, so a tensor of
+    another shape would be read out of its bounds."""
+    for name, t, shape in tensors:
+        if t is None:
+            continue
+        if not isinstance(t, torch.Tensor):
+            raise TypeError("%s must be a torch.Tensor" % name)
+        if shape is not None and tuple(t.shape) != tuple(shape):
+            raise ValueError("%s has shape %s, expected %s" % (name, tuple(t.shape), tuple(shape)))
+        if dtype is not None and t.dtype != dtype:
+            raise TypeError("%s has dtype %s, expected %s" % (name, t.dtype, dtype))
+        if not t.is_contiguous():
+            raise ValueError("%s must be contiguous" % name)
+
+
+def _on_gpu(x, tensors):
+    """x on a GPU and every other tensor on the same one (checked after the
+    shapes, which do not depend on the device)."""
+    if x.device.type != "cuda":
+        raise ValueError("x is on %s; every tensor must be on a GPU" % x.device)
+    for name, t in tensors:
+        if t is not None and t.device != x.device:
+            raise ValueError("%s is on %s; every tensor must be on %s" % (name, t.device, x.device))
+
+
+def _param_specs(C, L, k, w_base, b_base, s_base, w_wav, s_wav):
+    return [("w_base", w_base, (C, 1, k, k)), ("b_base", b_base, (C,)),
+            ("s_base", s_base, (C,)), ("w_wav", w_wav, (L, C, 4, k, k)),
+            ("s_wav", s_wav, (L, C, 4))]
+
+
+def _check_call(x, w_wav, acts, params, workspace):
+    """Shared checks: the activations `acts` ([B, C, H, W] each), the
+    parameters, and the workspace (any dtype)."""
+    B, C, H, W, L, k = _layer_dims(x, w_wav)
+    specs = [(n, t, (B, C, H, W)) for n, t in acts] + _param_specs(C, L, k, *params)
+    _expect(x.dtype, specs)
+    _expect(None, [("workspace", workspace, None)])
+    _on_gpu(x, [(n, t) for n, t, _ in specs] + [("workspace", workspace)])
+
+
 def _stream(stream, device):
     if stream is None:
         stream = torch.cuda.current_stream(device)
@@ -124,6 +178,8 @@ def _workspace(shape, device, workspace):
 def wtconv_fwd(x, w_base, b_base, s_base, w_wav, s_wav, y=None,
                workspace=None, stream=None):
     """y = WTConv(x) on x's device; returns y."""
+    _check_call(x, w_wav, [("x", x), ("y", y)], (w_base, b_base, s_base, w_wav, s_wav),
+                workspace)
     s = shape_of(x, w_wav)
     if y is None:
         y = torch.empty_like(x)
@@ -137,6 +193,8 @@ def wtconv_fwd(x, w_base, b_base, s_base, w_wav, s_wav, y=None,
 def wtconv_bwd_input(dy, w_base, s_base, w_wav, s_wav, dx=None,
                      workspace=None, stream=None):
     """dx = transpose of the layer applied to dy; returns dx."""
+    _check_call(dy, w_wav, [("dy", dy), ("dx", dx)], (w_base, None, s_base, w_wav, s_wav),
+                workspace)
     s = shape_of(dy, w_wav)
     if dx is None:
         dx = torch.empty_like(dy)
@@ -157,9 +215,30 @@ def _grads(w_base, b_base, s_base, w_wav, s_wav):
             "ds_wav": torch.empty_like(s_wav)}
 
 
+def _check_grads(x, w_wav, grads):
+    if grads is None:
+        return
+    B, C, H, W, L, k = _layer_dims(x, w_wav)
+    missing = [n for n in GRAD_NAMES if n not in grads]
+    if missing:
+        raise KeyError("grads lacks %s" % ", ".join(missing))
+    specs = [("grads[%s]" % g, t, sh) for g, (_, t, sh) in
+             zip(GRAD_NAMES, _param_specs(C, L, k, *[grads[n] for n in GRAD_NAMES]))]
+    _expect(x.dtype, specs)
+
+
+def _grads_on_gpu(x, grads):
+    if grads is not None:
+        _on_gpu(x, [("grads[%s]" % n, grads[n]) for n in GRAD_NAMES])
+
+
 def wtconv_bwd_weight(x, dy, w_base, b_base, s_base, w_wav, s_wav, grads=None,
                       workspace=None, stream=None):
     """Parameter gradients; returns a dict keyed by GRAD_NAMES."""
+    _check_grads(x, w_wav, grads)
+    _check_call(x, w_wav, [("x", x), ("dy", dy)], (w_base, b_base, s_base, w_wav, s_wav),
+                workspace)
+    _grads_on_gpu(x, grads)
     s = shape_of(x, w_wav)
     if grads is None:
         grads = _grads(w_base, b_base, s_base, w_wav, s_wav)
@@ -174,6 +253,10 @@ def wtconv_bwd_weight(x, dy, w_base, b_base, s_base, w_wav, s_wav, grads=None,
 def wtconv_bwd(x, dy, w_base, b_base, s_base, w_wav, s_wav, dx=None, grads=None,
                workspace=None, stream=None):
     """Input and parameter gradients in one call; returns (dx, grads dict)."""
+    _check_grads(x, w_wav, grads)
+    _check_call(x, w_wav, [("x", x), ("dy", dy), ("dx", dx)],
+                (w_base, b_base, s_base, w_wav, s_wav), workspace)
+    _grads_on_gpu(x, grads)
     s = shape_of(x, w_wav)
     if dx is None:
         dx = torch.empty_like(dy)
@@ -196,6 +279,19 @@ def dw_shape_of(x, w):
     return DwShape(int(B), int(C), int(H), int(W), int(w.shape[-1]), _dtype_code(x.dtype))
 
 
+def _check_dw(x, w, acts, others):
+    if x.dim() != 4:
+        raise ValueError("activations must be 4-D [B, C, H, W], got shape %s" % (tuple(x.shape),))
+    if w.dim() != 4 or w.shape[1] != 1 or w.shape[2] != w.shape[3]:
+        raise ValueError("w must be [C, 1, k, k], got shape %s" % (tuple(w.shape),))
+    B, C, H, W = x.shape
+    k = w.shape[-1]
+    specs = ([(n, t, (B, C, H, W)) for n, t in acts] + [("w", w, (C, 1, k, k))] +
+             [(n, t, (C, 1, k, k) if n == "dw" else (C,)) for n, t in others])
+    _expect(x.dtype, specs)
+    _on_gpu(x, [(n, t) for n, t, _ in specs])
+
+
 def dwconv_workspace_size(shape):
     n = ctypes.c_size_t(0)
     _check(lib.dwconv_workspace_size(ctypes.byref(shape), ctypes.byref(n)),
@@ -205,6 +301,7 @@ def dwconv_workspace_size(shape):
 
 def dwconv_fwd(x, w, bias, y=None, stream=None):
     """y = depthwise conv of x with w [C, 1, k, k] plus bias [C]; returns y."""
+    _check_dw(x, w, [("x", x), ("y", y)], [("bias", bias)])
     s = dw_shape_of(x, w)
     if y is None:
         y = torch.empty_like(x)
@@ -215,6 +312,9 @@ def dwconv_fwd(x, w, bias, y=None, stream=None):
 
 def dwconv_bwd(x, dy, w, dx=None, dw=None, db=None, workspace=None, stream=None):
     """(dx, dw, db) of the depthwise conv in one pass."""
+    _check_dw(x, w, [("x", x), ("dy", dy), ("dx", dx)], [("dw", dw), ("db", db)])
+    _expect(None, [("workspace", workspace, None)])
+    _on_gpu(x, [("workspace", workspace)])
     s = dw_shape_of(x, w)
     dx = torch.empty_like(dy) if dx is None else dx
     dw = torch.empty_like(w) if dw is None else dw
