@@ -15,7 +15,8 @@
  * Tensors (contiguous, row-major, device memory, element type `dtype`):
  *   x, y, dy, dx : [B][C][H][W]      w, dw : [C][1][k][k]      bias, db : [C]
  * Arithmetic, ownership, threading and error codes are those of wtconv.h:
- * fp32 accumulation, one rounding per output; the caller owns every buffer;
+ * fp32 accumulation, one rounding per output; the caller owns every buffer,
+ * each of at least the elements its shape implies (pointers only are seen);
  * calls only enqueue on `stream`; every check happens before anything is
  * enqueued.  Shapes without a kernel in this build (the ConvNeXt-T stage
  * shapes at k = 7 are built) return WTCONV_ERR_UNSUPPORTED.

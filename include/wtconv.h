@@ -40,6 +40,10 @@
  *   w_wav        : [L][C][4][k][k]    s_wav          : [L][C][4]
  *   subband order (LL, LH, HL, HH).
  *
+ * The library sees pointers only: each must address at least the elements
+ * its shape implies, on the current HIP device; a shorter buffer, or host
+ * memory, is read or written out of bounds on the GPU.
+ *
  * Arithmetic: loads are widened to fp32, every sum is accumulated in fp32 and
  * each output is rounded once (round-to-nearest-even) to `dtype`.
  *
