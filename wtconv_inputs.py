@@ -39,7 +39,8 @@ class Workload:
 
 
 # Named workloads: tiny correctness case, ConvNeXt-T stage shapes, the fp16
-# stage-1 shape and a high-resolution deep cascade.
+# stage-1 shape, a high-resolution deep cascade, and the same at 1024^2 (whose
+# deepest levels no longer fit one workgroup's LDS).
 WORKLOADS = {
     "tiny": Workload("tiny", 1, 8, 32, 32, 2, 5, "f32"),
     "stage1": Workload("stage1", 64, 96, 56, 56, 2, 5, "f32"),
@@ -47,6 +48,7 @@ WORKLOADS = {
     "stage3": Workload("stage3", 64, 384, 14, 14, 1, 5, "f32"),
     "stage1_f16": Workload("stage1_f16", 128, 96, 56, 56, 2, 5, "f16"),
     "highres": Workload("highres", 8, 64, 512, 512, 5, 5, "f32"),
+    "highres1024": Workload("highres1024", 8, 64, 1024, 1024, 5, 5, "f32"),
 }
 
 
