@@ -521,36 +521,9 @@ struct Fetch {
     using raw_t = typename RawVec<V * int(sizeof(T))>::type;
     raw_t r[IT][ROWS];
 
-    // Issue the loads of planes b0..b0+P-1 (zeros past B).  In tile mode the
-    // footprint starts at (y0 - ah(0), x0 - ah(0)) of an Hp x Wp plane and
-    // items outside the plane read as zeros (Hp, Wp, y0, x0 multiples of 4).
-    __device__ __forceinline__ void issue(const T* __restrict__ src, int b0, int B, int C,
-                                          int c, int tid, int y0 = 0, int x0 = 0,
-                                          int Hp = G::H, int Wp = G::W) {
-#pragma unroll
-        for (int it = 0; it < IT; ++it) {
-            const int item = tid + it * G::NT;
-            const int cv = item % NV;
-            const int rb = (item / NV) % RB;
-            const int pl = item / (NV * RB);
-            const int b = b0 + pl;
-            const int yy = y0 - A0 + ROWS * rb, xx = x0 - A0 + cv * V;
-            bool in = (ITEMS % G::NT == 0 || item < ITEMS) && b < B;
-            if constexpr (G::HT > 0) in = in && yy >= 0 && yy < Hp && xx >= 0 && xx < Wp;
-            if (in) {
-                const raw_t* s = reinterpret_cast<const raw_t*>(
-                    src + ((size_t(b) * C + c) * Hp + yy) * Wp + xx);
-#pragma unroll
-                for (int k = 0; k < ROWS; ++k) r[it][k] = s[k * (Wp / V)];
-            } else {
-#pragma unroll
-                for (int k = 0; k < ROWS; ++k) r[it][k] = raw_t{};
-            }
-        }
-    }
-
-    // Whole planes: the same loads through a buffer resource, with no
-    // branch (items past ITEMS and planes past B read zeros).
+    // Whole planes: the loads of planes b0..b0+P-1 through a buffer
+    // resource, with no branch (items past ITEMS and planes past B read
+    // zeros).
     __device__ __forceinline__ void issue_buf(const T* __restrict__ src, int b0, int B, int C,
                                               int c, int tid) {
         static_assert(G::HT == 0, "whole planes only");
@@ -1121,8 +1094,10 @@ __global__ __launch_bounds__(NT) void k_plane_bww(
     const int g0 = chunk * gpw;
     const int g1 = min(g0 + gpw, ngroups);
     Fetch<G, T> fx, fd;
-    fx.issue(x, g0 * P, B, C, c, tid);
-    fd.issue(dy, g0 * P, B, C, c, tid);
+    if (g0 < g1) {
+        fx.issue_buf(x, g0 * P, B, C, c, tid);
+        fd.issue_buf(dy, g0 * P, B, C, c, tid);
+    }
     for (int i = tid; i < G::side + G::vside; i += NT) lds[i] = 0.f;
     __syncthreads();
 
@@ -1154,8 +1129,8 @@ __global__ __launch_bounds__(NT) void k_plane_bww(
         fx.template commit<true, false>(lds, tid);
         fd.template commit<false, true>(lds, tid);
         if (g + 1 < g1) {
-            fx.issue(x, b0 + P, B, C, c, tid);
-            fd.issue(dy, b0 + P, B, C, c, tid);
+            fx.issue_buf(x, b0 + P, B, C, c, tid);
+            fd.issue_buf(dy, b0 + P, B, C, c, tid);
         }
         __syncthreads();
         static_for<Fetch<G, T>::LEVELS + 1, L + 1>([&](auto lc) {
