@@ -1229,8 +1229,13 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void k_
     using F = Fetch<G, T>;
     constexpr int KK = G::KK, Q = G::Q, R = G::R, DY = bwd_dy_base<G>();
     extern __shared__ float lds[];
-    float* ldy = lds + DY;
-    float* wf = ldy + G::side;
+    // The dy side starts DY floats in: as a compile-time constant that
+    // offset does not fit the 8-bit offsets of paired LDS reads and costs an
+    // address add per pair; held in a register, each row needs one base.
+    int dyo = DY;
+    asm volatile("" : "+s"(dyo));
+    float* ldy = lds + dyo;
+    float* wf = lds + DY + G::side;
     const int tid = threadIdx.x;
     const int ngroups = cdiv(B, P);
     const long q0 = rows.q0(blockIdx.x);
@@ -1255,7 +1260,6 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void k_
     const int ncols = min(R, wcols - job.strip * R);
     const bool full = nrows == Q && ncols == R;
     const int dst = win + G::p * pitch + G::p;
-    float w[KK];
     float gacc[KK];
     float sdy = 0.f;
     int cur = -1;
@@ -1263,8 +1267,6 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void k_
         // one channel for the whole range: fold once, before the loop
         fold_weights<G, T, true>(wf, wb, wb, sb, ww, sw, C, c, tid);
         __syncthreads();
-#pragma unroll
-        for (int t = 0; t < KK; ++t) w[t] = wf[wsrc + t];
 #pragma unroll
         for (int t = 0; t < KK; ++t) gacc[t] = 0.f;
         cur = c;
@@ -1287,8 +1289,6 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void k_
             fold_weights<G, T, true>(wf, wb, wb, sb, ww, sw, C, c, tid);
             __syncthreads();
 #pragma unroll
-            for (int t = 0; t < KK; ++t) w[t] = wf[wsrc + t];
-#pragma unroll
             for (int t = 0; t < KK; ++t) gacc[t] = 0.f;
             sdy = 0.f;
             cur = c;
@@ -1303,16 +1303,31 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void k_
         });
         float acc[Q][R];
         if (job.on) {
-            // outside the level's core both windows read zeros, so the
-            // centre of a partial tile needs no mask
+            // The tile's own dy values (V^l_s at level l), read from the
+            // core of its array: outside a level's core the arrays hold
+            // zeros, so a partial tile needs no mask.  The weight taps come
+            // first and the rotated-filter conv second, with the filters read
+            // from LDS just before it (the empty asm keeps those reads and
+            // the dy window's after the correlation): neither the filters nor
+            // the conv sums are live beside the correlation's accumulators.
             float d[Q][R];
-            conv_tile<K, Q, R, true>(ldy + win, pitch, w, 0.f, acc, d);
+#pragma unroll
+            for (int qq = 0; qq < Q; ++qq)
+#pragma unroll
+                for (int j = 0; j < R; ++j) d[qq][j] = ldy[dst + qq * pitch + j];
             if (job.lvl == 0)
 #pragma unroll
                 for (int qq = 0; qq < Q; ++qq)
 #pragma unroll
                     for (int j = 0; j < R; ++j) sdy += d[qq][j];
             corr_tile<K, Q, R>(d, lds + win, pitch, gacc);
+            int wo = wsrc, yw = win;
+            asm volatile("" : "+v"(wo));
+            asm volatile("" : "+v"(yw));
+            float w[KK];
+#pragma unroll
+            for (int t = 0; t < KK; ++t) w[t] = wf[wo + t];
+            conv_tile<K, Q, R>(ldy + yw, pitch, w, 0.f, acc);
         }
         const bool wrap = grp + 1 == ngroups;
         const int cn = wrap ? c + 1 : c, gn = wrap ? 0 : grp + 1;
