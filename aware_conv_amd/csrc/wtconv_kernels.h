@@ -1716,7 +1716,11 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(K >= 7 ? 1 :
     using F = Fetch<G, T, true>;
     constexpr int KK = G::KK, Q = G::Q, R = G::R, DY = bwd_dy_base<G>();
     extern __shared__ float lds[];
-    float* ldy = lds + DY;
+    // the dy side's offset in a register: one base per window row instead of
+    // an address add per paired LDS read
+    int dyo = DY;
+    asm volatile("" : "+s"(dyo));
+    float* ldy = lds + dyo;
     const int tid = threadIdx.x;
     const int c = blockIdx.x % C;
     const int chunk = blockIdx.x / C;
@@ -1770,21 +1774,29 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(K >= 7 ? 1 :
         if (deep) fetch_deep<G>(dr, deep, b, C, c, y0, x0, Hp, Wp, tid);
         float acc[Q][R];
         if (job.on) {
+            // the tile's own dy values: past the job's part of the core the
+            // arrays hold halo (real neighbours), so they are masked; the
+            // core past the plane's edge reads zeros.  Taps first, then the
+            // rotated-filter conv of the dy window (kept after the
+            // correlation by the empty asm, so that its rows are not live
+            // beside the tap accumulators).
             float d[Q][R];
-            conv_tile<K, Q, R, true>(ldy + win, pitch, w, 0.f, acc, d);
-            // the centre past the job's part of the core is halo (real
-            // neighbours), and the core past the plane's edge reads zeros
 #pragma unroll
             for (int qq = 0; qq < Q; ++qq)
 #pragma unroll
-                for (int j = 0; j < R; ++j)
-                    if (!full && !(qq < nrows && j < ncols)) d[qq][j] = 0.f;
+                for (int j = 0; j < R; ++j) {
+                    const float v = ldy[dst + qq * pitch + j];
+                    d[qq][j] = (full || (qq < nrows && j < ncols)) ? v : 0.f;
+                }
             if (job.lvl == 0)
 #pragma unroll
                 for (int qq = 0; qq < Q; ++qq)
 #pragma unroll
                     for (int j = 0; j < R; ++j) sdy += d[qq][j];
             corr_tile<K, Q, R>(d, lds + win, pitch, gacc);
+            int yw = win;
+            asm volatile("" : "+v"(yw));
+            conv_tile<K, Q, R>(ldy + yw, pitch, w, 0.f, acc);
         }
         if (px) {
             // the core of U^LT_LL(x): the tile's share of the box sums that
