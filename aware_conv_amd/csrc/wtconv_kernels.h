@@ -949,11 +949,15 @@ constexpr size_t bww_lds_bytes() {
 // resources with no branch, so the only wait before a group's input is used
 // is for that input.
 // Register budget of the forward: the waves per SIMD the LDS footprint
-// allows, at most 4 (3 for fp16, whose 8-wide rows need more registers).
+// allows, at most 3.  Shapes that fit 128 VGPRs keep four waves anyway; the
+// ones that do not (the 56 x 56 stage shape among them) would spill at four,
+// and each spilled register is a scratch store per thread of every
+// workgroup, HBM writes beside the output, for no speed (the forward is
+// bound by its instruction count, not by its occupancy).
 template <int K, int L, int H, int W, int P, int NT, typename T>
 constexpr int apply_waves() {
     const int w = waves_for_lds(apply_lds_bytes<Geo<K, L, H, W, P, NT>>(), NT);
-    const int cap = sizeof(T) == 2 ? 3 : 4;
+    constexpr int cap = 3;
     return w < cap ? w : cap;
 }
 
