@@ -770,6 +770,67 @@ __device__ __forceinline__ void corr_tile(const float (&d)[Q][R], const float* s
     }
 }
 
+// One pass over a tile's window serving two sums: the conv
+// acc[q][j] = sum_{u,v} w[u*K+v] * src[(q+u)*pitch + j+v] and the
+// correlation g[u*K+v] += sum_{q,j} a[q][j] * src[(q+u)*pitch + j+v]; ctr
+// gets the window's centre (the tile's own input values).  The window is read
+// one row ahead of the FMAs that use it and no further: after a row, an empty
+// asm on every sum the row touched and on the next row's offset keeps the
+// scheduler from hoisting later rows above it (volatile asm statements keep
+// their order), so two rows are live instead of the whole window beside the
+// 2 x (tile + taps) accumulators.
+template <int K, int Q, int R>
+__device__ __forceinline__ void conv_corr_tile(const float* src, int pitch,
+                                               const float (&w)[K * K], const float (&a)[Q][R],
+                                               float (&acc)[Q][R], float (&g)[K * K],
+                                               float (&ctr)[Q][R]) {
+    constexpr int p = K / 2, NR = Q + K - 1, NC = R + K - 1;
+#pragma unroll
+    for (int q = 0; q < Q; ++q)
+#pragma unroll
+        for (int j = 0; j < R; ++j) acc[q][j] = 0.f;
+    float in[2][NC];
+#pragma unroll
+    for (int m = 0; m < NC; ++m) in[0][m] = src[m];
+    int nxt = pitch;  // element offset of the next row
+#pragma unroll
+    for (int ir = 0; ir < NR; ++ir) {
+        const float* cur = in[ir & 1];
+        if (ir + 1 < NR) {
+#pragma unroll
+            for (int m = 0; m < NC; ++m) in[(ir + 1) & 1][m] = src[nxt + m];
+            nxt += pitch;
+        }
+        if (ir >= p && ir < p + Q)
+#pragma unroll
+            for (int j = 0; j < R; ++j) ctr[ir - p][j] = cur[j + p];
+#pragma unroll
+        for (int q = 0; q < Q; ++q) {
+            const int u = ir - q;
+            if (u >= 0 && u < K) {
+#pragma unroll
+                for (int v = 0; v < K; ++v)
+#pragma unroll
+                    for (int j = 0; j < R; ++j) {
+                        acc[q][j] = fmaf(w[u * K + v], cur[j + v], acc[q][j]);
+                        g[u * K + v] = fmaf(a[q][j], cur[j + v], g[u * K + v]);
+                    }
+            }
+        }
+#pragma unroll
+        for (int q = 0; q < Q; ++q) {
+            const int u = ir - q;
+            if (u >= 0 && u < K) {
+#pragma unroll
+                for (int j = 0; j < R; ++j) asm volatile("" : "+v"(acc[q][j]));
+#pragma unroll
+                for (int v = 0; v < K; ++v) asm volatile("" : "+v"(g[u * K + v]));
+            }
+        }
+        asm volatile("" : "+v"(nxt));
+    }
+}
+
 // Fold level l's convolved subbands into the LL of level l-1.  A coarse
 // coefficient lands on the 2x2 block below it with the sign its subband has
 // at each position: the column bit flips LH and HH, the row bit HL and HH.
@@ -1368,6 +1429,185 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void k_
         reduce_row<G>(lds, gacc, sdy,
                       part + (size_t(cur) * rows.rmax + (blockIdx.x - rows.first(cur))) * G::NPART,
                       G::NPART, tid);
+}
+
+// LDS of the one-side fused backward: one array layout that x passes through
+// before dy, the folded filters after it; the reduction rows reuse the start.
+template <class G>
+constexpr size_t bwd1_lds_bytes() {
+    const size_t a = sizeof(float) * (G::side + G::NWF);
+    const size_t b = sizeof(float) * G::NT * (G::KK + 1);
+    return a > b ? a : b;
+}
+
+// Fused backward with one LDS side.  The weight taps are taken transposed:
+// dK[u][v] = sum_{m,n} U[m][n] V[m-u+p][n-v+p] (U: x's subband, V: dy's), so
+// a lane needs x only at its own tile (U[q][j], read from the arrays after x
+// is analysed into them) and reads one window, of dy, for both the
+// rotated-filter conv of the input gradient and the taps: tap (u, v) meets
+// the window at row q + K-1-u, column j + K-1-v, so the taps accumulate in
+// rotated order (gacc[KK-1-t] is tap t) with the conv's access pattern.  x
+// goes through the arrays, then dy: half the LDS of two sides, which lets
+// three workgroups share a compute unit, and half the window reads.  Items
+// and CROSS as in k_plane_bwd; the register budget is held to the waves per
+// SIMD the LDS allows, at most three.
+template <class G>
+constexpr int bwd1_waves() {
+    const int w = waves_for_lds(bwd1_lds_bytes<G>(), G::NT);
+    return w < 3 ? w : 3;
+}
+
+template <int K, int L, int H, int W, int P, int NT, typename T, bool CROSS>
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(
+    bwd1_waves<Geo<K, L, H, W, P, NT>>()))) void k_plane_bwd1(
+    const T* __restrict__ x, const T* __restrict__ dy, const T* __restrict__ wb,
+    const T* __restrict__ sb, const T* __restrict__ ww, const T* __restrict__ sw,
+    T* __restrict__ dx, float* __restrict__ part, int B, int C, LinearRows rows) {
+    using G = Geo<K, L, H, W, P, NT>;
+    using F = Fetch<G, T>;
+    constexpr int KK = G::KK, Q = G::Q, R = G::R;
+    extern __shared__ float lds[];
+    float* wf = lds + G::side;
+    const int tid = threadIdx.x;
+    const int ngroups = cdiv(B, P);
+    const long q0 = rows.q0(blockIdx.x);
+    const int nitems = int(rows.q0(blockIdx.x + 1) - q0);
+    int c = int(q0 / ngroups), grp = int(q0 % ngroups);
+    F fx, fd;
+    if (nitems > 0) {
+        fx.issue_buf(x, grp * P, B, C, c, tid);
+        fd.issue_buf(dy, grp * P, B, C, c, tid);
+    }
+    for (int i = tid; i < G::side; i += NT) lds[i] = 0.f;
+
+    const Job job = decode_job<G>(tid);
+    const int wsrc = job.lvl == 0 ? 0 : KK * (1 + (job.lvl - 1) * 4 + job.s);
+    const int win = window_index<G>(job);
+    const int pitch = level_pitch<G>(job.lvl);
+    const int hrows = by_level<G>(job.lvl, [](auto lc) { return G::hl(decltype(lc)::value); });
+    const int wcols = by_level<G>(job.lvl, [](auto lc) { return G::wl(decltype(lc)::value); });
+    const int nrows = min(Q, hrows - job.grp * Q);
+    const int ncols = min(R, wcols - job.strip * R);
+    const bool full = nrows == Q && ncols == R;
+    const int dst = win + G::p * pitch + G::p;
+    float gacc[KK];  // rotated: gacc[KK - 1 - t] accumulates tap t
+    float sdy = 0.f;
+    int cur = -1;
+    // the finished channel's partial row, taps back in order
+    auto flush = [&](int ch) {
+        float g[KK];
+#pragma unroll
+        for (int t = 0; t < KK; ++t) g[t] = gacc[KK - 1 - t];
+        reduce_row<G>(lds, g, sdy,
+                      part + (size_t(ch) * rows.rmax + (blockIdx.x - rows.first(ch))) * G::NPART,
+                      G::NPART, tid);
+    };
+    if constexpr (!CROSS) {
+        fold_weights<G, T, true>(wf, wb, wb, sb, ww, sw, C, c, tid);
+        __syncthreads();
+#pragma unroll
+        for (int t = 0; t < KK; ++t) gacc[t] = 0.f;
+        cur = c;
+    }
+
+    for (int it = 0; it < nitems; ++it) {
+        const int b0 = grp * P;
+        // the row phases' per-lane addresses derive from an opaque copy of
+        // the thread index: recomputed each group (a few adds) instead of
+        // held in registers through the conv
+        int t = tid;
+        asm volatile("" : "+v"(t));
+        if (CROSS && c != cur) {
+            if (cur >= 0) {
+                // the reduction overwrites the head of the arrays: zeroed
+                // again (their borders must read zeros), filters folded again
+                flush(cur);
+                __syncthreads();
+                constexpr int RED = NT * (KK + 1) < G::side ? NT * (KK + 1) : G::side;
+                for (int i = tid; i < RED; i += NT) lds[i] = 0.f;
+            }
+            fold_weights<G, T, true>(wf, wb, wb, sb, ww, sw, C, c, tid);
+            __syncthreads();
+#pragma unroll
+            for (int t = 0; t < KK; ++t) gacc[t] = 0.f;
+            sdy = 0.f;
+            cur = c;
+        }
+        // x through the arrays: the lane keeps U at its tile (zeros outside
+        // the level's core, so a partial tile needs no mask)
+        fx.template commit<true, false>(lds, t);
+        __syncthreads();
+        static_for<F::LEVELS + 1, L + 1>([&](auto lc) {
+            analysis_level<G, decltype(lc)::value, false>(lds, t);
+            __syncthreads();
+        });
+        float u[Q][R];
+        if (job.on)
+#pragma unroll
+            for (int qq = 0; qq < Q; ++qq)
+#pragma unroll
+                for (int j = 0; j < R; ++j) u[qq][j] = lds[dst + qq * pitch + j];
+        __syncthreads();
+        // then dy: one window for the input-gradient conv and the taps
+        fd.template commit<true, false>(lds, t);
+        __syncthreads();
+        static_for<F::LEVELS + 1, L + 1>([&](auto lc) {
+            analysis_level<G, decltype(lc)::value, false>(lds, t);
+            __syncthreads();
+        });
+        float acc[Q][R];
+        if (job.on) {
+            float w[KK];
+#pragma unroll
+            for (int t = 0; t < KK; ++t) w[t] = wf[wsrc + t];
+            float d[Q][R];
+            conv_corr_tile<K, Q, R>(lds + win, pitch, w, u, acc, gacc, d);
+            if (job.lvl == 0)
+#pragma unroll
+                for (int qq = 0; qq < Q; ++qq)
+#pragma unroll
+                    for (int j = 0; j < R; ++j) sdy += d[qq][j];
+        }
+        const bool wrap = grp + 1 == ngroups;
+        const int cn = wrap ? c + 1 : c, gn = wrap ? 0 : grp + 1;
+        // The next group's loads, after the FMAs (the offset fence follows
+        // the accumulator fences of the tile pass) and unconditional: past
+        // the range's last item they cover no planes (b0 = B: an empty
+        // buffer range, every load reads zero without touching memory).
+        // Skipped loads would keep this group's registers live, around the
+        // loop, beside the accumulators.
+        asm volatile("" : "+v"(t));
+        {
+            const bool more = it + 1 < nitems;
+            fx.issue_buf(x, more ? gn * P : B, B, C, more ? cn : c, t);
+            fd.issue_buf(dy, more ? gn * P : B, B, C, more ? cn : c, t);
+        }
+        __syncthreads();
+        if (job.on) {
+            if (full) {
+#pragma unroll
+                for (int qq = 0; qq < Q; ++qq)
+#pragma unroll
+                    for (int j = 0; j < R; ++j) lds[dst + qq * pitch + j] = acc[qq][j];
+            } else {
+#pragma unroll
+                for (int qq = 0; qq < Q; ++qq)
+#pragma unroll
+                    for (int j = 0; j < R; ++j)
+                        if (qq < nrows && j < ncols) lds[dst + qq * pitch + j] = acc[qq][j];
+            }
+        }
+        __syncthreads();
+        static_for<0, L - 2>([&](auto lc) {
+            cascade_level<G, L - decltype(lc)::value>(lds, t);
+            __syncthreads();
+        });
+        final_store<G, T>(lds, dx, b0, B, C, c, t);
+        c = cn;
+        grp = gn;
+        __syncthreads();
+    }
+    if (cur >= 0) flush(cur);
 }
 
 // Sum the partial rows of each channel in order and apply the chain rule

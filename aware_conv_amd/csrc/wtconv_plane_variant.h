@@ -19,6 +19,22 @@ struct PlaneVariant {
 
 constexpr size_t kPlaneMaxLds = 163840;  // LDS of one gfx950 compute unit
 
+// Which fused backward a shape takes.  The one-side kernel (x, then dy,
+// through one set of arrays; one window per tile for the conv and the taps)
+// has half the LDS and half the window reads of the two-side kernel but one
+// more commit phase and two more barriers per group.  Measured on the stage
+// shapes, it wins where a lane's tile holds at least 20 outputs (56 x 56:
+// 28 outputs, 97.6 -> 89.2 us per backward) or where there are no wavelet
+// levels (the plain depthwise conv: x's pass is a copy), and loses on the
+// 14-output tiles of the 28 x 28 and 14 x 14 shapes (56.0 -> 58.5 and
+// 40.6 -> 46.2 us), whose two-side LDS already lets three workgroups share a
+// compute unit.
+template <int K, int L, int H, int W, int P, int NT>
+constexpr bool bwd_one_side() {
+    using G = dev::Geo<K, L, H, W, P, NT>;
+    return (L == 0 || G::Q * G::R >= 20) && dev::bwd1_lds_bytes<G>() <= kPlaneMaxLds;
+}
+
 template <int K, int L, int H, int W, int P, int NT, typename T>
 PlaneVariant make_plane_variant(int dtype) {
     using namespace dev;
@@ -26,10 +42,14 @@ PlaneVariant make_plane_variant(int dtype) {
     using GG = GeoGrad<K, L, H, W, P, NT>;
     const size_t la = apply_lds_bytes<G>();
     const size_t lb = bww_lds_bytes<GG>();
-    constexpr size_t ld = bwd_lds_bytes<GG>();
+    constexpr bool one_side = bwd_one_side<K, L, H, W, P, NT>();
+    constexpr size_t ld = one_side ? bwd1_lds_bytes<G>() : bwd_lds_bytes<GG>();
     const void* fused = nullptr;
     const void* fused_cross = nullptr;
-    if constexpr (ld <= kPlaneMaxLds) {
+    if constexpr (one_side) {
+        fused = reinterpret_cast<const void*>(&k_plane_bwd1<K, L, H, W, P, NT, T, false>);
+        fused_cross = reinterpret_cast<const void*>(&k_plane_bwd1<K, L, H, W, P, NT, T, true>);
+    } else if constexpr (ld <= kPlaneMaxLds) {
         fused = reinterpret_cast<const void*>(&k_plane_bwd<K, L, H, W, P, NT, T, false>);
         fused_cross = reinterpret_cast<const void*>(&k_plane_bwd<K, L, H, W, P, NT, T, true>);
     }
