@@ -1240,14 +1240,6 @@ __global__ __launch_bounds__(NT) void k_plane_bww(
 // the same banks.
 template <class G>
 constexpr int bwd_dy_base() { return cdiv(G::side, 32) * 32; }
-// The fused tile backward keeps no filters in LDS.
-template <class G>
-constexpr size_t tile_bwd_lds_bytes() {
-    const size_t a = sizeof(float) * (bwd_dy_base<G>() + G::side);
-    const size_t b = sizeof(float) * G::NT * (G::KK + 1);
-    const size_t f = sizeof(float) * G::NWF;
-    return a > b ? (a > f ? a : f) : (b > f ? b : f);
-}
 template <class G>
 constexpr size_t bwd_lds_bytes() {
     const size_t a = sizeof(float) * (bwd_dy_base<G>() + G::side + G::NWF);
@@ -1939,32 +1931,48 @@ __global__ __launch_bounds__(NT) void k_tile_bww(const T* __restrict__ x,
 namespace wtc {
 namespace dev {
 
+// LDS of the one-side tile backward: one array layout (x's core, then dy with
+// its halos), the reduction rows, or the folded filters on their way to
+// registers, whichever is largest.
+template <class G>
+constexpr size_t tile_bwd1_lds_bytes() {
+    const size_t a = sizeof(float) * G::side;
+    const size_t b = sizeof(float) * G::NT * (G::KK + 1);
+    const size_t f = sizeof(float) * G::NWF;
+    return a > b ? (a > f ? a : f) : (b > f ? b : f);
+}
+template <class G>
+constexpr int tile_bwd1_waves() {
+    const int w = waves_for_lds(tile_bwd1_lds_bytes<G>(), G::NT);
+    return w < 3 ? w : 3;
+}
+
 // Fused backward of a large plane's tiles: the input gradient of the base
 // conv and levels 1..LT (plus the deep levels' contribution `deep`, NULL if
 // none) and the weight-gradient partials of those levels, reading x and dy
 // once; with `px` (NULL: none) also the box sums U^LT_LL(x) of the planes.
-// (channel, chunk) workgroups as in k_tile_bww.  dy and x are analysed
-// side by side, both with the tile's halos; each lane runs the
-// rotated-filter conv on its dy window, keeps the window's centre, masked to
-// its part of the core, and correlates it with its x window.  Two
-// workgroups per compute unit fit its LDS for k <= 5, which sets the
-// register budget; the 7 x 7 tiles need the LDS of one and take the
-// registers that leaves.
+// (channel, chunk) workgroups as in k_tile_bww.  One LDS side and transposed
+// weight taps (as k_plane_bwd1): a lane needs x's subbands only at its own
+// outputs, which lie in the tile's core, and the tile is aligned to 2^LT, so
+// x is loaded and analysed for the core alone (a quarter of the footprint
+// at 32 x 32, LT = 3) and each lane keeps U at its tile, masked to its part
+// of the core; then dy, with the halos, goes through the same arrays and
+// one window per tile feeds the input-gradient conv and the taps.  Levels
+// beyond the fetch's are analysed over their halos for x too, from stale
+// values there: only core coefficients, which depend on core values alone,
+// are read.  Registers for up to three waves per SIMD where the LDS allows.
 template <int K, int LT, int TH, int TW, int NT, typename T>
-__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(K >= 7 ? 1 : 2))) void k_tile_bwd(
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(
+    tile_bwd1_waves<Geo<K, LT, TH, TW, 1, NT, LT>>()))) void k_tile_bwd1(
     const T* __restrict__ x, const T* __restrict__ dy, const T* __restrict__ wb,
     const T* __restrict__ sb, const T* __restrict__ ww, const T* __restrict__ sw,
     const float* __restrict__ deep, T* __restrict__ dx, float* __restrict__ part,
     float* __restrict__ px, int B, int C, int Hp, int Wp, int upw, int npart) {
     using G = Geo<K, LT, TH, TW, 1, NT, LT>;
-    using F = Fetch<G, T, true>;
-    constexpr int KK = G::KK, Q = G::Q, R = G::R, DY = bwd_dy_base<G>();
+    using FX = Fetch<G, T, false>;  // x: the tile's core
+    using FD = Fetch<G, T, true>;   // dy: the core and its halos
+    constexpr int KK = G::KK, Q = G::Q, R = G::R;
     extern __shared__ float lds[];
-    // the dy side's offset in a register: one base per window row instead of
-    // an address add per paired LDS read
-    int dyo = DY;
-    asm volatile("" : "+s"(dyo));
-    float* ldy = lds + dyo;
     const int tid = threadIdx.x;
     const int c = blockIdx.x % C;
     const int chunk = blockIdx.x / C;
@@ -1973,7 +1981,8 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(K >= 7 ? 1 :
     const int u0 = chunk * upw;
     const int u1 = min(u0 + upw, units);
     TileCursor cu = TileCursor::at(u0, B, nty, ntx);  // c stays 0: one channel
-    F fx, fd;
+    FX fx;
+    FD fd;
     if (u0 < u1) {
         fx.issue_tile_buf(x, cu.b, B, C, c, tid, cu.ty * TH, cu.tx * TW, Hp, Wp);
         fd.issue_tile_buf(dy, cu.b, B, C, c, tid, cu.ty * TH, cu.tx * TW, Hp, Wp);
@@ -1988,76 +1997,85 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(K >= 7 ? 1 :
     const int ncols = min(R, wcols - job.strip * R);
     const bool full = nrows == Q && ncols == R;
     const int dst = win + G::p * pitch + G::p;
-    // the folded filters pass through the head of the x side on their way to
-    // registers, so that two workgroups fit a compute unit's LDS at k = 5
+    // the folded filters pass through the head of the arrays on their way
+    // to registers (one channel per workgroup)
     float w[KK];
     fold_weights<G, T, true>(lds, wb, wb, sb, ww, sw, C, c, tid);
     __syncthreads();
 #pragma unroll
     for (int t = 0; t < KK; ++t) w[t] = lds[wsrc + t];
     __syncthreads();
-    for (int i = tid; i < DY + G::side; i += NT) lds[i] = 0.f;
+    for (int i = tid; i < G::side; i += NT) lds[i] = 0.f;
     __syncthreads();
-    float gacc[KK];
+    float gacc[KK];  // rotated: gacc[KK - 1 - t] accumulates tap t
 #pragma unroll
     for (int t = 0; t < KK; ++t) gacc[t] = 0.f;
     float sdy = 0.f;
 
     for (int u = u0; u < u1; ++u) {
+        // row-phase addresses from an opaque copy of the thread index:
+        // recomputed per tile rather than held through the conv
+        int t = tid;
+        asm volatile("" : "+v"(t));
         const int b = cu.b, y0 = cu.ty * TH, x0 = cu.tx * TW;
         const TileCursor nx = cu.next(B, nty, ntx);
-        fx.template commit<true, false>(lds, tid);
-        fd.template commit<true, false>(ldy, tid);
+        fx.template commit<true, false>(lds, t);
         __syncthreads();
-        static_for<F::LEVELS + 1, LT + 1>([&](auto lc) {
-            analysis_level<G, decltype(lc)::value, false>(lds, tid);
-            analysis_level<G, decltype(lc)::value, false>(ldy, tid);
+        static_for<FX::LEVELS + 1, LT + 1>([&](auto lc) {
+            analysis_level<G, decltype(lc)::value, false>(lds, t);
             __syncthreads();
         });
-        DeepRegs<G> dr;
-        if (deep) fetch_deep<G>(dr, deep, b, C, c, y0, x0, Hp, Wp, tid);
-        float acc[Q][R];
-        if (job.on) {
-            // the tile's own dy values: past the job's part of the core the
-            // arrays hold halo (real neighbours), so they are masked; the
-            // core past the plane's edge reads zeros.  Taps first, then the
-            // rotated-filter conv of the dy window (kept after the
-            // correlation by the empty asm, so that its rows are not live
-            // beside the tap accumulators).
-            float d[Q][R];
+        float ux[Q][R];
+        if (job.on)
 #pragma unroll
             for (int qq = 0; qq < Q; ++qq)
 #pragma unroll
                 for (int j = 0; j < R; ++j) {
-                    const float v = ldy[dst + qq * pitch + j];
-                    d[qq][j] = (full || (qq < nrows && j < ncols)) ? v : 0.f;
+                    const float v = lds[dst + qq * pitch + j];
+                    ux[qq][j] = (full || (qq < nrows && j < ncols)) ? v : 0.f;
                 }
-            if (job.lvl == 0)
-#pragma unroll
-                for (int qq = 0; qq < Q; ++qq)
-#pragma unroll
-                    for (int j = 0; j < R; ++j) sdy += d[qq][j];
-            corr_tile<K, Q, R>(d, lds + win, pitch, gacc);
-            int yw = win;
-            asm volatile("" : "+v"(yw));
-            conv_tile<K, Q, R>(ldy + yw, pitch, w, 0.f, acc);
-        }
         if (px) {
             // the core of U^LT_LL(x): the tile's share of the box sums that
             // the deeper levels' weight gradient starts from
-            constexpr int h = G::hl(LT), w = G::wl(LT);
+            constexpr int h = G::hl(LT), wl = G::wl(LT);
             const int hd = Hp >> LT, wd = Wp >> LT;
-            if (tid < h * w) {
-                const int i = tid / w, j = tid % w;
+            if (t < h * wl) {
+                const int i = t / wl, j = t % wl;
                 const int gy = (y0 >> LT) + i, gx = (x0 >> LT) + j;
                 if (gy < hd && gx < wd)
                     px[(size_t(b) * C + c) * hd * wd + size_t(gy) * wd + gx] =
                         lds[G::uidx(LT, 0, 0, i, j)];
             }
         }
-        if (u + 1 < u1) {
-            fx.issue_tile_buf(x, nx.b, B, C, c, tid, nx.ty * TH, nx.tx * TW, Hp, Wp);
-            fd.issue_tile_buf(dy, nx.b, B, C, c, tid, nx.ty * TH, nx.tx * TW, Hp, Wp);
+        __syncthreads();
+        fd.template commit<true, false>(lds, t);
+        __syncthreads();
+        static_for<FD::LEVELS + 1, LT + 1>([&](auto lc) {
+            analysis_level<G, decltype(lc)::value, false>(lds, t);
+            __syncthreads();
+        });
+        DeepRegs<G> dr;
+        if (deep) fetch_deep<G>(dr, deep, b, C, c, y0, x0, Hp, Wp, t);
+        float acc[Q][R];
+        if (job.on) {
+            // the window's centre past the job's part of the core is halo
+            // (real neighbours): masked out of the dy sum
+            float d[Q][R];
+            conv_corr_tile<K, Q, R>(lds + win, pitch, w, ux, acc, gacc, d);
+            if (job.lvl == 0)
+#pragma unroll
+                for (int qq = 0; qq < Q; ++qq)
+#pragma unroll
+                    for (int j = 0; j < R; ++j)
+                        if (full || (qq < nrows && j < ncols)) sdy += d[qq][j];
+        }
+        // the next tile's loads after the FMAs, unconditional (past the range
+        // they cover an empty buffer range: b = B)
+        asm volatile("" : "+v"(t));
+        {
+            const bool more = u + 1 < u1;
+            fx.issue_tile_buf(x, more ? nx.b : B, B, C, c, t, nx.ty * TH, nx.tx * TW, Hp, Wp);
+            fd.issue_tile_buf(dy, more ? nx.b : B, B, C, c, t, nx.ty * TH, nx.tx * TW, Hp, Wp);
         }
         __syncthreads();
         if (job.on) {
@@ -2065,22 +2083,25 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(K >= 7 ? 1 :
             for (int qq = 0; qq < Q; ++qq)
 #pragma unroll
                 for (int j = 0; j < R; ++j)
-                    if (full || (qq < nrows && j < ncols)) ldy[dst + qq * pitch + j] = acc[qq][j];
+                    if (full || (qq < nrows && j < ncols)) lds[dst + qq * pitch + j] = acc[qq][j];
         }
         __syncthreads();
         if (deep) {
-            add_deep<G>(ldy, dr, tid);
+            add_deep<G>(lds, dr, t);
             __syncthreads();
         }
         static_for<0, LT - 2>([&](auto lc) {
-            cascade_level<G, LT - decltype(lc)::value>(ldy, tid);
+            cascade_level<G, LT - decltype(lc)::value>(lds, t);
             __syncthreads();
         });
-        final_store<G, T>(ldy, dx, b, B, C, c, tid, y0, x0, Hp, Wp);
+        final_store<G, T>(lds, dx, b, B, C, c, t, y0, x0, Hp, Wp);
         cu = nx;
         __syncthreads();
     }
-    reduce_row<G>(lds, gacc, sdy, part + (size_t(chunk) * C + c) * npart, npart, tid);
+    float g[KK];
+#pragma unroll
+    for (int t = 0; t < KK; ++t) g[t] = gacc[KK - 1 - t];
+    reduce_row<G>(lds, g, sdy, part + (size_t(chunk) * C + c) * npart, npart, tid);
 }
 
 }  // namespace dev

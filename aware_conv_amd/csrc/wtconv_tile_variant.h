@@ -35,8 +35,8 @@ TileVariant make_tile_variant(int dtype) {
         reinterpret_cast<const void*>(&dev::k_tile_apply<K, LT, kTileH, ATW, kTileNT, T, false>),
         reinterpret_cast<const void*>(&dev::k_tile_apply<K, LT, kTileH, ATW, kTileNT, T, true>),
         reinterpret_cast<const void*>(&dev::k_tile_bww<K, LT, kTileH, kTileW, kTileNT, T>),
-        reinterpret_cast<const void*>(&dev::k_tile_bwd<K, LT, kTileH, kTileW, kTileNT, T>),
-        dev::apply_lds_bytes<GA>(), dev::bww_lds_bytes<G>(), dev::tile_bwd_lds_bytes<G>()};
+        reinterpret_cast<const void*>(&dev::k_tile_bwd1<K, LT, kTileH, kTileW, kTileNT, T>),
+        dev::apply_lds_bytes<GA>(), dev::bww_lds_bytes<G>(), dev::tile_bwd1_lds_bytes<G>()};
 }
 
 // Tables of the per-k translation units (LT = 1, 2, 3; fp32 and fp16).
