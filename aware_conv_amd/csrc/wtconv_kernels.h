@@ -1504,11 +1504,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(
 
     for (int it = 0; it < nitems; ++it) {
         const int b0 = grp * P;
-        // the row phases' per-lane addresses derive from an opaque copy of
-        // the thread index: recomputed each group (a few adds) instead of
-        // held in registers through the conv
         int t = tid;
-        asm volatile("" : "+v"(t));
         if (CROSS && c != cur) {
             if (cur >= 0) {
                 // the reduction overwrites the head of the arrays: zeroed
@@ -1941,10 +1937,14 @@ constexpr size_t tile_bwd1_lds_bytes() {
     const size_t f = sizeof(float) * G::NWF;
     return a > b ? (a > f ? a : f) : (b > f ? b : f);
 }
+// Waves per SIMD for the register budget: what the LDS allows, at most 3,
+// and 2 for 7 x 7 filters (their 49 taps and wider windows need the 256
+// VGPRs of two waves; at three they spill).
 template <class G>
 constexpr int tile_bwd1_waves() {
     const int w = waves_for_lds(tile_bwd1_lds_bytes<G>(), G::NT);
-    return w < 3 ? w : 3;
+    const int cap = G::K >= 7 ? 2 : 3;
+    return w < cap ? w : cap;
 }
 
 // Fused backward of a large plane's tiles: the input gradient of the base
@@ -2013,10 +2013,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(
     float sdy = 0.f;
 
     for (int u = u0; u < u1; ++u) {
-        // row-phase addresses from an opaque copy of the thread index:
-        // recomputed per tile rather than held through the conv
         int t = tid;
-        asm volatile("" : "+v"(t));
         const int b = cu.b, y0 = cu.ty * TH, x0 = cu.tx * TW;
         const TileCursor nx = cu.next(B, nty, ntx);
         fx.template commit<true, false>(lds, t);
