@@ -88,12 +88,25 @@ __global__ __launch_bounds__(128) void k_box_sums(const T* __restrict__ src,
     }
 }
 
-// P of one plane -> bordered array m = 0.
+// P of one plane -> bordered array m = 0.  Eight loads are issued before
+// their stores: one element per iteration would wait a device-memory round
+// trip per element.
 __device__ void load_p(const float* __restrict__ Pp, const DeepLayout& D, float* lds, int base,
                        int tid, int nt) {
-    for (int e = tid; e < D.hp * D.wp; e += nt) {
-        const int i = e / D.wp, j = e % D.wp;
-        lds[base + (i + D.p) * D.bp(0) + D.p + j] = Pp[e];
+    constexpr int U = 8;
+    const int n = D.hp * D.wp;
+    for (int e0 = tid; e0 < n; e0 += U * nt) {
+        float v[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int e = e0 + u * nt;
+            v[u] = e < n ? Pp[e] : 0.f;
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int e = e0 + u * nt;
+            if (e < n) lds[base + (e / D.wp + D.p) * D.bp(0) + D.p + e % D.wp] = v[u];
+        }
     }
 }
 
