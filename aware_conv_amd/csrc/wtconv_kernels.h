@@ -831,6 +831,51 @@ __device__ __forceinline__ void conv_corr_tile(const float* src, int pitch,
     }
 }
 
+// The correlation of conv_corr_tile alone (no conv): g[u*K+v] +=
+// sum_{q,j} a[q][j] * src[(q+u)*pitch + j+v], ctr the window's centre, with
+// the same one-row-ahead reads and fences.
+template <int K, int Q, int R>
+__device__ __forceinline__ void corr_window_tile(const float* src, int pitch,
+                                                 const float (&a)[Q][R], float (&g)[K * K],
+                                                 float (&ctr)[Q][R]) {
+    constexpr int p = K / 2, NR = Q + K - 1, NC = R + K - 1;
+    float in[2][NC];
+#pragma unroll
+    for (int m = 0; m < NC; ++m) in[0][m] = src[m];
+    int nxt = pitch;
+#pragma unroll
+    for (int ir = 0; ir < NR; ++ir) {
+        const float* cur = in[ir & 1];
+        if (ir + 1 < NR) {
+#pragma unroll
+            for (int m = 0; m < NC; ++m) in[(ir + 1) & 1][m] = src[nxt + m];
+            nxt += pitch;
+        }
+        if (ir >= p && ir < p + Q)
+#pragma unroll
+            for (int j = 0; j < R; ++j) ctr[ir - p][j] = cur[j + p];
+#pragma unroll
+        for (int q = 0; q < Q; ++q) {
+            const int u = ir - q;
+            if (u >= 0 && u < K) {
+#pragma unroll
+                for (int v = 0; v < K; ++v)
+#pragma unroll
+                    for (int j = 0; j < R; ++j)
+                        g[u * K + v] = fmaf(a[q][j], cur[j + v], g[u * K + v]);
+            }
+        }
+#pragma unroll
+        for (int q = 0; q < Q; ++q) {
+            const int u = ir - q;
+            if (u >= 0 && u < K)
+#pragma unroll
+                for (int v = 0; v < K; ++v) asm volatile("" : "+v"(g[u * K + v]));
+        }
+        asm volatile("" : "+v"(nxt));
+    }
+}
+
 // Fold level l's convolved subbands into the LL of level l-1.  A coarse
 // coefficient lands on the 2x2 block below it with the sign its subband has
 // at each position: the column bit flips LH and HH, the row bit HL and HH.
@@ -1442,14 +1487,16 @@ constexpr size_t bwd1_lds_bytes() {
 // goes through the arrays, then dy: half the LDS of two sides, which lets
 // three workgroups share a compute unit, and half the window reads.  Items
 // and CROSS as in k_plane_bwd; the register budget is held to the waves per
-// SIMD the LDS allows, at most three.
+// SIMD the LDS allows, at most three.  Without DX the kernel is the weight
+// gradient alone (wtconv_bwd_weight): no conv, no input gradient, `dx` and
+// the filters unread.
 template <class G>
 constexpr int bwd1_waves() {
     const int w = waves_for_lds(bwd1_lds_bytes<G>(), G::NT);
     return w < 3 ? w : 3;
 }
 
-template <int K, int L, int H, int W, int P, int NT, typename T, bool CROSS>
+template <int K, int L, int H, int W, int P, int NT, typename T, bool CROSS, bool DX = true>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(
     bwd1_waves<Geo<K, L, H, W, P, NT>>()))) void k_plane_bwd1(
     const T* __restrict__ x, const T* __restrict__ dy, const T* __restrict__ wb,
@@ -1495,7 +1542,8 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(
                       G::NPART, tid);
     };
     if constexpr (!CROSS) {
-        fold_weights<G, T, true>(wf, wb, wb, sb, ww, sw, C, c, tid);
+        if constexpr (DX) fold_weights<G, T, true>(wf, wb, wb, sb, ww, sw, C, c, tid);
+        // also orders the zeroing above before the first commit
         __syncthreads();
 #pragma unroll
         for (int t = 0; t < KK; ++t) gacc[t] = 0.f;
@@ -1514,7 +1562,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(
                 constexpr int RED = NT * (KK + 1) < G::side ? NT * (KK + 1) : G::side;
                 for (int i = tid; i < RED; i += NT) lds[i] = 0.f;
             }
-            fold_weights<G, T, true>(wf, wb, wb, sb, ww, sw, C, c, tid);
+            if constexpr (DX) fold_weights<G, T, true>(wf, wb, wb, sb, ww, sw, C, c, tid);
             __syncthreads();
 #pragma unroll
             for (int t = 0; t < KK; ++t) gacc[t] = 0.f;
@@ -1545,11 +1593,15 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(
         });
         float acc[Q][R];
         if (job.on) {
-            float w[KK];
-#pragma unroll
-            for (int t = 0; t < KK; ++t) w[t] = wf[wsrc + t];
             float d[Q][R];
-            conv_corr_tile<K, Q, R>(lds + win, pitch, w, u, acc, gacc, d);
+            if constexpr (DX) {
+                float w[KK];
+#pragma unroll
+                for (int t = 0; t < KK; ++t) w[t] = wf[wsrc + t];
+                conv_corr_tile<K, Q, R>(lds + win, pitch, w, u, acc, gacc, d);
+            } else {
+                corr_window_tile<K, Q, R>(lds + win, pitch, u, gacc, d);
+            }
             if (job.lvl == 0)
 #pragma unroll
                 for (int qq = 0; qq < Q; ++qq)
@@ -1571,29 +1623,31 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(
             fd.issue_buf(dy, more ? gn * P : B, B, C, more ? cn : c, t);
         }
         __syncthreads();
-        if (job.on) {
-            if (full) {
+        if constexpr (DX) {
+            if (job.on) {
+                if (full) {
 #pragma unroll
-                for (int qq = 0; qq < Q; ++qq)
+                    for (int qq = 0; qq < Q; ++qq)
 #pragma unroll
-                    for (int j = 0; j < R; ++j) lds[dst + qq * pitch + j] = acc[qq][j];
-            } else {
+                        for (int j = 0; j < R; ++j) lds[dst + qq * pitch + j] = acc[qq][j];
+                } else {
 #pragma unroll
-                for (int qq = 0; qq < Q; ++qq)
+                    for (int qq = 0; qq < Q; ++qq)
 #pragma unroll
-                    for (int j = 0; j < R; ++j)
-                        if (qq < nrows && j < ncols) lds[dst + qq * pitch + j] = acc[qq][j];
+                        for (int j = 0; j < R; ++j)
+                            if (qq < nrows && j < ncols) lds[dst + qq * pitch + j] = acc[qq][j];
+                }
             }
-        }
-        __syncthreads();
-        static_for<0, L - 2>([&](auto lc) {
-            cascade_level<G, L - decltype(lc)::value>(lds, t);
             __syncthreads();
-        });
-        final_store<G, T>(lds, dx, b0, B, C, c, t);
+            static_for<0, L - 2>([&](auto lc) {
+                cascade_level<G, L - decltype(lc)::value>(lds, t);
+                __syncthreads();
+            });
+            final_store<G, T>(lds, dx, b0, B, C, c, t);
+            __syncthreads();
+        }
         c = cn;
         grp = gn;
-        __syncthreads();
     }
     if (cur >= 0) flush(cur);
 }

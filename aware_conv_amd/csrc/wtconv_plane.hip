@@ -135,38 +135,18 @@ hipError_t finalize_grads(const wtconv_shape& s, const float* part, int rows, co
                                  : launch_final<__half>(s, part, rows, none, p, g, stream);
 }
 
-hipError_t plane_bwd_weight(const wtconv_shape& s, const void* x, const void* dy,
-                            const Params& p, const Grads& g, void* workspace,
-                            hipStream_t stream) {
-    const Variant* v = find_variant(s);
-    if (!v) return hipErrorInvalidValue;
-    hipError_t e = prepare(v->bww, v->lds_bww);
-    if (e != hipSuccess) return e;
-    const int nchunk = bww_chunks(s, v->P, resident_wgs(v->bww, v->NT, v->lds_bww));
-    int gpw = cdiv(cdiv(s.B, v->P), nchunk), B = s.B, C = s.C;
-    float* part = static_cast<float*>(workspace);
-    void* args[] = {&x, &dy, &part, &B, &C, &gpw};
-    e = hipLaunchKernel(v->bww, dim3(unsigned(nchunk) * unsigned(s.C)), dim3(v->NT), args,
-                        v->lds_bww, stream);
-    if (e == hipSuccess) e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    return finalize_grads(s, part, nchunk, p, g, stream);
-}
-
-hipError_t plane_bwd(const wtconv_shape& s, const void* x, const void* dy, const Params& p,
-                     void* dx, const Grads& g, void* workspace, hipStream_t stream) {
-    const Variant* v = find_variant(s);
-    if (!v) return hipErrorInvalidValue;
-    if (!v->bwd) {
-        hipError_t e = plane_apply(s, dy, p, dx, true, stream);
-        if (e != hipSuccess) return e;
-        return plane_bwd_weight(s, x, dy, p, g, workspace, stream);
-    }
-    hipError_t e = prepare(v->bwd, v->lds_bwd);
+namespace {
+// The fused backward's launch (kernels of the LinearRows family: k_plane_bwd,
+// k_plane_bwd1, with or without dx): workgroups over balanced ranges of
+// (channel, group) items, then the finalize over each channel's rows.
+hipError_t launch_linear(const wtconv_shape& s, const Variant* v, const void* fn_one,
+                         const void* fn_cross, const void* x, const void* dy, const Params& p,
+                         void* dx, const Grads& g, void* workspace, hipStream_t stream) {
+    hipError_t e = prepare(fn_one, v->lds_bwd);
     if (e != hipSuccess) return e;
     const int ngroups = cdiv(s.B, v->P);
     const long total = long(ngroups) * s.C;
-    long nwg = resident_wgs(v->bwd, v->NT, v->lds_bwd);
+    long nwg = resident_wgs(fn_one, v->NT, v->lds_bwd);
     if (nwg > kMaxBwdWGs) nwg = kMaxBwdWGs;
     // a multiple of C puts every range inside one channel, which the kernel
     // without mid-range reductions runs faster: take it when it keeps at
@@ -192,13 +172,48 @@ hipError_t plane_bwd(const wtconv_shape& s, const void* x, const void* dy, const
     const void* ww = p.w_wav;
     const void* sw = p.s_wav;
     void* args[] = {&x, &dy, &wb, &sb, &ww, &sw, &dx, &part, &B, &C, &rows};
-    const void* fn = cross ? v->bwd_cross : v->bwd;
+    const void* fn = cross ? fn_cross : fn_one;
     if (cross && (e = prepare(fn, v->lds_bwd)) != hipSuccess) return e;
     e = hipLaunchKernel(fn, dim3(unsigned(nwg)), dim3(v->NT), args, v->lds_bwd, stream);
     if (e == hipSuccess) e = hipGetLastError();
     if (e != hipSuccess) return e;
     return s.dtype == WTCONV_F32 ? launch_final<float>(s, part, 0, rows, p, g, stream)
                                  : launch_final<__half>(s, part, 0, rows, p, g, stream);
+}
+}  // namespace
+
+hipError_t plane_bwd_weight(const wtconv_shape& s, const void* x, const void* dy,
+                            const Params& p, const Grads& g, void* workspace,
+                            hipStream_t stream) {
+    const Variant* v = find_variant(s);
+    if (!v) return hipErrorInvalidValue;
+    // shapes with the one-side fused backward take its weight-only form
+    if (v->bww1)
+        return launch_linear(s, v, v->bww1, v->bww1_cross, x, dy, p, nullptr, g, workspace,
+                             stream);
+    hipError_t e = prepare(v->bww, v->lds_bww);
+    if (e != hipSuccess) return e;
+    const int nchunk = bww_chunks(s, v->P, resident_wgs(v->bww, v->NT, v->lds_bww));
+    int gpw = cdiv(cdiv(s.B, v->P), nchunk), B = s.B, C = s.C;
+    float* part = static_cast<float*>(workspace);
+    void* args[] = {&x, &dy, &part, &B, &C, &gpw};
+    e = hipLaunchKernel(v->bww, dim3(unsigned(nchunk) * unsigned(s.C)), dim3(v->NT), args,
+                        v->lds_bww, stream);
+    if (e == hipSuccess) e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    return finalize_grads(s, part, nchunk, p, g, stream);
+}
+
+hipError_t plane_bwd(const wtconv_shape& s, const void* x, const void* dy, const Params& p,
+                     void* dx, const Grads& g, void* workspace, hipStream_t stream) {
+    const Variant* v = find_variant(s);
+    if (!v) return hipErrorInvalidValue;
+    if (!v->bwd) {
+        hipError_t e = plane_apply(s, dy, p, dx, true, stream);
+        if (e != hipSuccess) return e;
+        return plane_bwd_weight(s, x, dy, p, g, workspace, stream);
+    }
+    return launch_linear(s, v, v->bwd, v->bwd_cross, x, dy, p, dx, g, workspace, stream);
 }
 
 hipError_t zero_grads(const wtconv_shape& s, const Params& p, const Grads& g,

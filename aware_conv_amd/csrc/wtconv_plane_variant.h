@@ -14,6 +14,8 @@ struct PlaneVariant {
     const void* bww;
     const void* bwd;        // fused backward, NULL where its LDS does not fit
     const void* bwd_cross;  // the same, for ranges that span channels
+    const void* bww1;       // weight gradient alone on the one-side kernel, or NULL
+    const void* bww1_cross;
     size_t lds_apply, lds_bww, lds_bwd;
 };
 
@@ -46,9 +48,13 @@ PlaneVariant make_plane_variant(int dtype) {
     constexpr size_t ld = one_side ? bwd1_lds_bytes<G>() : bwd_lds_bytes<GG>();
     const void* fused = nullptr;
     const void* fused_cross = nullptr;
+    const void* wonly = nullptr;
+    const void* wonly_cross = nullptr;
     if constexpr (one_side) {
         fused = reinterpret_cast<const void*>(&k_plane_bwd1<K, L, H, W, P, NT, T, false>);
         fused_cross = reinterpret_cast<const void*>(&k_plane_bwd1<K, L, H, W, P, NT, T, true>);
+        wonly = reinterpret_cast<const void*>(&k_plane_bwd1<K, L, H, W, P, NT, T, false, false>);
+        wonly_cross = reinterpret_cast<const void*>(&k_plane_bwd1<K, L, H, W, P, NT, T, true, false>);
     } else if constexpr (ld <= kPlaneMaxLds) {
         fused = reinterpret_cast<const void*>(&k_plane_bwd<K, L, H, W, P, NT, T, false>);
         fused_cross = reinterpret_cast<const void*>(&k_plane_bwd<K, L, H, W, P, NT, T, true>);
@@ -57,7 +63,7 @@ PlaneVariant make_plane_variant(int dtype) {
                         reinterpret_cast<const void*>(&k_plane_apply<K, L, H, W, P, NT, T, false>),
                         reinterpret_cast<const void*>(&k_plane_apply<K, L, H, W, P, NT, T, true>),
                         reinterpret_cast<const void*>(&k_plane_bww<K, L, H, W, P, NT, T>),
-                        fused, fused_cross, la, lb, ld};
+                        fused, fused_cross, wonly, wonly_cross, la, lb, ld};
 }
 
 // Rows (K, L, H, W, planes per group, threads), both dtypes each.

@@ -86,6 +86,11 @@ def call_of(kernel_name, fused):
         c = "wtconv_bwd_input" if head.rstrip("> ").endswith("true") else "wtconv_fwd"
     elif "k_plane_bww" in n or "k_tile_bww" in n or "k_deep_bww" in n or "k_bww_final" in n:
         c = "wtconv_bwd_weight"
+    elif "k_plane_bwd1" in n and n.split("(")[0].rstrip("> ").endswith("false") and \
+            n.split("(")[0].count(",") == 8:
+        # the one-side backward's last template argument DX: false is the
+        # weight gradient alone
+        c = "wtconv_bwd_weight"
     elif "k_plane_bwd" in n or "k_tile_bwd" in n:
         c = "wtconv_bwd"
     if fused and c in ("wtconv_bwd_input", "wtconv_bwd_weight"):

@@ -21,7 +21,10 @@ import bench  # noqa: E402
     ("void wtc::dev::k_deep_bww<5>(...)", True, "wtconv_bwd"),
     ("void wtc::dev::k_bww_final<float>(...)", False, "wtconv_bwd_weight"),
     ("void wtc::dev::k_plane_bwd<5, 2, 56, 56, 1, 256, float, false>(...)", True, "wtconv_bwd"),
-    ("void wtc::dev::k_plane_bwd1<5, 2, 56, 56, 1, 256, float, false>(...)", True, "wtconv_bwd"),
+    ("void wtc::dev::k_plane_bwd1<5, 2, 56, 56, 1, 256, float, false, true>(...)", True, "wtconv_bwd"),
+    ("void wtc::dev::k_plane_bwd1<5, 2, 56, 56, 1, 256, float, true, true>(...)", False, "wtconv_bwd"),
+    ("void wtc::dev::k_plane_bwd1<5, 2, 56, 56, 1, 256, float, true, false>(...)", False, "wtconv_bwd_weight"),
+    ("void wtc::dev::k_plane_bwd1<5, 2, 56, 56, 1, 256, float, false, false>(...)", True, "wtconv_bwd"),
     ("void wtc::dev::k_tile_bwd1<5, 3, 32, 32, 256, float>(...)", True, "wtconv_bwd"),
     ("__amd_rocclr_copyBuffer", True, None),
     ("void at::native::roll_cuda_kernel<float>(...)", True, None),
