@@ -162,16 +162,17 @@ def test_tiled_ranges_span_images_and_channels(B, C, k, L, H, W, dtype):
 
 
 @pytest.mark.parametrize("B,C,k,L,H,W,dtype", [
-    (4, 200, 5, 2, 56, 56, "f32"),   # one-side fused backward (28-output tiles)
-    (4, 200, 5, 2, 56, 56, "f16"),
+    (4, 260, 5, 2, 56, 56, "f32"),   # one-side fused backward (28-output tiles)
+    (4, 260, 5, 2, 56, 56, "f16"),
     (8, 300, 5, 2, 28, 28, "f32"),   # two-side fused backward (14-output tiles)
 ])
 def test_fused_backward_ranges_span_channels(B, C, k, L, H, W, dtype):
     """More (channel, group) items than resident workgroups, and a channel
-    count of which the resident slots (three per compute unit on a 256-unit
-    device) hold no multiple within 7/8: the fused backward's ranges span
-    channels, reducing each finished channel's taps on the way and folding
-    the next channel's filters, in both backward kernels."""
+    count of which the resident slots (three or four per compute unit on a
+    256-unit device) hold no multiple within 7/8: the ranges of the fused
+    backward and of the weight-only backward span channels, reducing each
+    finished channel's taps on the way and folding the next channel's
+    filters, in both backward kernels."""
     d = wi.make_inputs(B, C, H, W, L, k, dtype, seed=C + H)
     g = torch.Generator().manual_seed(17)
     td = d["x"].dtype
