@@ -476,12 +476,13 @@ int resident(const void* fn, int nt, size_t lds) {
     return cus * per;
 }
 
-int tile_units_per_channel(const wtconv_shape& s) {
-    return s.B * ((s.H + kTileH - 1) / kTileH) * ((s.W + kTileW - 1) / kTileW);
+// Tiles per channel at the given tile size (default: the weight-gradient
+// kernel's, the most of any tile kernel, which bounds the partial rows).
+int tile_units_per_channel(const wtconv_shape& s, int th = kTileH, int tw = kTileW) {
+    return s.B * ((s.H + th - 1) / th) * ((s.W + tw - 1) / tw);
 }
 
-int tile_chunks(const wtconv_shape& s, int slots) {
-    const int units = tile_units_per_channel(s);
+int tile_chunks(const wtconv_shape& s, int slots, int units) {
     int want = slots / (s.C > 0 ? s.C : 1);
     if (want < 1) want = 1;
     if (want > kMaxTileChunks) want = kMaxTileChunks;
@@ -760,8 +761,8 @@ hipError_t launch_weight_grads(const wtconv_shape& s, const TileVariant* v, cons
     const int LT = tile_lt(s);
     hipError_t e;
     if ((e = set_lds(v->bww, v->lds_bww)) != hipSuccess) return e;
-    const int nchunk = tile_chunks(s, resident(v->bww, v->NT, v->lds_bww));
-    const int units = tile_units_per_channel(s);
+    const int units = tile_units_per_channel(s, v->TH, v->TW);
+    const int nchunk = tile_chunks(s, resident(v->bww, v->NT, v->lds_bww), units);
     int upw = (units + nchunk - 1) / nchunk;
     int B = s.B, C = s.C, H = s.H, W = s.W;
     int npart = s.k * s.k * (1 + 4 * s.L) + 1;
@@ -845,8 +846,8 @@ hipError_t tile_bwd(const wtconv_shape& s, const void* x, const void* dy, const 
             return e;
     }
     if ((e = set_lds(v->bwd, v->lds_bwd)) != hipSuccess) return e;
-    const int nchunk = tile_chunks(s, resident(v->bwd, v->NT, v->lds_bwd));
-    const int units = tile_units_per_channel(s);
+    const int units = tile_units_per_channel(s, v->TH, v->BTW);
+    const int nchunk = tile_chunks(s, resident(v->bwd, v->NT, v->lds_bwd), units);
     int upw = (units + nchunk - 1) / nchunk;
     int B = s.B, C = s.C, H = s.H, W = s.W;
     int npart = s.k * s.k * (1 + 4 * s.L) + 1;
