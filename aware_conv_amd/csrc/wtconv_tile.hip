@@ -248,12 +248,23 @@ __global__ __launch_bounds__(256) void k_deep_bww(const float* __restrict__ px,
         float acc[K];
 #pragma unroll
         for (int vv = 0; vv < K; ++vv) acc[vv] = 0.f;
+        // kDeepRS columns per step from a register window (rows are padded
+        // to whole kDeepRS segments, with zeros past the level's width):
+        // kDeepRS + (kDeepRS + K - 1) LDS reads per kDeepRS * K FMAs
+        constexpr int RS = kDeepRS;
         for (int i = i0; i < i1; ++i)
-            for (int j = 0; j < w; ++j) {
-                const float v = lds[D.u(m, s, i, j) + shift];
-                const float* xr = lds + D.u(m, s, i + uu - D.p, j - D.p);
+            for (int j0 = 0; j0 < w; j0 += RS) {
+                const float* vr = lds + D.u(m, s, i, j0) + shift;
+                const float* xr = lds + D.u(m, s, i + uu - D.p, j0 - D.p);
+                float dv[RS], xw[RS + K - 1];
 #pragma unroll
-                for (int vv = 0; vv < K; ++vv) acc[vv] = fmaf(v, xr[vv], acc[vv]);
+                for (int r = 0; r < RS; ++r) dv[r] = vr[r];
+#pragma unroll
+                for (int r = 0; r < RS + K - 1; ++r) xw[r] = xr[r];
+#pragma unroll
+                for (int r = 0; r < RS; ++r)
+#pragma unroll
+                    for (int vv = 0; vv < K; ++vv) acc[vv] = fmaf(dv[r], xw[r + vv], acc[vv]);
             }
 #pragma unroll
         for (int vv = 0; vv < K; ++vv) red[e * K + vv] = acc[vv];
@@ -395,18 +406,31 @@ __global__ __launch_bounds__(256) void k_gdeep_corr(const float* __restrict__ ux
     float acc[KK];
 #pragma unroll
     for (int t = 0; t < KK; ++t) acc[t] = 0.f;
-    for (int e = tid; e < h * w; e += NT) {
-        const int i = e / w, j = e % w;
-        const float dv = v[e];
+    // a thread takes RS columns of a row per item: RS values of dy's level
+    // and, per tap row, RS + K - 1 of x's (masked at the level's edges), so
+    // RS * KK FMAs per RS + K (RS + K - 1) loads instead of KK + 1 per KK
+    constexpr int RS = 8;
+    const int nb = (w + RS - 1) / RS;
+    for (int e = tid; e < h * nb; e += NT) {
+        const int i = e / nb, j0 = (e % nb) * RS;
+        float dv[RS];
+#pragma unroll
+        for (int r = 0; r < RS; ++r) dv[r] = j0 + r < w ? v[i * w + j0 + r] : 0.f;
 #pragma unroll
         for (int uu = 0; uu < K; ++uu) {
             const int y = i + uu - p;
             if (y < 0 || y >= h) continue;
+            float xw[RS + K - 1];
 #pragma unroll
-            for (int vv = 0; vv < K; ++vv) {
-                const int x = j + vv - p;
-                if (x >= 0 && x < w) acc[uu * K + vv] = fmaf(dv, u[y * w + x], acc[uu * K + vv]);
+            for (int r = 0; r < RS + K - 1; ++r) {
+                const int x = j0 + r - p;
+                xw[r] = x >= 0 && x < w ? u[y * w + x] : 0.f;
             }
+#pragma unroll
+            for (int r = 0; r < RS; ++r)
+#pragma unroll
+                for (int vv = 0; vv < K; ++vv)
+                    acc[uu * K + vv] = fmaf(dv[r], xw[r + vv], acc[uu * K + vv]);
         }
     }
 #pragma unroll
