@@ -38,6 +38,13 @@
 // fixed order and writes one fp32 partial row.  A finalize kernel sums the
 // rows of the batch chunks in order and applies the chain rule through the
 // fold, so results are bitwise reproducible.
+//
+// The fused backward (input gradient and weight taps in one pass) comes in
+// two forms: x and dy side by side in LDS, or -- where a lane's tile is large
+// enough -- one set of arrays that x and then dy pass through, with the taps
+// taken transposed so that one dy window per tile serves the conv and the
+// taps (k_plane_bwd1; on large planes k_tile_bwd1, whose x pass needs only
+// the tile's core).
 #include <hip/hip_fp16.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -1477,6 +1484,13 @@ constexpr size_t bwd1_lds_bytes() {
     return a > b ? a : b;
 }
 
+// Waves per SIMD for its register budget: what the LDS allows, at most 3.
+template <class G>
+constexpr int bwd1_waves() {
+    const int w = waves_for_lds(bwd1_lds_bytes<G>(), G::NT);
+    return w < 3 ? w : 3;
+}
+
 // Fused backward with one LDS side.  The weight taps are taken transposed:
 // dK[u][v] = sum_{m,n} U[m][n] V[m-u+p][n-v+p] (U: x's subband, V: dy's), so
 // a lane needs x only at its own tile (U[q][j], read from the arrays after x
@@ -1490,12 +1504,6 @@ constexpr size_t bwd1_lds_bytes() {
 // SIMD the LDS allows, at most three.  Without DX the kernel is the weight
 // gradient alone (wtconv_bwd_weight): no conv, no input gradient, `dx` and
 // the filters unread.
-template <class G>
-constexpr int bwd1_waves() {
-    const int w = waves_for_lds(bwd1_lds_bytes<G>(), G::NT);
-    return w < 3 ? w : 3;
-}
-
 template <int K, int L, int H, int W, int P, int NT, typename T, bool CROSS, bool DX = true>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(
     bwd1_waves<Geo<K, L, H, W, P, NT>>()))) void k_plane_bwd1(
