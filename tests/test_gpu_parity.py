@@ -17,63 +17,9 @@ import torch
 
 import oracle
 import wtconv_inputs as wi
+from parity_util import NAMES, TOL, assert_parity, lib, rel_err  # noqa: F401
 
 pytestmark = pytest.mark.gpu
-
-TOL = {"f32": 1e-5, "f16": 2e-2}
-NAMES = ("y", "dx", "dw_base", "db_base", "ds_base", "dw_wav", "ds_wav")
-
-
-def lib():
-    from aware_conv_amd import _lib
-    return _lib
-
-
-def gpu_run(d, dev="cuda", fused=False):
-    L = lib()
-    t = {k: v.to(dev) for k, v in d.items()}
-    p = [t[n] for n in ("w_base", "b_base", "s_base", "w_wav", "s_wav")]
-    y = L.wtconv_fwd(t["x"], *p)
-    if fused:
-        dx, g = L.wtconv_bwd(t["x"], t["dy"], *p)
-    else:
-        dx = L.wtconv_bwd_input(t["dy"], p[0], p[2], p[3], p[4])
-        g = L.wtconv_bwd_weight(t["x"], t["dy"], *p)
-    torch.cuda.synchronize()
-    out = {"y": y, "dx": dx}
-    out.update(g)
-    return {k: v.double().cpu().numpy() for k, v in out.items()}
-
-
-def oracle_run(d):
-    a = {k: v.double().numpy() for k, v in d.items()}
-    p = [a[n] for n in ("w_base", "b_base", "s_base", "w_wav", "s_wav")]
-    out = {"y": oracle.fwd(a["x"], *p)}
-    g = oracle.bwd(a["x"], a["dy"], *p)
-    out.update(g)
-    return out
-
-
-def rel_err(g, o):
-    g = g.reshape(o.shape)
-    m = np.abs(o).max() if o.size else 0.0
-    e = np.abs(g - o).max() if o.size else 0.0
-    return e / m if m > 0 else e
-
-
-def assert_parity(d, dtype, label, names=NAMES):
-    o = oracle_run(d)
-    runs = {}
-    for fused in (False, True):
-        tag = label + (" fused" if fused else "")
-        print("\ncase %s" % tag, flush=True)
-        g = runs[fused] = gpu_run(d, fused=fused)
-        errs = {n: rel_err(g[n], o[n]) for n in names}
-        print("%s: %s" % (tag, " ".join("%s=%.2e" % kv for kv in errs.items())), flush=True)
-        for n in names:
-            assert np.all(np.isfinite(g[n])), (tag, n)
-            assert errs[n] <= TOL[dtype], (tag, n, errs[n])
-    assert np.array_equal(runs[True]["dx"], runs[False]["dx"]), label
 
 
 @pytest.mark.parametrize("name", ["tiny", "stage1", "stage2", "stage3", "stage1_f16", "highres"])
