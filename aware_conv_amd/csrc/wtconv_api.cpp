@@ -46,6 +46,45 @@ bool overlap(const void* a, const void* b, size_t n) {
     return n > 0 && x < y + n && y < x + n;
 }
 
+// Two byte ranges [a, a + na) and [b, b + nb) share a byte.
+bool overlap2(const void* a, size_t na, const void* b, size_t nb) {
+    const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+    return na > 0 && nb > 0 && x < y + nb && y < x + na;
+}
+
+struct Span {
+    const void* p;
+    size_t n;
+};
+
+// The backward's outputs (dx when fused, then the five gradients) against
+// every buffer of the call: an output that shares a byte with an input, or
+// with another output, would be read or written while another wave writes
+// it (the finalize reads the parameters while it writes the gradients).
+bool backward_aliases(const wtconv_shape* s, const void* x, const void* dy,
+                      const void* const (&params)[5], void* dx, void* const (&grads)[5]) {
+    const size_t e = elem_size(s->dtype), KK = size_t(s->k) * s->k, C = size_t(s->C),
+                 L = size_t(s->L);
+    const size_t pn[5] = {C * KK * e, C * e, C * e, L * C * 4 * KK * e, L * C * 4 * e};
+    const size_t act = act_bytes(s);
+    Span in[8];
+    int nin = 0;
+    in[nin++] = Span{x, act};
+    in[nin++] = Span{dy, act};
+    for (int i = 0; i < 5; ++i) in[nin++] = Span{params[i], pn[i]};
+    Span out[6];
+    int nout = 0;
+    if (dx) out[nout++] = Span{dx, act};
+    for (int i = 0; i < 5; ++i) out[nout++] = Span{grads[i], pn[i]};
+    for (int o = 0; o < nout; ++o) {
+        for (int i = 0; i < nin; ++i)
+            if (overlap2(out[o].p, out[o].n, in[i].p, in[i].n)) return true;
+        for (int q = o + 1; q < nout; ++q)
+            if (overlap2(out[o].p, out[o].n, out[q].p, out[q].n)) return true;
+    }
+    return false;
+}
+
 int check_params(const wtconv_shape* s, const void* w_base, const void* b_base,
                  const void* s_base, const void* w_wav, const void* s_wav) {
     if (s->C == 0) return WTCONV_OK;
@@ -213,12 +252,21 @@ int backward(const wtconv_shape* s, const void* x, const void* dy, const void* w
     Params p{w_base, b_base, s_base, w_wav, s_wav};
     Grads g{dw_base, db_base, ds_base, dw_wav, ds_wav};
     hipStream_t st = static_cast<hipStream_t>(stream);
-    if (empty_act(s)) return hip_status(wtc::zero_grads(*s, p, g, st));
-    if (!x || !dy || (fused && !dx)) return WTCONV_ERR_NULL;
-    if (!aligned(x, 16) || !aligned(dy, 16) || (fused && !aligned(dx, 16)))
-        return WTCONV_ERR_ALIGN;
-    if (fused && (overlap(dx, dy, act_bytes(s)) || overlap(dx, x, act_bytes(s))))
-        return WTCONV_ERR_ALIAS;
+    const bool empty = empty_act(s);
+    if (!empty) {
+        if (!x || !dy || (fused && !dx)) return WTCONV_ERR_NULL;
+        if (!aligned(x, 16) || !aligned(dy, 16) || (fused && !aligned(dx, 16)))
+            return WTCONV_ERR_ALIGN;
+    }
+    {
+        // (empty activations: only the gradients against the parameters)
+        const wtconv_shape ps = empty ? wtconv_shape{0, s->C, 0, 0, s->L, s->k, s->dtype} : *s;
+        const void* const params[5] = {w_base, b_base, s_base, w_wav, s_wav};
+        void* const grads[5] = {dw_base, db_base, ds_base, dw_wav, ds_wav};
+        if (backward_aliases(&ps, x, dy, params, fused && !empty ? dx : nullptr, grads))
+            return WTCONV_ERR_ALIAS;
+    }
+    if (empty) return hip_status(wtc::zero_grads(*s, p, g, st));
     const Plan pl = plan_for(s);
     if (!pl.ok) return WTCONV_ERR_UNSUPPORTED;
     rc = check_workspace(workspace_bytes(s), workspace, ws_bytes);
@@ -311,7 +359,7 @@ const char* wtconv_strerror(int code) {
         case WTCONV_ERR_ALIGN: return "misaligned pointer (activations and workspace need 16 bytes)";
         case WTCONV_ERR_WORKSPACE: return "workspace smaller than wtconv_workspace_size()";
         case WTCONV_ERR_UNSUPPORTED: return "no kernel for this shape in this build";
-        case WTCONV_ERR_ALIAS: return "an output overlaps an input";
+        case WTCONV_ERR_ALIAS: return "an output overlaps an input or another output";
         case WTCONV_ERR_HIP: return "a HIP kernel launch failed";
         default: return "unknown error code";
     }

@@ -87,7 +87,7 @@ typedef struct {
 #define WTCONV_ERR_WORKSPACE (-7)   /* ws_bytes below wtconv_workspace_size() */
 #define WTCONV_ERR_UNSUPPORTED (-8) /* valid shape this build has no kernel for
                                        (a plane of 2^31 bytes or more) */
-#define WTCONV_ERR_ALIAS (-9)       /* an output overlaps an input */
+#define WTCONV_ERR_ALIAS (-9)       /* an output overlaps an input or another output */
 #define WTCONV_ERR_HIP (-100)       /* a kernel launch failed */
 
 /*
@@ -129,7 +129,8 @@ int wtconv_bwd_input(const wtconv_shape* s, const void* dy,
  * Parameter gradients of <dy, y(x)> ("all parameter gradients", same
  * passage): dw_base [C][1][k][k], db_base [C], ds_base [C],
  * dw_wav [L][C][4][k][k], ds_wav [L][C][4], in `dtype`.  Gradients are
- * overwritten, not accumulated.  Sums over the batch and the plane are taken
+ * overwritten, not accumulated; no gradient buffer may overlap x, dy, a
+ * parameter or another gradient (WTCONV_ERR_ALIAS).  Sums over the batch and the plane are taken
  * in a fixed order, so results are bitwise reproducible for a given shape.
  * Needs wtconv_workspace_size() bytes of workspace.
  */
@@ -145,7 +146,8 @@ int wtconv_bwd_weight(const wtconv_shape* s, const void* x, const void* dy,
  * one call that reads x and dy once (the training step's backward, whose
  * speed-up over the unfused layer gist.science/pt reports under
  * "Resultados").  Arguments are those of the two calls, dx included: dx
- * [B][C][H][W] must overlap neither x nor dy; the gradients are overwritten.
+ * [B][C][H][W] must overlap neither x nor dy nor a parameter, nor a
+ * gradient buffer; the gradients are overwritten.
  * Results equal the two separate calls up to floating-point evaluation
  * order, and the parameter gradients are bitwise reproducible for a given
  * shape.  Needs wtconv_workspace_size() bytes of workspace.

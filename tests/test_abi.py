@@ -99,17 +99,65 @@ def test_bwd_input_checks(lb):
     assert f(ctypes.byref(good(lb, k=2)), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE2, None, 0, None) == -3
 
 
+# Distinct, disjoint fake buffers for the backward calls: 1 GiB apart, far
+# larger than any shape below, 256-byte aligned, never dereferenced.
+def far(i):
+    return ctypes.c_void_p((i + 1) << 30)
+
+
+X, DY, DX = far(0), far(1), far(2)
+PARAMS = [far(3 + i) for i in range(5)]
+GRADS = [far(8 + i) for i in range(5)]
+WS = far(13)
+
+
 def test_bwd_weight_workspace_checks(lb):
     s = good(lb)
     need = lb.wtconv_workspace_size(s)
     assert need > 0
     f = lb.lib.wtconv_bwd_weight
-    args = [ctypes.byref(s), FAKE, FAKE2] + [FAKE] * 5 + [FAKE2] * 5
-    assert f(*args, FAKE, need - 1, None) == -7
+    args = [ctypes.byref(s), X, DY] + PARAMS + GRADS
+    assert f(*args, WS, need - 1, None) == -7
     assert f(*args, None, need, None) == -1
     assert f(*args, MIS, need, None) == -6
-    bad = [ctypes.byref(s), FAKE, FAKE2] + [FAKE] * 5 + [FAKE2] * 4 + [None]
-    assert f(*bad, FAKE, need, None) == -1
+    bad = [ctypes.byref(s), X, DY] + PARAMS + GRADS[:4] + [None]
+    assert f(*bad, WS, need, None) == -1
+
+
+@pytest.mark.parametrize("fused", [False, True])
+def test_gradient_buffers_must_not_alias(lb, fused):
+    """Every gradient buffer against x, dy, dx, the parameters and the other
+    gradients (the finalize reads the parameters while it writes the
+    gradients): an overlap is refused before anything runs."""
+    s = good(lb)
+    need = lb.wtconv_workspace_size(s)
+
+    def call(x=X, dy=DY, dx=DX, params=PARAMS, grads=GRADS):
+        if fused:
+            return lb.lib.wtconv_bwd(ctypes.byref(s), x, dy, *params, dx, *grads, WS, need - 1,
+                                     None)
+        return lb.lib.wtconv_bwd_weight(ctypes.byref(s), x, dy, *params, *grads, WS, need - 1,
+                                        None)
+
+    assert call() == -7  # no overlap: the checks reach the (short) workspace
+    for g in range(5):
+        for other in [X, DY] + PARAMS + [GR for i, GR in enumerate(GRADS) if i != g]:
+            gr = list(GRADS)
+            gr[g] = other
+            assert call(grads=gr) == -9, (g, other)
+        # a gradient that starts inside a parameter's last bytes
+        gr = list(GRADS)
+        gr[g] = ctypes.c_void_p(PARAMS[3].value + 2 * 8 * 4 * 25 * 4 - 4)  # last 4 bytes of w_wav
+        assert call(grads=gr) == -9, g
+    if fused:
+        assert call(dx=GRADS[3]) == -9
+        assert call(dx=PARAMS[0]) == -9
+    # the empty batch writes the (zero) gradients: checked there too
+    s0 = good(lb, B=0)
+    gr = list(GRADS)
+    gr[2] = PARAMS[2]  # ds_base over s_base
+    assert lb.lib.wtconv_bwd_weight(ctypes.byref(s0), None, None, *PARAMS, *gr, None, 0,
+                                    None) == -9
 
 
 def test_workspace_size_queries(lb):
@@ -136,22 +184,20 @@ def test_fused_bwd_checks(lb):
     s = good(lb)
     need = lb.wtconv_workspace_size(s)
     f = lb.lib.wtconv_bwd
-    DX = ctypes.c_void_p(0x300000)
-    GR = ctypes.c_void_p(0x400000)
 
-    def call(shape=s, x=FAKE, dy=FAKE2, dx=DX, ws=FAKE, nws=need - 1, grads=GR):
-        return f(ctypes.byref(shape), x, dy, *[FAKE] * 5, dx, *[grads] * 5, ws, nws, None)
+    def call(shape=s, x=X, dy=DY, dx=DX, ws=WS, nws=need - 1, grads=GRADS):
+        return f(ctypes.byref(shape), x, dy, *PARAMS, dx, *grads, ws, nws, None)
 
     assert call() == -7                     # workspace one byte short
     assert call(nws=need, ws=None) == -1
     assert call(dx=None) == -1
-    assert call(grads=None) == -1
+    assert call(grads=[None] * 5) == -1
     assert call(dx=MIS) == -6
-    assert call(dx=FAKE) == -9              # dx aliases x
-    assert call(dx=FAKE2) == -9             # dx aliases dy
+    assert call(dx=X) == -9                 # dx aliases x
+    assert call(dx=DY) == -9                # dx aliases dy
     assert call(shape=good(lb, k=2)) == -3
-    far = [ctypes.c_void_p(n << 40) for n in (1, 2, 3)]  # 1 TiB apart: no overlap
-    assert call(shape=good(lb, H=32768, W=32768, L=4), x=far[0], dy=far[1], dx=far[2]) == -8
+    big = [ctypes.c_void_p(n << 40) for n in (1, 2, 3)]  # 1 TiB apart: no overlap
+    assert call(shape=good(lb, H=32768, W=32768, L=4), x=big[0], dy=big[1], dx=big[2]) == -8
 
 
 def test_dwconv_checks(lb):
