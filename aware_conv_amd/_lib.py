@@ -48,6 +48,8 @@ lib.wtconv_bwd_weight.argtypes = [_sp] + [_vp] * 12 + [_vp, ctypes.c_size_t, _vp
 lib.wtconv_bwd_weight.restype = ctypes.c_int
 lib.wtconv_bwd.argtypes = [_sp] + [_vp] * 13 + [_vp, ctypes.c_size_t, _vp]
 lib.wtconv_bwd.restype = ctypes.c_int
+lib.wtconv_bwd_noalloc.argtypes = [_sp] + [_vp] * 13 + [_vp]
+lib.wtconv_bwd_noalloc.restype = ctypes.c_int
 _dp = ctypes.POINTER(DwShape)
 lib.dwconv_workspace_size.argtypes = [_dp, ctypes.POINTER(ctypes.c_size_t)]
 lib.dwconv_workspace_size.restype = ctypes.c_int
@@ -59,7 +61,7 @@ lib.wtconv_strerror.argtypes = [ctypes.c_int]
 lib.wtconv_strerror.restype = ctypes.c_char_p
 
 EXPORTED = ("wtconv_workspace_size", "wtconv_fwd", "wtconv_bwd_input",
-            "wtconv_bwd_weight", "wtconv_bwd", "wtconv_strerror",
+            "wtconv_bwd_weight", "wtconv_bwd", "wtconv_bwd_noalloc", "wtconv_strerror",
             "dwconv_workspace_size", "dwconv_fwd", "dwconv_bwd")
 
 
@@ -267,6 +269,25 @@ def wtconv_bwd(x, dy, w_base, b_base, s_base, w_wav, s_wav, dx=None, grads=None,
         ctypes.byref(s), _ptr(x), _ptr(dy), _ptr(w_base), _ptr(b_base), _ptr(s_base),
         _ptr(w_wav), _ptr(s_wav), _ptr(dx), *[_ptr(grads[n]) for n in GRAD_NAMES],
         _ptr(ws), nws, _stream(stream, x.device)), "wtconv_bwd")
+    return dx, grads
+
+
+def wtconv_bwd_noalloc(x, dy, w_base, b_base, s_base, w_wav, s_wav, dx, grads,
+                       stream=None):
+    """wtconv_bwd with the library's static scratch as its workspace: the
+    outputs dx and grads (a dict keyed by GRAD_NAMES) are the caller's, and
+    nothing is allocated, here or in the library.  Returns (dx, grads)."""
+    if dx is None or grads is None:
+        raise ValueError("wtconv_bwd_noalloc writes into caller-provided dx and grads")
+    _check_grads(x, w_wav, grads)
+    _check_call(x, w_wav, [("x", x), ("dy", dy), ("dx", dx)],
+                (w_base, b_base, s_base, w_wav, s_wav), None)
+    _grads_on_gpu(x, grads)
+    s = shape_of(x, w_wav)
+    _check(lib.wtconv_bwd_noalloc(
+        ctypes.byref(s), _ptr(x), _ptr(dy), _ptr(w_base), _ptr(b_base), _ptr(s_base),
+        _ptr(w_wav), _ptr(s_wav), _ptr(dx), *[_ptr(grads[n]) for n in GRAD_NAMES],
+        _stream(stream, x.device)), "wtconv_bwd_noalloc")
     return dx, grads
 
 

@@ -3,6 +3,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "wtconv.h"
 #include "wtconv_internal.h"
 
@@ -234,11 +236,16 @@ int apply(const wtconv_shape* s, const void* in, const void* w_base, const void*
     return hip_status(e);
 }
 
-// Shared by the weight gradient and the fused backward (dx != NULL).
+int scratch_of_current_device(void** ptr);
+
+// Shared by the weight gradient and the fused backward (dx != NULL).  With
+// `noalloc`, the workspace is the static scratch array of the current device
+// (workspace and ws_bytes are ignored).
 int backward(const wtconv_shape* s, const void* x, const void* dy, const void* w_base,
              const void* b_base, const void* s_base, const void* w_wav, const void* s_wav,
              void* dx, void* dw_base, void* db_base, void* ds_base, void* dw_wav,
-             void* ds_wav, void* workspace, size_t ws_bytes, void* stream, bool fused) {
+             void* ds_wav, void* workspace, size_t ws_bytes, void* stream, bool fused,
+             bool noalloc = false) {
     int rc = check_shape(s);
     if (rc) return rc;
     rc = check_params(s, w_base, b_base, s_base, w_wav, s_wav);
@@ -269,6 +276,18 @@ int backward(const wtconv_shape* s, const void* x, const void* dy, const void* w
     if (empty) return hip_status(wtc::zero_grads(*s, p, g, st));
     const Plan pl = plan_for(s);
     if (!pl.ok) return WTCONV_ERR_UNSUPPORTED;
+    if (noalloc) {
+        // every check above is done: only now is the device touched
+        const size_t need = workspace_bytes(s);
+        if (need > size_t(WTCONV_NOALLOC_SCRATCH_BYTES)) return WTCONV_ERR_SCRATCH;
+        workspace = nullptr;
+        ws_bytes = 0;
+        if (need > 0) {
+            rc = scratch_of_current_device(&workspace);
+            if (rc) return rc;
+            ws_bytes = size_t(WTCONV_NOALLOC_SCRATCH_BYTES);
+        }
+    }
     rc = check_workspace(workspace_bytes(s), workspace, ws_bytes);
     if (rc) return rc;
     const wtconv_shape& r = pl.run;
@@ -299,6 +318,35 @@ int backward(const wtconv_shape* s, const void* x, const void* dy, const void* w
     if (err == hipSuccess && fused && pl.padded)
         err = wtc::copy_planes(dxr, dx, planes_of(s), r.H, r.W, s->H, s->W, s->dtype, st);
     return hip_status(err);
+}
+
+// Scratch of wtconv_bwd_noalloc: the workspace of the fused backward
+// (partial rows of the parameter gradients; on large planes also the deeper
+// levels' box sums, their contribution and levels) for callers that cannot
+// allocate.  Every GPU the library runs on holds its own copy, at its own
+// address, until the process ends.  In host code `scratch` names a host-side
+// stand-in: its device address comes from hipGetSymbolAddress, once per
+// device, and only that address is ever passed to a kernel.
+static __device__ __align__(256) unsigned char scratch[WTCONV_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 256;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxDevices];  // device address of `scratch`, per device
+
+// The device address of `scratch` on the current device, looked up on the
+// first call on that device.
+int scratch_of_current_device(void** ptr) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return WTCONV_ERR_HIP;
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p)
+            return WTCONV_ERR_HIP;
+        g_scratch_ptr[dev] = p;
+    }
+    *ptr = g_scratch_ptr[dev];
+    return WTCONV_OK;
 }
 
 }  // namespace
@@ -348,6 +396,14 @@ int wtconv_bwd(const wtconv_shape* s, const void* x, const void* dy, const void*
                     ds_base, dw_wav, ds_wav, workspace, ws_bytes, stream, true);
 }
 
+int wtconv_bwd_noalloc(const wtconv_shape* s, const void* x, const void* dy,
+                       const void* w_base, const void* b_base, const void* s_base,
+                       const void* w_wav, const void* s_wav, void* dx, void* dw_base,
+                       void* db_base, void* ds_base, void* dw_wav, void* ds_wav, void* stream) {
+    return backward(s, x, dy, w_base, b_base, s_base, w_wav, s_wav, dx, dw_base, db_base,
+                    ds_base, dw_wav, ds_wav, nullptr, 0, stream, true, true);
+}
+
 const char* wtconv_strerror(int code) {
     switch (code) {
         case WTCONV_OK: return "ok";
@@ -360,6 +416,8 @@ const char* wtconv_strerror(int code) {
         case WTCONV_ERR_WORKSPACE: return "workspace smaller than wtconv_workspace_size()";
         case WTCONV_ERR_UNSUPPORTED: return "no kernel for this shape in this build";
         case WTCONV_ERR_ALIAS: return "an output overlaps an input or another output";
+        case WTCONV_ERR_SCRATCH:
+            return "shape needs more workspace than wtconv_bwd_noalloc's static scratch holds";
         case WTCONV_ERR_HIP: return "a HIP kernel launch failed";
         default: return "unknown error code";
     }

@@ -50,7 +50,8 @@
  * Ownership and threading: the caller owns every buffer, the workspace
  * included.  The library never allocates, frees or synchronises; every call
  * only enqueues kernels on `stream` (a hipStream_t, NULL for the default
- * stream) and returns.  The library keeps no state between calls.
+ * stream) and returns.  The library keeps no state between calls, apart
+ * from the static scratch of wtconv_bwd_noalloc (see there).
  *
  * Errors: every argument check happens before anything is enqueued, so a
  * negative return means nothing ran.  WTCONV_ERR_HIP means a launch failed
@@ -88,6 +89,8 @@ typedef struct {
 #define WTCONV_ERR_UNSUPPORTED (-8) /* valid shape this build has no kernel for
                                        (a plane of 2^31 bytes or more) */
 #define WTCONV_ERR_ALIAS (-9)       /* an output overlaps an input or another output */
+#define WTCONV_ERR_SCRATCH (-10)    /* wtconv_bwd_noalloc: the shape needs more workspace
+                                       than WTCONV_NOALLOC_SCRATCH_BYTES */
 #define WTCONV_ERR_HIP (-100)       /* a kernel launch failed */
 
 /*
@@ -157,6 +160,30 @@ int wtconv_bwd(const wtconv_shape* s, const void* x, const void* dy,
                const void* w_wav, const void* s_wav, void* dx, void* dw_base,
                void* db_base, void* ds_base, void* dw_wav, void* ds_wav,
                void* workspace, size_t ws_bytes, void* stream);
+
+/*
+ * Allocation-free fused backward, for callers that cannot allocate device
+ * memory or cannot own a workspace: code under HIP graph capture, tight
+ * serving loops, harnesses that forbid allocation.  Same arguments and
+ * results as wtconv_bwd without the workspace, which is instead a static
+ * array of WTCONV_NOALLOC_SCRATCH_BYTES in device memory that every GPU the
+ * library runs on holds until the process ends (its address is looked up
+ * once per device, on the first call there).  Shapes whose
+ * wtconv_workspace_size() exceeds that size are refused with
+ * WTCONV_ERR_SCRATCH before anything runs (the WTConvNeXt stage shapes need
+ * a few MiB, 8 x 64 x 512 x 512 at five levels about 33 MiB).  The call
+ * allocates nothing: no hipMalloc, no hipFree, no allocating library call.
+ * Every call on one GPU shares that GPU's array, which keeps the last call's
+ * contents (nothing in it needs to start at zero): calls that overlap in
+ * time on one GPU -- on different streams, or from different threads --
+ * race on it and give undefined results; order them on one stream.
+ */
+#define WTCONV_NOALLOC_SCRATCH_BYTES (64u << 20)
+int wtconv_bwd_noalloc(const wtconv_shape* s, const void* x, const void* dy,
+                       const void* w_base, const void* b_base, const void* s_base,
+                       const void* w_wav, const void* s_wav, void* dx,
+                       void* dw_base, void* db_base, void* ds_base,
+                       void* dw_wav, void* ds_wav, void* stream);
 
 /* Static description of an error code (never NULL). */
 const char* wtconv_strerror(int code);

@@ -200,6 +200,35 @@ def test_fused_bwd_checks(lb):
     assert call(shape=good(lb, H=32768, W=32768, L=4), x=big[0], dy=big[1], dx=big[2]) == -8
 
 
+def test_noalloc_bwd_checks(lb):
+    """The allocation-free fused backward runs the same checks as wtconv_bwd,
+    then refuses shapes whose workspace exceeds its static scratch, all
+    before touching the device."""
+    f = lb.lib.wtconv_bwd_noalloc
+
+    def call(shape, x=X, dy=DY, dx=DX, grads=GRADS):
+        return f(ctypes.byref(shape), x, dy, *PARAMS, dx, *grads, None)
+
+    assert f(None, X, DY, *PARAMS, DX, *GRADS, None) == -1
+    assert call(good(lb, k=4)) == -3
+    assert call(good(lb), dx=None) == -1
+    assert call(good(lb), dx=MIS) == -6
+    assert call(good(lb), dx=DY) == -9
+    assert call(good(lb), grads=GRADS[:4] + [PARAMS[4]]) == -9
+    limit = 64 << 20
+    src = open(os.path.join(ROOT, "include", "wtconv.h")).read()
+    assert "#define WTCONV_NOALLOC_SCRATCH_BYTES (64u << 20)" in src
+    # 8 x 64 x 1024^2 at five levels needs ~225 MiB: refused
+    s = good(lb, B=8, C=64, H=1024, W=1024, L=5)
+    assert lb.wtconv_workspace_size(s) > limit
+    big = [ctypes.c_void_p(n << 40) for n in (1, 2, 3)]  # 1 TiB apart: 2 GiB tensors
+    assert call(s, x=big[0], dy=big[1], dx=big[2]) == -10
+    # the named stage shapes fit (a few MiB); 8 x 64 x 512^2 at five levels too
+    for kw in (dict(B=64, C=96, H=56, W=56), dict(B=64, C=384, H=14, W=14, L=1),
+               dict(B=8, C=64, H=512, W=512, L=5)):
+        assert lb.wtconv_workspace_size(good(lb, **kw)) <= limit, kw
+
+
 def test_dwconv_checks(lb):
     s = lb.DwShape(2, 8, 56, 56, 7, lb.WTCONV_F32)
     f, b = lb.lib.dwconv_fwd, lb.lib.dwconv_bwd
