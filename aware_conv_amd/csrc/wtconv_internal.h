@@ -65,6 +65,14 @@ hipError_t tile_bwd_weight(const wtconv_shape& s, const void* x, const void* dy,
 hipError_t tile_bwd(const wtconv_shape& s, const void* x, const void* dy, const Params& p,
                     void* dx, const Grads& g, void* workspace, hipStream_t stream);
 
+// Raise `fn`'s dynamic-LDS limit to `lds` where that exceeds 64 KiB (once
+// per device and kernel).
+hipError_t prepare_lds(const void* fn, size_t lds);
+// Workgroups of `fn` (nt threads, lds bytes of dynamic LDS) that fit the
+// current device at once: compute units times resident workgroups per unit,
+// 1024 when it cannot be queried.  Queried once per device, kernel and size.
+int resident_wgs(const void* fn, int nt, size_t lds);
+
 // Planes of Hs x Ws -> planes of Hd x Wd: the top-left min(Hs,Hd) x
 // min(Ws,Wd) corner copied, zeros elsewhere (zero extension or cropping).
 hipError_t copy_planes(const void* src, void* dst, long planes, int Hs, int Ws, int Hd, int Wd,

@@ -22,23 +22,7 @@ const Variant* find_variant(const wtconv_shape& s) {
     return nullptr;
 }
 
-hipError_t prepare(const void* fn, size_t lds) {
-    if (lds > 65536)
-        return hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
-    return hipSuccess;
-}
-
-// Workgroups that fit on the whole device at once for this kernel (compute
-// units times resident workgroups per unit), 1024 when it cannot be queried.
-int resident_wgs(const void* fn, int nt, size_t lds) {
-    int dev = 0, cus = 0, per = 0;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, fn, nt, lds) != hipSuccess ||
-        cus <= 0 || per <= 0)
-        return 1024;
-    return cus * per;
-}
+hipError_t prepare(const void* fn, size_t lds) { return prepare_lds(fn, lds); }
 
 // Weight gradient: chunks of the batch per channel.  At most this many, so
 // that the workspace size is a function of the shape alone.

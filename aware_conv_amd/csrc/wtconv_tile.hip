@@ -484,21 +484,9 @@ size_t deep_bww_lds(const wtconv_shape& s) {
 constexpr size_t kMaxLds = 160 * 1024;
 constexpr int kMaxTileChunks = 64;
 
-hipError_t set_lds(const void* fn, size_t lds) {
-    if (lds > 65536)
-        return hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
-    return hipSuccess;
-}
+hipError_t set_lds(const void* fn, size_t lds) { return prepare_lds(fn, lds); }
 
-int resident(const void* fn, int nt, size_t lds) {
-    int dev = 0, cus = 0, per = 0;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, fn, nt, lds) != hipSuccess ||
-        cus <= 0 || per <= 0)
-        return 1024;
-    return cus * per;
-}
+int resident(const void* fn, int nt, size_t lds) { return resident_wgs(fn, nt, lds); }
 
 // Tiles per channel at the given tile size (default: the weight-gradient
 // kernel's, the most of any tile kernel, which bounds the partial rows).

@@ -7,9 +7,10 @@ A step is one pass of the whole hot path over one batch on synthetic inputs
 already resident in device memory: wtconv_fwd, then the backward, by default
 the fused wtconv_bwd (input and parameter gradients reading x and dy once),
 with --backward split the two calls wtconv_bwd_input and wtconv_bwd_weight.
-By default the step's kernels are replayed from a HIP graph (one per buffer
-set), as a training loop that captures its step would run them; --launch
-eager times the calls as issued (also reported as eager_ms_per_step).
+By default the step's kernels are replayed from a HIP graph (one graph of
+one step per buffer set, in a row), as a training loop that captures its step
+would run them; --launch eager times the calls as issued (also reported as
+eager_ms_per_step).
 W untimed steps, then exactly K timed steps bracketed by device
 synchronisation; value = images per second over the K steps.  Each
 step reads its own set of buffers, rotating over enough sets that no step
@@ -25,7 +26,22 @@ Also reported, on the same JSON line:
                counter summary when it was taken on the current kernel source,
                else null
   cpu_baseline the fp64 oracle (test infrastructure, timed as it stands) on
-               the host cores, on the same workload, about ten seconds of work
+               the host cores, on the same workload, about ten seconds of work,
+               with the host CPU's model and a one-thread time on a few images
+  step_ms      p10 / p50 / p90 of the per-step device times (a pass of K
+               steps, each behind a short spin kernel so that HIP events see
+               kernel time only; the per-call times come from the same
+               events), the mean of the timed steps, and the mean with every
+               step on the same buffer set (warm caches) beside the rotated,
+               cache-cold one
+  copy_probe   a plain device-to-device copy of 768 MiB timed on the same
+               device: the HBM bandwidth reachable on this machine, and the step's
+               effective bandwidth as a fraction of it
+Before any of it the device runs the step, in the launch mode that is timed,
+back to back for CLOCK_WARMUP_MS of wall time (untimed; reported as
+clock_warmup_ms): the clocks and the launch path take some tens of
+milliseconds of continuous work to settle, and a training loop runs in the
+settled state.
   dw7x7_baseline  the plain 7x7 depthwise conv with bias (include/dwconv.h,
                the layer WTConv replaces) timed the same way on the same
                activations: forward + one-pass backward per step, and the
@@ -47,6 +63,7 @@ PEAK_HBM_GBS = 8000.0
 KERNEL_SOURCES = os.path.join(ROOT, "aware_conv_amd", "csrc")
 TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "traffic_{workload}_{backward}.json")
 COPY_PROBE_BYTES = 3 << 28  # 768 MiB: larger than any other copy of a bench run
+CLOCK_WARMUP_MS = 500.0
 
 
 def conv_flops_per_pixel(L, k):
@@ -147,15 +164,21 @@ def summarize_traffic(fetch_dir, write_dir, wl, act_bytes, fused):
     return summary
 
 
-def cpu_baseline(wl, min_seconds=10.0):
-    import numpy as np
+def cpu_model():
+    """The host CPU's model name, from /proc/cpuinfo (None if unreadable)."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
 
-    import oracle
-    import wtconv_inputs as wi
-    d = wi.workload_inputs(wl)
-    a = {k: v.double().numpy() for k, v in d.items()}
-    p = [a[n] for n in ("w_base", "b_base", "s_base", "w_wav", "s_wav")]
-    # bounded sample: whole batches until min_seconds of work, at least one
+
+def _oracle_rate(oracle, a, p, images, min_seconds):
+    """Images per second of oracle fwd + bwd over the batch `a` (whole
+    batches until min_seconds of work, at least one)."""
     reps, t0 = 0, time.perf_counter()
     while True:
         oracle.fwd(a["x"], *p)
@@ -163,32 +186,154 @@ def cpu_baseline(wl, min_seconds=10.0):
         reps += 1
         el = time.perf_counter() - t0
         if el >= min_seconds:
-            break
-    del np
-    return {"value": round(reps * wl.B / el, 3), "unit": "images/s", "cores": oracle.num_threads(),
+            return reps, el, reps * images / el
+
+
+def cpu_baseline(wl, min_seconds=10.0, one_thread_seconds=3.0):
+    import oracle
+    import wtconv_inputs as wi
+    d = wi.workload_inputs(wl)
+    a = {k: v.double().numpy() for k, v in d.items()}
+    p = [a[n] for n in ("w_base", "b_base", "s_base", "w_wav", "s_wav")]
+    cores = oracle.num_threads()
+    reps, el, rate = _oracle_rate(oracle, a, p, wl.B, min_seconds)
+    # one thread, on the first images of the batch (the same per-image work)
+    nb = max(1, min(wl.B, 2))
+    a1 = dict(a, x=a["x"][:nb].copy(), dy=a["dy"][:nb].copy())
+    oracle.set_threads(1)
+    try:
+        reps1, el1, rate1 = _oracle_rate(oracle, a1, p, nb, one_thread_seconds)
+    finally:
+        oracle.set_threads(cores)
+    return {"value": round(rate, 3), "unit": "images/s", "cores": cores,
             "kind": "oracle",
-            "sample": "%d full %s batch(es) of %d images (fwd + bwd), fp64, %.1f s" % (reps, wl.name, wl.B, el)}
+            "sample": "%d full %s batch(es) of %d images (fwd + bwd), fp64, %.1f s" % (
+                reps, wl.name, wl.B, el),
+            "cpu_model": cpu_model(), "host_cpus": os.cpu_count(),
+            "one_thread": {"value": round(rate1, 3), "unit": "images/s",
+                           "sample": "%d x %d image(s) of %s (fwd + bwd), fp64, %.1f s" % (
+                               reps1, nb, wl.name, el1)}}
+
+
+class GraphSteps:
+    """Steps replayed from HIP graphs: one graph holds `len(sets)` steps in a
+    row, one per buffer set (so that consecutive steps read different
+    buffers), and graphs of the first r steps serve a remainder.  Replaying
+    one graph over and over costs the runtime less than switching between
+    graphs every step.  Nothing is allocated inside: every output is
+    preallocated.  With same=True every step of the graphs uses sets[0]."""
+
+    def __init__(self, torch, sets, step, same=False):
+        self.torch, self.sets, self.step, self.same = torch, sets, step, same
+        self.graphs = {}
+
+    def graph(self, r):
+        if r not in self.graphs:
+            g = self.torch.cuda.CUDAGraph()
+            with self.torch.cuda.graph(g):
+                for i in range(r):
+                    self.step(self.sets[0 if self.same else i])
+            self.torch.cuda.synchronize()
+            self.graphs[r] = g
+        return self.graphs[r]
+
+    def prepare(self, *counts):
+        """Capture, ahead of any timing, every graph that run(n) needs for
+        each n in counts."""
+        for n in counts:
+            full, r = divmod(n, len(self.sets))
+            if full:
+                self.graph(len(self.sets))
+            if r:
+                self.graph(r)
+        return self
+
+    def run(self, n):
+        """Enqueue exactly n steps."""
+        full, r = divmod(n, len(self.sets))
+        if full:
+            g = self.graph(len(self.sets))
+            for _ in range(full):
+                g.replay()
+        if r:
+            self.graph(r).replay()
+
+
+def time_steps(torch, run, warmup, steps):
+    """run(warmup) untimed, then run(steps) bracketed by device
+    synchronisation; returns the elapsed seconds of the timed steps."""
+    run(warmup)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    run(steps)
+    torch.cuda.synchronize()
+    return time.perf_counter() - t0
 
 
 def time_graphs(torch, sets, step, warmup, steps):
-    """Capture one step per buffer set into a HIP graph (nothing is allocated
-    inside: every output is preallocated), then time `steps` replays in
-    rotation after `warmup`; returns the elapsed seconds."""
-    graphs = []
-    for t in sets:
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
-            step(t)
-        graphs.append(g)
-    torch.cuda.synchronize()
-    for i in range(warmup):
-        graphs[i % len(graphs)].replay()
+    """`steps` graph-replayed steps in rotation over the buffer sets after
+    `warmup`; returns the elapsed seconds."""
+    return time_steps(torch, GraphSteps(torch, sets, step).prepare(warmup, steps).run, warmup,
+                      steps)
+
+
+def gate_cycles(torch, us):
+    """Argument of torch.cuda._sleep that keeps the stream busy for about
+    `us` microseconds (calibrated here)."""
+    n = 1 << 20
+    for _ in range(2):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        torch.cuda._sleep(n)
+        b.record()
+        torch.cuda.synchronize()
+        per_us = n / max(a.elapsed_time(b) * 1e3, 1e-3)
+    return int(per_us * us)
+
+
+def percentiles(v, qs=(10, 50, 90)):
+    """Nearest-rank percentiles of the values v."""
+    v = sorted(v)
+    out = {}
+    for q in qs:
+        i = min(len(v) - 1, max(0, int(round(q / 100.0 * len(v) + 0.5)) - 1))
+        out["p%d" % q] = round(v[i], 5)
+    return out
+
+
+def clock_warmup(torch, run, ms):
+    """Keep the device busy with back-to-back steps (run(n) enqueues n) for
+    about `ms` milliseconds (untimed), so that what follows sees settled
+    clocks and a warm launch path: a few steps estimate the step time, then
+    the rest are enqueued without a synchronisation between them (an idle
+    gap lets the clocks drop again).  Returns (steps run, ms spent)."""
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for i in range(steps):
-        graphs[i % len(graphs)].replay()
+    run(8)
     torch.cuda.synchronize()
-    return time.perf_counter() - t0
+    t1 = time.perf_counter()
+    run(8)
+    torch.cuda.synchronize()
+    est = max((time.perf_counter() - t1) * 1e3 / 8, 1e-3)
+    n = int(max(0.0, ms - (time.perf_counter() - t0) * 1e3) / est)
+    run(n)
+    torch.cuda.synchronize()
+    return 16 + n, (time.perf_counter() - t0) * 1e3
+
+
+def copy_probe_gbs(torch, dev, nbytes=COPY_PROBE_BYTES, reps=5):
+    """Read + write bandwidth (GB/s) of a plain device-to-device copy."""
+    src = torch.ones(nbytes // 4, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    el = time.perf_counter() - t0
+    del src, dst
+    return 2.0 * nbytes * reps / el / 1e9
 
 
 def dw7_baseline(L, torch, sets, wl, warmup, steps, stream, launch):
@@ -217,15 +362,17 @@ def dw7_baseline(L, torch, sets, wl, warmup, steps, stream, launch):
         if ev is not None:
             ev[2].record(st)
 
-    for i in range(warmup):
-        step(sets[i % len(sets)])
-    torch.cuda.synchronize()
+    def eager(n):
+        for i in range(n):
+            step(sets[i % len(sets)])
+
+    el = time_steps(torch, eager, warmup, steps)
+    gate = gate_cycles(torch, 400.0)
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
-    t0 = time.perf_counter()
     for i in range(steps):
+        torch.cuda._sleep(gate)
         step(sets[i % len(sets)], evs[i])
     torch.cuda.synchronize()
-    el = time.perf_counter() - t0
     fwd_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / steps
     bwd_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / steps
     if launch == "graph":
@@ -257,8 +404,10 @@ def main():
                          "calls as issued.  Per-call times always come from an eager "
                          "pass with events between the calls")
     ap.add_argument("--copy-probe", action="store_true",
-                    help="also run a plain device copy of the step's input size "
+                    help="also run three plain device copies of 768 MiB at the end "
                          "(calibrates rocprofv3 byte counters)")
+    ap.add_argument("--clock-warmup-ms", type=float, default=CLOCK_WARMUP_MS,
+                    help="untimed steps for this much wall time before anything is timed")
     ap.add_argument("--summarize-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="turn two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) of "
                          "'bench.py --copy-probe' into profiles/traffic_<workload>.json")
@@ -331,25 +480,48 @@ def main():
         if ev is not None:
             ev[len(calls)].record(st)
 
-    for i in range(args.warmup):
-        step(sets[i % nsets])
+    def eager(n, same=False):
+        for i in range(n):
+            step(sets[0 if same else i % nsets])
+
+    eager(2)  # first calls: library loading, launch set-up
     torch.cuda.synchronize()
+    if args.launch == "graph":
+        rot = GraphSteps(torch, sets, step).prepare(args.warmup, args.steps, 8)
+        same = GraphSteps(torch, sets, step, same=True).prepare(args.warmup, args.steps)
+        run = rot.run
+    else:
+        run = eager
+    # the timed steps first, right after the warm-up, in the launch mode
+    # they are timed in
+    cw_steps, cw_ms = clock_warmup(torch, run, args.clock_warmup_ms)
+    elapsed = time_steps(torch, run, args.warmup, args.steps)
+    if args.launch == "graph":
+        warm_el = time_steps(torch, same.run, args.warmup, args.steps)
+        del rot, same
+    else:
+        warm_el = time_steps(torch, lambda n: eager(n, True), args.warmup, args.steps)
+    eager_el = time_steps(torch, eager, args.warmup, args.steps)
+    eager_ms_step = eager_el * 1e3 / args.steps
+    # Per-call device time: every step waits behind a short spin kernel, so
+    # that its calls are all enqueued before the device reaches them and the
+    # events between them see kernel time only, not the host's launch work.
+    gate = gate_cycles(torch, 400.0)
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(calls) + 1)]
            for _ in range(args.steps)]
-    t0 = time.perf_counter()
     for i in range(args.steps):
+        torch.cuda._sleep(gate)
         step(sets[i % nsets], evs[i])
     torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
-    eager_ms_step = elapsed * 1e3 / args.steps
     per = {c: [e[i].elapsed_time(e[i + 1]) for e in evs] for i, c in enumerate(calls)}
     avg_ms = {k: sum(v) / len(v) for k, v in per.items()}
-    if args.launch == "graph":
-        elapsed = time_graphs(torch, sets, step, args.warmup, args.steps)
+    step_pct = percentiles([e[0].elapsed_time(e[len(calls)]) for e in evs])
 
     dw = None
     if not args.no_dw_baseline:
         dw = dw7_baseline(L, torch, sets, wl, args.warmup, args.steps, stream, args.launch)
+
+    copy_gbs = copy_probe_gbs(torch, dev)
 
     if args.copy_probe:
         src = torch.ones(COPY_PROBE_BYTES // 4, dtype=torch.float32, device=dev)
@@ -395,9 +567,18 @@ def main():
                    "levels": wl.L, "k": wl.k, "backward": args.backward,
                    "launch": args.launch, "buffer_sets": nsets},
         "eager_ms_per_step": round(eager_ms_step, 4),
+        "clock_warmup_ms": round(cw_ms, 1),
+        "clock_warmup_steps": cw_steps,
+        "step_ms": dict(step_pct, mean=round(ms_step, 5),
+                        warm_mean=round(warm_el * 1e3 / args.steps, 5)),
         "step_algo_bytes": step_bytes,
         "effective_hbm_gbs": round(step_bytes / (elapsed / args.steps) / 1e9, 1),
         "effective_hbm_frac": round(step_bytes / (elapsed / args.steps) / 1e9 / PEAK_HBM_GBS, 4),
+        "copy_probe": {"gbs": round(copy_gbs, 1), "frac_of_peak": round(copy_gbs / PEAK_HBM_GBS, 4),
+                       "effective_hbm_frac_of_copy": round(
+                           step_bytes / (elapsed / args.steps) / 1e9 / copy_gbs, 4)},
+        "valu_frac": round(sum(passes[c] for c in calls) * flops_pass / (elapsed / args.steps) /
+                           1e12 / PEAK_FP32_VALU_TFLOPS, 4),
         "per_call_ms": {k: round(v, 5) for k, v in avg_ms.items()},
         # inference alone: the forward call of the same timed steps
         "inference_images_per_s": round(wl.B / (avg_ms["wtconv_fwd"] * 1e-3), 1),
@@ -412,6 +593,8 @@ def main():
             # which these kernels are built without
             "frac_of_packed_fp32_peak": round(achieved_tf / PEAK_FP32_PACKED_TFLOPS, 4),
             "traffic": traffic,
+            "traffic_bytes_per_output_element": (round(traffic / wl.N, 3)
+                                                  if traffic is not None else None),
             "hbm_gbs": round(algo_bytes[dom] / dur_s / 1e9, 1),
             "hbm_frac": round(algo_bytes[dom] / dur_s / 1e9 / PEAK_HBM_GBS, 4),
             "flops_per_launch": passes[dom] * flops_pass,

@@ -56,6 +56,8 @@ def _load():
         lib.oracle_bwd.restype = i
         lib.oracle_num_threads.argtypes = []
         lib.oracle_num_threads.restype = i
+        lib.oracle_set_threads.argtypes = [i]
+        lib.oracle_set_threads.restype = None
         lib.oracle_haar_analysis.argtypes = [i, i, dp, dp]
         lib.oracle_haar_analysis.restype = i
         lib.oracle_haar_synthesis.argtypes = [i, i, dp, dp]
@@ -67,6 +69,12 @@ def _load():
 def num_threads():
     """OpenMP threads the oracle runs with (OMP_NUM_THREADS or all cores)."""
     return int(_load().oracle_num_threads())
+
+
+def set_threads(n):
+    """OpenMP threads of the oracle's later calls (results do not depend on
+    it: every sum runs in a fixed order within one plane or channel)."""
+    _load().oracle_set_threads(int(n))
 
 
 def _f64(a):

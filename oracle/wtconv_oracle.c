@@ -74,6 +74,16 @@ int oracle_num_threads(void) {
 #endif
 }
 
+/* Threads of the calls that follow (n >= 1; timing only, results do not
+ * depend on it). */
+void oracle_set_threads(int n) {
+#ifdef _OPENMP
+    if (n >= 1) omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}
+
 /* out[i][j] = sum_{u,v} K[u][v] * z[i+u-p][j+v-p], zero outside z. */
 static void conv_same(const double* z, int h, int w, const double* K, int k,
                       double* out) {

@@ -63,3 +63,15 @@ def test_source_hash_ignores_comments(tmp_path, monkeypatch):
     assert bench.source_hash() == h0
     src.write_text("__global__ void k(float* p) { p[0] = 2.f; }\n")
     assert bench.source_hash() != h0
+
+
+def test_percentiles_nearest_rank():
+    v = list(range(1, 101))  # 1..100
+    assert bench.percentiles(v) == {"p10": 10, "p50": 50, "p90": 90}
+    assert bench.percentiles([5.0]) == {"p10": 5.0, "p50": 5.0, "p90": 5.0}
+    assert bench.percentiles([3.0, 1.0, 2.0], qs=(50,)) == {"p50": 2.0}
+
+
+def test_cpu_model_reads_proc_cpuinfo():
+    m = bench.cpu_model()
+    assert m is None or (isinstance(m, str) and m)

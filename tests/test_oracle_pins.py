@@ -408,3 +408,23 @@ def test_result_independent_of_thread_count():
         env = dict(os.environ, OMP_NUM_THREADS=t)
         outs.append(subprocess.check_output([sys.executable, "-c", code], env=env))
     assert outs[0] == outs[1]
+
+
+def test_set_threads_keeps_the_bits():
+    """The thread count the bench's one-thread leg sets changes no result."""
+    r = np.random.default_rng(1)
+    x = r.normal(size=(2, 3, 16, 16))
+    dy = r.normal(size=x.shape)
+    p = (r.normal(size=(3, 3, 3)), r.normal(size=3), r.normal(size=3),
+         r.normal(size=(2, 3, 4, 3, 3)), r.normal(size=(2, 3, 4)))
+    n = oracle.num_threads()
+    g0 = oracle.bwd(x, dy, *p)
+    oracle.set_threads(1)
+    try:
+        assert oracle.num_threads() == 1
+        g1 = oracle.bwd(x, dy, *p)
+    finally:
+        oracle.set_threads(n)
+    assert oracle.num_threads() == n
+    for k in g0:
+        assert np.array_equal(g0[k], g1[k]), k
