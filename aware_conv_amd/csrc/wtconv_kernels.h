@@ -717,6 +717,27 @@ __device__ __forceinline__ int level_pitch(int lvl) {
     return by_level<G>(lvl, [&](auto lc) { return G::pitch(decltype(lc)::value); });
 }
 
+// Sum of a lane's tile of values: each row in order, then the row sums
+// pairwise.  A running total over many tiles then takes one addition per
+// tile instead of one per value, which keeps its rounding error that of a
+// run as long as the number of tiles.
+template <int Q, int R>
+__device__ __forceinline__ float tile_sum(const float (&d)[Q][R]) {
+    float rs[Q];
+#pragma unroll
+    for (int q = 0; q < Q; ++q) {
+        float a = d[q][0];
+#pragma unroll
+        for (int j = 1; j < R; ++j) a += d[q][j];
+        rs[q] = a;
+    }
+#pragma unroll
+    for (int w = 1; w < Q; w *= 2)
+#pragma unroll
+        for (int q = 0; q + w < Q; q += 2 * w) rs[q] += rs[q + w];
+    return rs[0];
+}
+
 // acc[q][j] = sum_{u,v} w[u*K+v] * src[(q+u)*pitch + j+v].  With CAPTURE the
 // window's centre, the tile's own input values, is kept in ctr[q][j].
 template <int K, int Q, int R, bool CAPTURE = false>
@@ -1156,23 +1177,46 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(
     }
 }
 
+// Sum over a team of 8 consecutive lanes (aligned within a 16-lane DPP row),
+// in a fixed order: two quad-permute steps leave every lane of a quad its
+// quad's sum, then row_shr:4 hands lanes 4..7 of the team the first quad's,
+// so lane 4 of the team holds the total (the other lanes hold partials).
+__device__ __forceinline__ float team8_sum(float s) {
+    constexpr int kXor1 = 0xB1;   // quad_perm [1, 0, 3, 2]
+    constexpr int kXor2 = 0x4E;   // quad_perm [2, 3, 0, 1]
+    constexpr int kShr4 = 0x114;  // row_shr:4
+    s += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(s), kXor1, 0xF, 0xF, false));
+    s += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(s), kXor2, 0xF, 0xF, false));
+    s += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(s), kShr4, 0xF, 0xF, false));
+    return s;
+}
+
 // Fixed-order workgroup reduction of the lanes' tap accumulators into one
 // partial row [G_b (KK), sum dy, G[l][s] (4 L KK)], zero-padded to npart
-// floats: each entry sums the lanes of its (array, subband) in lane order.
-// Overwrites LDS from `lds` on; the caller has synchronised the workgroup.
+// floats.  The lanes stage their accumulators in LDS; then each entry is
+// summed by a team of 8 lanes -- lane m of the team takes the entry's lanes
+// m, m + 8, ... of its (array, subband) in order, and the team's sums meet
+// in a DPP tree (team8_sum) -- so no lane walks a long serial chain and the
+// order, hence every bit, is fixed.  Overwrites LDS from `lds` on; the
+// caller has synchronised the workgroup.
 template <class G>
 __device__ __forceinline__ void reduce_row(float* lds, const float (&acc)[G::KK], float sdy,
                                            float* __restrict__ row, int npart, int tid) {
-    constexpr int KK = G::KK, RS = KK + 1;
+    constexpr int KK = G::KK, RS = KK + 1, TEAM = 8, TEAMS = G::NT / TEAM;
+    static_assert(G::NT % TEAM == 0, "whole teams");
     float* red = lds;  // [NT][KK + 1]
 #pragma unroll
     for (int t = 0; t < KK; ++t) red[tid * RS + t] = acc[t];
     red[tid * RS + KK] = sdy;
     __syncthreads();
-    for (int o = tid; o < npart; o += G::NT) {
+    const int m = tid % TEAM;
+    // a trip count uniform over the workgroup: every lane reaches the DPP
+    // steps of every round
+    for (int o0 = 0; o0 < npart; o0 += TEAMS) {
+        const int o = o0 + tid / TEAM;
         float s = 0.f;
         if (o <= KK) {
-            for (int t = G::jstart(0); t < G::jstart(1); ++t) s += red[t * RS + o];
+            for (int t = G::jstart(0) + m; t < G::jstart(1); t += TEAM) s += red[t * RS + o];
         } else if (o < G::NPART) {
             const int r = o - KK - 1, ls = r / KK, tap = r % KK;
             const int l = (ls >> 2) + 1, sb = ls & 3;
@@ -1182,13 +1226,14 @@ __device__ __forceinline__ void reduce_row(float* lds, const float (&acc)[G::KK]
                     constexpr int per = G::NS(lv) * G::NG(lv);
                     for (int pl = 0; pl < G::P; ++pl) {
                         const int t0 = G::jstart(lv) + (pl * 4 + sb) * per;
-                        for (int t = t0; t < t0 + per; ++t) s += red[t * RS + tap];
+                        for (int t = t0 + m; t < t0 + per; t += TEAM) s += red[t * RS + tap];
                     }
                 }
                 return 0;
             });
         }
-        row[o] = s;
+        s = team8_sum(s);
+        if (m == 4 && o < npart) row[o] = s;
     }
 }
 
@@ -1271,8 +1316,8 @@ __global__ __launch_bounds__(NT) void k_plane_bww(
                         const int xx = min(job.strip * R + j, W - 1);
                         const float v = to_f(dp[yy * W + xx]);
                         d[q][j] = ok ? v : 0.f;
-                        sdy += d[q][j];
                     }
+                sdy += tile_sum<Q, R>(d);
             } else {
 #pragma unroll
                 for (int q = 0; q < Q; ++q)
@@ -1424,11 +1469,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void k_
             for (int qq = 0; qq < Q; ++qq)
 #pragma unroll
                 for (int j = 0; j < R; ++j) d[qq][j] = ldy[dst + qq * pitch + j];
-            if (job.lvl == 0)
-#pragma unroll
-                for (int qq = 0; qq < Q; ++qq)
-#pragma unroll
-                    for (int j = 0; j < R; ++j) sdy += d[qq][j];
+            if (job.lvl == 0) sdy += tile_sum<Q, R>(d);
             corr_tile<K, Q, R>(d, lds + win, pitch, gacc);
             int wo = wsrc, yw = win;
             asm volatile("" : "+v"(wo));
@@ -1610,11 +1651,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(
             } else {
                 corr_window_tile<K, Q, R>(lds + win, pitch, u, gacc, d);
             }
-            if (job.lvl == 0)
-#pragma unroll
-                for (int qq = 0; qq < Q; ++qq)
-#pragma unroll
-                    for (int j = 0; j < R; ++j) sdy += d[qq][j];
+            if (job.lvl == 0) sdy += tile_sum<Q, R>(d);
         }
         const bool wrap = grp + 1 == ngroups;
         const int cn = wrap ? c + 1 : c, gn = wrap ? 0 : grp + 1;
@@ -1665,69 +1702,85 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(
 // dbeta = <Kb, G_b> + bias sum dy, dK[l,s] = gamma 4^-l G[l,s],
 // dgamma[l,s] = 4^-l <K[l,s], G[l,s]>.  Rows of channel c: with
 // rows.nwg = 0, `nchunk` rows at (chunk * C + c); otherwise the LinearRows
-// rows of c.  nchunk = 0 (and rows.nwg = 0) gives zero gradients.
+// rows of c.  nchunk = 0 (and rows.nwg = 0) gives zero gradients.  The row
+// sums and the products are taken in fp64 and rounded once to the output
+// type.  Every device-memory read (scales, bias, filters, rows) is issued
+// before the workgroup's one barrier, so the kernel waits on one round trip
+// to memory, not one per dependent step.
 template <typename T>
 __global__ __launch_bounds__(256) void k_bww_final(
     const float* __restrict__ part, int nchunk, LinearRows rows, int C, int K, int L,
     const T* __restrict__ wb, const T* __restrict__ bb, const T* __restrict__ sb,
     const T* __restrict__ ww, const T* __restrict__ sw, T* __restrict__ dwb,
     T* __restrict__ dbb, T* __restrict__ dsb, T* __restrict__ dww, T* __restrict__ dsw) {
-    extern __shared__ float g[];  // [NPART] summed rows, then Kb [KK] and K [4 L KK]
-    const int KK = K * K, NPART = KK + 1 + 4 * L * KK;
+    // [NPART] row sums (fp64), then the filters Kb [KK], K [4 L KK] and the
+    // scales gamma [4 L] (fp32)
+    extern __shared__ double gsum[];
+    const int KK = K * K, NPART = KK + 1 + 4 * L * KK, NF = KK + 4 * L * KK, NS = 4 * L;
     const int c = blockIdx.x, tid = threadIdx.x, nt = blockDim.x;
-    float* kf = g + NPART;
-    // the filters go to LDS alongside the row sums, so the products below
-    // wait on no further device-memory round trip
-    for (int i = tid; i < KK + 4 * L * KK; i += nt) {
-        if (i < KK) {
-            kf[i] = to_f(wb[size_t(c) * KK + i]);
-        } else {
-            const int j = i - KK, ls = j / KK, t = j % KK, l = ls >> 2, s = ls & 3;
-            kf[i] = to_f(ww[((size_t(l) * C + c) * 4 + s) * KK + t]);
-        }
-    }
+    float* kf = reinterpret_cast<float*>(gsum + NPART);
+    float* gam = kf + NF;
+    // sb == NULL: no base scale (the plain depthwise conv), no dsb
+    const float beta = sb ? to_f(sb[c]) : 1.f;
+    const float bias = dsb ? to_f(bb[c]) : 0.f;
     const bool lin = rows.nwg > 0;
     const int nrow = lin ? rows.count(c) : nchunk;
     const size_t base = lin ? size_t(c) * rows.rmax : size_t(c);
     const size_t step = lin ? 1 : size_t(C);
-    for (int i = tid; i < NPART; i += nt) {
-        float v[8];
-        float s = 0.f;
-        for (int ch0 = 0; ch0 < nrow; ch0 += 8) {
-#pragma unroll
-            for (int u = 0; u < 8; ++u)
-                v[u] = ch0 + u < nrow ? part[(base + size_t(ch0 + u) * step) * NPART + i] : 0.f;
-#pragma unroll
-            for (int u = 0; u < 8; ++u) s += v[u];
+    const int nmax = NF > NPART ? NF : NPART;
+    for (int i = tid; i < nmax; i += nt) {
+        float f = 0.f, sc = 0.f;
+        if (i < KK) {
+            f = to_f(wb[size_t(c) * KK + i]);
+        } else if (i < NF) {
+            const int j = i - KK, ls = j / KK, t = j % KK, l = ls >> 2, s = ls & 3;
+            f = to_f(ww[((size_t(l) * C + c) * 4 + s) * KK + t]);
         }
-        g[i] = s;
+        if (i < NS) sc = to_f(sw[(size_t(i >> 2) * C + c) * 4 + (i & 3)]);
+        double acc = 0.0;
+        if (i < NPART) {
+            // eight rows per round, loaded unconditionally (a row index past
+            // the last reads the last row again and is masked), so that the
+            // eight loads are in flight together
+            for (int ch0 = 0; ch0 < nrow; ch0 += 8) {
+                float v[8];
+#pragma unroll
+                for (int u = 0; u < 8; ++u) {
+                    const int r = min(ch0 + u, nrow - 1);
+                    v[u] = part[(base + size_t(r) * step) * NPART + i];
+                }
+#pragma unroll
+                for (int u = 0; u < 8; ++u) acc += ch0 + u < nrow ? double(v[u]) : 0.0;
+            }
+            gsum[i] = acc;
+        }
+        if (i < NF) kf[i] = f;
+        if (i < NS) gam[i] = sc;
     }
     __syncthreads();
-    // sb == NULL: no base scale (the plain depthwise conv), no dsb
-    const float beta = sb ? to_f(sb[c]) : 1.f;
-    for (int i = tid; i < KK; i += nt) dwb[size_t(c) * KK + i] = from_f<T>(beta * g[i]);
+    for (int i = tid; i < KK; i += nt) dwb[size_t(c) * KK + i] = from_f<T>(float(beta * gsum[i]));
     if (tid == 0) {
-        dbb[c] = from_f<T>(beta * g[KK]);
+        dbb[c] = from_f<T>(float(beta * gsum[KK]));
         if (dsb) {
-            float dot = 0.f;
-            for (int t = 0; t < KK; ++t) dot = fmaf(kf[t], g[t], dot);
-            dsb[c] = from_f<T>(fmaf(to_f(bb[c]), g[KK], dot));
+            double dot = double(bias) * gsum[KK];
+            for (int t = 0; t < KK; ++t) dot += double(kf[t]) * gsum[t];
+            dsb[c] = from_f<T>(float(dot));
         }
     }
     for (int i = tid; i < 4 * L * KK; i += nt) {
         const int ls = i / KK, t = i % KK, l = ls >> 2, s = ls & 3;
         const size_t gi = (size_t(l) * C + c) * 4 + s;
-        dww[gi * KK + t] = from_f<T>(to_f(sw[gi]) * ldexpf(1.f, -2 * (l + 1)) * g[KK + 1 + i]);
+        dww[gi * KK + t] = from_f<T>(float(double(gam[ls]) * ldexp(1.0, -2 * (l + 1)) *
+                                           gsum[KK + 1 + i]));
     }
-    for (int i = tid; i < 4 * L; i += nt) {
+    for (int i = tid; i < NS; i += nt) {
         const int l = i >> 2, s = i & 3;
         const size_t gi = (size_t(l) * C + c) * 4 + s;
-        float dot = 0.f;
-        for (int t = 0; t < KK; ++t) dot = fmaf(kf[KK + i * KK + t], g[KK + 1 + i * KK + t], dot);
-        dsw[gi] = from_f<T>(ldexpf(1.f, -2 * (l + 1)) * dot);
+        double dot = 0.0;
+        for (int t = 0; t < KK; ++t) dot += double(kf[KK + i * KK + t]) * gsum[KK + 1 + i * KK + t];
+        dsw[gi] = from_f<T>(float(ldexp(1.0, -2 * (l + 1)) * dot));
     }
 }
-
 
 // ---------------------------------------------------------------------------
 // Tiles of large planes
@@ -1967,8 +2020,8 @@ __global__ __launch_bounds__(NT) void k_tile_bww(const T* __restrict__ x,
                         const bool ok = qq < nrows && j < ncols && yy < Hp && xx < Wp;
                         const float v = to_f(dp[min(yy, Hp - 1) * Wp + min(xx, Wp - 1)]);
                         d[qq][j] = ok ? v : 0.f;
-                        sdy += d[qq][j];
                     }
+                sdy += tile_sum<Q, R>(d);
             } else {
 #pragma unroll
                 for (int qq = 0; qq < Q; ++qq)
@@ -2121,12 +2174,15 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(
             // (real neighbours): masked out of the dy sum
             float d[Q][R];
             conv_corr_tile<K, Q, R>(lds + win, pitch, w, ux, acc, gacc, d);
-            if (job.lvl == 0)
+            if (job.lvl == 0) {
+                float m[Q][R];
 #pragma unroll
                 for (int qq = 0; qq < Q; ++qq)
 #pragma unroll
                     for (int j = 0; j < R; ++j)
-                        if (full || (qq < nrows && j < ncols)) sdy += d[qq][j];
+                        m[qq][j] = (full || (qq < nrows && j < ncols)) ? d[qq][j] : 0.f;
+                sdy += tile_sum<Q, R>(m);
+            }
         }
         // the next tile's loads after the FMAs, unconditional (past the range
         // they cover an empty buffer range: b = B)

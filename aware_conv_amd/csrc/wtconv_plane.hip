@@ -102,8 +102,9 @@ template <typename T>
 hipError_t launch_final(const wtconv_shape& s, const float* part, int nchunk,
                         const LinearRows& rows, const Params& p, const Grads& g,
                         hipStream_t stream) {
-    const int KK = s.k * s.k;
-    const size_t lds = sizeof(float) * (size_t(2) * KK + 1 + size_t(8) * s.L * KK);
+    // fp64 row sums [NPART], fp32 filters [KK + 4 L KK] and scales [4 L]
+    const size_t KK = size_t(s.k) * s.k, L = size_t(s.L);
+    const size_t lds = sizeof(double) * (KK + 1 + 4 * L * KK) + sizeof(float) * (KK + 4 * L * KK + 4 * L);
     hipLaunchKernelGGL(k_bww_final<T>, dim3(s.C), dim3(256), lds, stream, part, nchunk, rows, s.C,
                        s.k, s.L, (const T*)p.w_base, (const T*)p.b_base, (const T*)p.s_base,
                        (const T*)p.w_wav, (const T*)p.s_wav, (T*)g.dw_base, (T*)g.db_base,

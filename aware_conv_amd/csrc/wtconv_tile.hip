@@ -483,6 +483,11 @@ size_t deep_bww_lds(const wtconv_shape& s) {
 
 constexpr size_t kMaxLds = 160 * 1024;
 constexpr int kMaxTileChunks = 64;
+// Tiles per workgroup of the weight-gradient kernels, at most: each lane
+// adds its taps over the workgroup's tiles in fp32, one after another, and
+// the rounding of such a run grows with its length; past this many tiles a
+// channel gets more workgroups (and partial rows, summed in fp64).
+constexpr int kMaxUnitsPerRow = 64;
 
 hipError_t set_lds(const void* fn, size_t lds) { return prepare_lds(fn, lds); }
 
@@ -499,8 +504,17 @@ int tile_chunks(const wtconv_shape& s, int slots, int units) {
     if (want < 1) want = 1;
     if (want > kMaxTileChunks) want = kMaxTileChunks;
     if (want > units) want = units;
-    const int upw = (units + want - 1) / want;
+    int upw = (units + want - 1) / want;
+    if (upw > kMaxUnitsPerRow) upw = kMaxUnitsPerRow;
     return (units + upw - 1) / upw;
+}
+
+// The most chunks tile_chunks returns for `units` tiles per channel, for any
+// occupancy: what the workspace holds rows for.
+int tile_chunk_bound(int units) {
+    const int a = units < kMaxTileChunks ? units : kMaxTileChunks;
+    const int b = (units + kMaxUnitsPerRow - 1) / kMaxUnitsPerRow;
+    return a > b ? a : b;
 }
 
 template <typename T, int K>
@@ -558,8 +572,7 @@ size_t p_bytes(const wtconv_shape& s) {
 size_t rows_bytes(const wtconv_shape& s) {
     const int LT = tile_lt(s);
     const size_t KK = size_t(s.k) * s.k, npart = KK + 1 + 4 * size_t(s.L) * KK;
-    const int units = tile_units_per_channel(s);
-    const size_t chunks = size_t(units < kMaxTileChunks ? units : kMaxTileChunks) +
+    const size_t chunks = size_t(tile_chunk_bound(tile_units_per_channel(s))) +
                           (s.L > LT ? size_t(s.B) : 0);
     return align_up(chunks * s.C * npart * sizeof(float));
 }

@@ -3,10 +3,11 @@ against the oracle where it stays exact at a fraction of the cost: y and dx of
 one plane depend only on that plane and its channel's parameters, and a
 channel's parameter gradients only on that channel's planes.
 
-y and dx keep the fp32 bar of 1e-5.  A parameter gradient here sums
-B * H * W = 34.6M products per tap in fp32, 173 times as many as at the
-stage-1 workload (64 * 56 * 56), and the rounding error of a sum grows like
-the square root of its length: the gradients get 1e-5 * sqrt(173) = 1.3e-4."""
+Every output keeps the fp32 bar of 1e-5.  A parameter gradient here sums
+B * H * W = 34.6M products per tap: each lane adds its products over at most
+64 tiles in fp32, the lanes of a workgroup meet in a fixed-order tree, and the
+workgroups' partial rows are summed in fp64, so the error stays that of short
+fp32 runs however long the whole sum."""
 import numpy as np
 import pytest
 import torch
@@ -57,7 +58,7 @@ def test_more_than_2_31_elements():
         edx = rel_err(dx[b:b + 1, c:c + 1].double().cpu().numpy(), oracle.bwd(xo, dyo, *po)["dx"])
         print("plane (%d, %d): y %.2e dx %.2e" % (b, c, ey, edx), flush=True)
         assert ey <= 1e-5 and edx <= 1e-5, (b, c, ey, edx)
-    grad_tol = 1e-5 * np.sqrt((B * H * W) / (64 * 56 * 56))
+    grad_tol = 1e-5
     for c in (0, 63):
         xo = x[:, c:c + 1].double().cpu().numpy()
         dyo = dy[:, c:c + 1].double().cpu().numpy()
