@@ -17,6 +17,8 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 OUT = os.path.join(HERE, "libwtconv.so")
+PROBE_SRC = os.path.join(CSRC, "probe", "valu_rate.hip")
+PROBE_OUT = os.path.join(HERE, "valu_probe")
 BUILD = os.path.join(HERE, "_build")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -57,8 +59,15 @@ def build(verbose=True):
     if r.returncode != 0:
         raise RuntimeError("link failed:\n%s%s" % (r.stdout, r.stderr))
     os.replace(tmp, OUT)
+    # the vector-ALU issue-rate probe (bench.py --valu-probe), same flags
+    tmp = PROBE_OUT + ".tmp%d" % os.getpid()
+    cmd = [HIPCC] + [f for f in FLAGS if f != "-fPIC"] + [PROBE_SRC, "-o", tmp]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError("hipcc failed on %s:\n%s%s" % (PROBE_SRC, r.stdout, r.stderr))
+    os.replace(tmp, PROBE_OUT)
     if verbose:
-        print("built", OUT)
+        print("built", OUT, "and", PROBE_OUT)
     return OUT
 
 

@@ -17,11 +17,14 @@ step reads its own set of buffers, rotating over enough sets that no step
 finds the previous step's tensors in the 256 MB last-level cache.
 
 Also reported, on the same JSON line:
-  roofline     the dominant kernel (longest average launch, timed live with
-               HIP events on the stream it is launched on) against the
-               roof that bounds it: algorithmic FLOPs over the fp32 vector
-               peak without packed FP32 (the kernels are built with packed
-               FP32 selection off), with its HBM bandwidth fraction alongside;
+  roofline     the dominant call (longest average device time, timed with
+               HIP events on the stream it is launched on) against the roof
+               that bounds it by arithmetic intensity: algorithmic bytes over
+               the 8 TB/s HBM peak when its FLOPs per byte fall below the ridge
+               (157.3 TFLOP/s fp32 vector / 8 TB/s = 19.7 FLOP/B), else
+               algorithmic FLOPs over 157.3 TFLOP/s; both fractions are
+               reported.  Plain v_fmac_f32 issues at that vector rate on
+               gfx950 (no packed-FP32 instruction is needed or used);
                traffic = HBM bytes per launch from the committed rocprofv3
                counter summary when it was taken on the current kernel source,
                else null
@@ -57,9 +60,9 @@ import time
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-PEAK_FP32_VALU_TFLOPS = 78.6    # 256 CU * 4 SIMD * 16 lanes * 2 FLOP * 2.4 GHz, no packed FP32
-PEAK_FP32_PACKED_TFLOPS = 157.3  # the same with packed FP32 (the published fp32 vector peak)
+PEAK_FP32_VALU_TFLOPS = 157.3  # MI355X fp32 vector peak (published); v_fmac_f32 issues at it
 PEAK_HBM_GBS = 8000.0
+RIDGE_FLOP_PER_BYTE = PEAK_FP32_VALU_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)
 KERNEL_SOURCES = os.path.join(ROOT, "aware_conv_amd", "csrc")
 TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "traffic_{workload}_{backward}.json")
 COPY_PROBE_BYTES = 3 << 28  # 768 MiB: larger than any other copy of a bench run
@@ -162,6 +165,35 @@ def summarize_traffic(fetch_dir, write_dir, wl, act_bytes, fused):
         "write_bytes_per_launch": out["WRITE_SIZE"]["bytes_per_call"],
     }
     return summary
+
+
+def roofline(call, flops, nbytes, dur_s, traffic, n_out):
+    """The roofline record of one call: bound by arithmetic intensity
+    (algorithmic FLOPs per algorithmic byte) against the ridge, achieved and
+    peak in that roof's unit, and the other roof's fraction alongside."""
+    gbs = nbytes / dur_s / 1e9
+    tfs = flops / dur_s / 1e12
+    ai = flops / nbytes
+    hbm = ai < RIDGE_FLOP_PER_BYTE
+    rec = {
+        "kernel": call,
+        "bound": "hbm" if hbm else "alu",
+        "achieved": round(gbs if hbm else tfs, 2),
+        "peak": PEAK_HBM_GBS if hbm else PEAK_FP32_VALU_TFLOPS,
+        "unit": "GB/s" if hbm else "TFLOP/s",
+        "frac": round(gbs / PEAK_HBM_GBS if hbm else tfs / PEAK_FP32_VALU_TFLOPS, 4),
+        "traffic": traffic,
+        "traffic_bytes_per_output_element": (round(traffic / n_out, 3)
+                                              if traffic is not None else None),
+        "flop_per_byte": round(ai, 2),
+        "hbm_gbs": round(gbs, 1),
+        "hbm_frac": round(gbs / PEAK_HBM_GBS, 4),
+        "valu_tflops": round(tfs, 2),
+        "valu_frac": round(tfs / PEAK_FP32_VALU_TFLOPS, 4),
+        "flops_per_launch": flops,
+        "algo_bytes_per_launch": nbytes,
+    }
+    return rec
 
 
 def cpu_model():
@@ -408,6 +440,10 @@ def main():
                          "(calibrates rocprofv3 byte counters)")
     ap.add_argument("--clock-warmup-ms", type=float, default=CLOCK_WARMUP_MS,
                     help="untimed steps for this much wall time before anything is timed")
+    ap.add_argument("--valu-probe", action="store_true",
+                    help="run the vector-ALU issue-rate probe (built by build()) and print "
+                         "its JSON line: the fp32 FMA rate the roofline's 157.3 TFLOP/s "
+                         "stands for")
     ap.add_argument("--summarize-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="turn two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) of "
                          "'bench.py --copy-probe' into profiles/traffic_<workload>.json")
@@ -424,6 +460,15 @@ def main():
             json.dump(summ, f, indent=1, sort_keys=True)
         print(json.dumps(summ, indent=1, sort_keys=True))
         return
+    if args.valu_probe:
+        import subprocess
+        probe = os.path.join(ROOT, "aware_conv_amd", "valu_probe")
+        if not os.path.exists(probe):
+            sys.exit("valu_probe is not built: run __graft_entry__.build() first")
+        r = subprocess.run([probe], capture_output=True, text=True, timeout=120)
+        sys.stdout.write(r.stdout)
+        sys.stderr.write(r.stderr)
+        sys.exit(r.returncode)
     if args.gpus != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path "
               "(--gpus %d requested)" % args.gpus, file=sys.stderr)
@@ -541,7 +586,6 @@ def main():
     passes = {"wtconv_fwd": 1, "wtconv_bwd_input": 1, "wtconv_bwd_weight": 1, "wtconv_bwd": 2}
     dom = max(avg_ms, key=avg_ms.get)
     dur_s = avg_ms[dom] * 1e-3
-    achieved_tf = passes[dom] * flops_pass / dur_s / 1e12
     traffic = None
     tpath = TRAFFIC_SUMMARY.format(workload=wl.name, backward=args.backward)
     if os.path.exists(tpath):
@@ -582,24 +626,7 @@ def main():
         "per_call_ms": {k: round(v, 5) for k, v in avg_ms.items()},
         # inference alone: the forward call of the same timed steps
         "inference_images_per_s": round(wl.B / (avg_ms["wtconv_fwd"] * 1e-3), 1),
-        "roofline": {
-            "kernel": dom,
-            "bound": "alu",
-            "achieved": round(achieved_tf, 2),
-            "peak": PEAK_FP32_VALU_TFLOPS,
-            "unit": "TFLOP/s",
-            "frac": round(achieved_tf / PEAK_FP32_VALU_TFLOPS, 4),
-            # the published fp32 vector peak counts packed FP32 instructions,
-            # which these kernels are built without
-            "frac_of_packed_fp32_peak": round(achieved_tf / PEAK_FP32_PACKED_TFLOPS, 4),
-            "traffic": traffic,
-            "traffic_bytes_per_output_element": (round(traffic / wl.N, 3)
-                                                  if traffic is not None else None),
-            "hbm_gbs": round(algo_bytes[dom] / dur_s / 1e9, 1),
-            "hbm_frac": round(algo_bytes[dom] / dur_s / 1e9 / PEAK_HBM_GBS, 4),
-            "flops_per_launch": passes[dom] * flops_pass,
-            "algo_bytes_per_launch": algo_bytes[dom],
-        },
+        "roofline": roofline(dom, passes[dom] * flops_pass, algo_bytes[dom], dur_s, traffic, wl.N),
     }
     if dw is not None:
         dw["wtconv_over_dw_train"] = round(value / dw["images_per_s"], 3)

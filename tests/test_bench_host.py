@@ -75,3 +75,16 @@ def test_percentiles_nearest_rank():
 def test_cpu_model_reads_proc_cpuinfo():
     m = bench.cpu_model()
     assert m is None or (isinstance(m, str) and m)
+
+
+def test_roofline_bound_follows_arithmetic_intensity():
+    # fp32 stage-1 forward: 2.17 GFLOP on 154 MB, 14 FLOP/B < 19.7: HBM-bound
+    r = bench.roofline("wtconv_fwd", 2.17e9, 154e6, 50e-6, None, 1)
+    assert r["bound"] == "hbm" and r["unit"] == "GB/s" and r["peak"] == 8000.0
+    assert r["achieved"] == pytest.approx(154e6 / 50e-6 / 1e9, rel=1e-3)
+    assert r["frac"] == pytest.approx(r["achieved"] / 8000.0, rel=1e-3)
+    # the same FLOPs on fp16 bytes (half): 28 FLOP/B > 19.7: FMA-bound
+    r = bench.roofline("wtconv_fwd", 2.17e9, 77e6, 50e-6, 80e6, 10)
+    assert r["bound"] == "alu" and r["unit"] == "TFLOP/s" and r["peak"] == 157.3
+    assert r["traffic_bytes_per_output_element"] == pytest.approx(8e6)
+    assert bench.RIDGE_FLOP_PER_BYTE == pytest.approx(157.3e12 / 8e12)
