@@ -12,7 +12,9 @@ import os
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libwtconv.so")
+# WTCONV_LIB: another build of the same library (the host-sanitized
+# libwtconv_asan.so for the CPU ABI tests)
+LIB_PATH = os.environ.get("WTCONV_LIB") or os.path.join(_HERE, "libwtconv.so")
 
 WTCONV_F32 = 0
 WTCONV_F16 = 1

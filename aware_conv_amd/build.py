@@ -1,11 +1,21 @@
 """Build the HIP library (libwtconv.so) in-tree for gfx950.
 
-    python -m aware_conv_amd.build
+    python -m aware_conv_amd.build              # libwtconv.so, valu_probe
+    python -m aware_conv_amd.build --sanitize   # libwtconv_asan.so
 
 compiles every source under ``csrc/`` with hipcc and links one shared object
 next to this file.  Packed-FP32 instruction selection is switched off for the
 device code (``-packed-fp32-ops``); hipcc's host pass warns that it does not
 know that feature, which is harmless.
+
+``--sanitize`` builds the same library with the host code (the C-ABI argument
+checks, workspace sizing, dispatch) under AddressSanitizer and
+UndefinedBehaviorSanitizer (``-Xarch_host`` before each ``-fsanitize=``: the
+GPU code is built as usual).  The CPU ABI tests run against it with
+
+    WTCONV_LIB=aware_conv_amd/libwtconv_asan.so ASAN_OPTIONS=detect_leaks=0 \
+    LD_PRELOAD=$(/opt/rocm/llvm/bin/clang -print-file-name=libclang_rt.asan-x86_64.so) \
+    python -m pytest tests/test_abi.py -q -m "not gpu"
 """
 import os
 import subprocess
@@ -20,6 +30,11 @@ OUT = os.path.join(HERE, "libwtconv.so")
 PROBE_SRC = os.path.join(CSRC, "probe", "valu_rate.hip")
 PROBE_OUT = os.path.join(HERE, "valu_probe")
 BUILD = os.path.join(HERE, "_build")
+OUT_ASAN = os.path.join(HERE, "libwtconv_asan.so")
+BUILD_ASAN = os.path.join(HERE, "_build_asan")
+# host-only sanitizers: each -fsanitize= right after -Xarch_host
+SAN_FLAGS = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+             "-Xarch_host", "-fno-omit-frame-pointer", "-Xarch_host", "-fno-sanitize-recover=all"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
@@ -35,9 +50,9 @@ def sources():
                   if f.endswith((".hip", ".cpp")))
 
 
-def _compile(src):
-    obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [HIPCC] + FLAGS + ["-c", src, "-o", obj]
+def _compile(src, build_dir=BUILD, extra=()):
+    obj = os.path.join(build_dir, os.path.basename(src) + ".o")
+    cmd = [HIPCC] + FLAGS + list(extra) + ["-c", src, "-o", obj]
     if src.endswith(".cpp"):
         cmd[1:1] = ["-x", "hip"]
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -71,6 +86,28 @@ def build(verbose=True):
     return OUT
 
 
+def build_sanitized(verbose=True):
+    """libwtconv_asan.so: host code under ASan and UBSan (CPU checks only)."""
+    os.makedirs(BUILD_ASAN, exist_ok=True)
+    srcs = sources()
+    workers = max(1, min(len(srcs), int(os.environ.get("MAX_JOBS", "8"))))
+    with ThreadPoolExecutor(workers) as ex:
+        objs = list(ex.map(lambda f: _compile(f, BUILD_ASAN, SAN_FLAGS), srcs))
+    tmp = OUT_ASAN + ".tmp%d" % os.getpid()
+    cmd = [HIPCC, "-shared", "-fPIC", "--offload-arch=gfx950", "-shared-libsan",
+           "-fsanitize=address,undefined", "-o", tmp] + objs
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError("link failed:\n%s%s" % (r.stdout, r.stderr))
+    os.replace(tmp, OUT_ASAN)
+    if verbose:
+        print("built", OUT_ASAN)
+    return OUT_ASAN
+
+
 if __name__ == "__main__":
-    build()
+    if "--sanitize" in sys.argv[1:]:
+        build_sanitized()
+    else:
+        build()
     sys.exit(0)

@@ -26,7 +26,9 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "wtconv_oracle.c")
-_LIB = os.path.join(_HERE, "liboracle.so")
+# ORACLE_LIB: another build of the same oracle (the sanitized one)
+_LIB = os.environ.get("ORACLE_LIB") or os.path.join(_HERE, "liboracle.so")
+_LIB_SAN = os.path.join(_HERE, "liboracle_asan.so")
 _lib = None
 
 
@@ -40,6 +42,19 @@ def build(force=False):
     subprocess.check_call(cmd)
     os.replace(tmp, _LIB)
     return _LIB
+
+
+def build_sanitized():
+    """liboracle_asan.so: the oracle under AddressSanitizer and
+    UndefinedBehaviorSanitizer (gcc), for a run of the pins with
+    ORACLE_LIB pointing at it and gcc's libasan preloaded."""
+    tmp = _LIB_SAN + ".tmp%d" % os.getpid()
+    cmd = ["gcc", "-O1", "-g", "-std=c99", "-fopenmp", "-shared", "-fPIC",
+           "-fsanitize=address,undefined", "-fno-sanitize-recover=all",
+           "-fno-omit-frame-pointer", "-o", tmp, _SRC]
+    subprocess.check_call(cmd)
+    os.replace(tmp, _LIB_SAN)
+    return _LIB_SAN
 
 
 def _load():
