@@ -15,33 +15,69 @@ namespace wtc {
 namespace {
 
 // dst (planes x Hd x Wd) from src (planes x Hs x Ws): dst[i][j] = src[i][j]
-// where i < Hs and j < Ws, else 0.  One thread per destination element.
-template <typename T>
+// where i < Hs and j < Ws, else 0.  A thread writes V consecutive elements
+// of one destination row (V = 4 when Wd is a multiple of 4, so that the
+// write is one 16-byte store for fp32, one 8-byte store for fp16; else 1)
+// and reads its source elements one by one (source rows are aligned to no
+// more than one element).  The row of a group is found once per group, with
+// 32-bit arithmetic where the rows fit it.
+template <typename T, int V>
 __global__ __launch_bounds__(256) void k_copy_planes(const T* __restrict__ src,
-                                                     T* __restrict__ dst, long planes, int Hs,
+                                                     T* __restrict__ dst, long rows, int Hs,
                                                      int Ws, int Hd, int Wd) {
-    const size_t n = size_t(planes) * Hd * Wd;
-    for (size_t e = size_t(blockIdx.x) * blockDim.x + threadIdx.x; e < n;
-         e += size_t(gridDim.x) * blockDim.x) {
-        const int j = int(e % Wd);
-        const size_t r = e / Wd;
-        const int i = int(r % Hd);
-        const size_t pl = r / Hd;
-        T v = T(0.f);
-        if (i < Hs && j < Ws) v = src[(pl * Hs + i) * Ws + j];
-        dst[e] = v;
+    const int gpr = Wd / V;  // groups per destination row
+    const long groups = rows * gpr;
+    for (long g = long(blockIdx.x) * blockDim.x + threadIdx.x; g < groups;
+         g += long(gridDim.x) * blockDim.x) {
+        long row;
+        int j0;
+        if (groups < (1L << 31)) {
+            const unsigned gu = unsigned(g);
+            row = gu / unsigned(gpr);
+            j0 = int(gu - unsigned(row) * unsigned(gpr)) * V;
+        } else {
+            row = g / gpr;
+            j0 = int(g - row * gpr) * V;
+        }
+        long pl;
+        int i;
+        if (rows < (1L << 31)) {
+            const unsigned ru = unsigned(row);
+            pl = ru / unsigned(Hd);
+            i = int(ru - unsigned(pl) * unsigned(Hd));
+        } else {
+            pl = row / Hd;
+            i = int(row - pl * Hd);
+        }
+        const T* s = src + (size_t(pl) * Hs + i) * Ws;
+        T v[V];
+#pragma unroll
+        for (int e = 0; e < V; ++e) v[e] = (i < Hs && j0 + e < Ws) ? s[j0 + e] : T(0.f);
+        T* d = dst + size_t(row) * Wd + j0;
+        if constexpr (V == 4) {
+            struct alignas(4 * sizeof(T)) Q { T e[4]; };
+            *reinterpret_cast<Q*>(d) = Q{{v[0], v[1], v[2], v[3]}};
+        } else {
+            d[0] = v[0];
+        }
     }
 }
 
 template <typename T>
 hipError_t launch_copy(const void* src, void* dst, long planes, int Hs, int Ws, int Hd, int Wd,
                        hipStream_t stream) {
-    const size_t n = size_t(planes) * Hd * Wd;
+    const long rows = planes * Hd;
+    const bool v4 = Wd % 4 == 0;
+    const size_t n = size_t(rows) * (v4 ? Wd / 4 : Wd);
     if (n == 0) return hipSuccess;
     size_t blocks = (n + 255) / 256;
-    if (blocks > 8192) blocks = 8192;
-    hipLaunchKernelGGL(k_copy_planes<T>, dim3(unsigned(blocks)), dim3(256), 0, stream,
-                       static_cast<const T*>(src), static_cast<T*>(dst), planes, Hs, Ws, Hd, Wd);
+    if (blocks > 16384) blocks = 16384;
+    if (v4)
+        hipLaunchKernelGGL((k_copy_planes<T, 4>), dim3(unsigned(blocks)), dim3(256), 0, stream,
+                           static_cast<const T*>(src), static_cast<T*>(dst), rows, Hs, Ws, Hd, Wd);
+    else
+        hipLaunchKernelGGL((k_copy_planes<T, 1>), dim3(unsigned(blocks)), dim3(256), 0, stream,
+                           static_cast<const T*>(src), static_cast<T*>(dst), rows, Hs, Ws, Hd, Wd);
     return hipGetLastError();
 }
 
