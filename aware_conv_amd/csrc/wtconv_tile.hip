@@ -20,7 +20,13 @@ namespace dev {
 
 // Outputs per work item along a row of a deep conv, and row chunks per
 // (level, subband, tap row) of a deep correlation.
-constexpr int kDeepRS = 8, kDeepNCH = 6;
+constexpr int kDeepRS = 8, kDeepNCH = 12;
+// Threads of a deep workgroup (one per plane).  A deep workgroup is a chain
+// of short phases over one plane's box sums; 512 threads split its
+// correlations into twice the row chunks of 256 (512², L = 5: k_deep_bww
+// 53 -> ~41 us, the fused backward 1008 -> 990 us; 1024 threads gain no
+// more).
+constexpr int kDeepNT = 512;
 
 // LDS plan of a deep workgroup (floats): folded filters, then per level m of
 // P (m = 0: P itself) a bordered x-side array set, then unbordered results.
@@ -133,7 +139,7 @@ __device__ void deep_analysis(const DeepLayout& D, float* lds, int shift, int ti
 // the plane's box sums P.  Each work item computes kDeepRS outputs of one
 // row of one subband from a K x (kDeepRS + K - 1) window held in registers.
 template <typename T, int K, bool FLIP>
-__global__ __launch_bounds__(256) void k_deep_apply(
+__global__ __launch_bounds__(kDeepNT) void k_deep_apply(
     const float* __restrict__ P, const T* __restrict__ ww, const T* __restrict__ sw,
     float* __restrict__ deep, int B, int C, int Hp, int Wp, int L, int LT) {
     extern __shared__ float lds[];
@@ -216,7 +222,7 @@ __global__ __launch_bounds__(256) void k_deep_apply(
 // (row0 + b) * C + c.  A work item is one (level, subband, tap row) over a
 // chunk of the rows, with K tap accumulators; the chunks are summed in order.
 template <int K>
-__global__ __launch_bounds__(256) void k_deep_bww(const float* __restrict__ px,
+__global__ __launch_bounds__(kDeepNT) void k_deep_bww(const float* __restrict__ px,
                                                   const float* __restrict__ pdy,
                                                   float* __restrict__ part, int B, int C,
                                                   int Hp, int Wp, int L, int LT, int row0,
@@ -714,7 +720,7 @@ hipError_t launch_deep_apply(const wtconv_shape& s, const float* P, const Params
     const void* ww = p.w_wav;
     const void* sw = p.s_wav;
     void* args[] = {&P, &ww, &sw, &deep, &B, &C, &H, &W, &L, &LTv};
-    e = hipLaunchKernel(fn, dim3(unsigned(B) * unsigned(C)), dim3(256), args, lds, stream);
+    e = hipLaunchKernel(fn, dim3(unsigned(B) * unsigned(C)), dim3(kDeepNT), args, lds, stream);
     if (e != hipSuccess) return e;
     return hipGetLastError();
 }
@@ -741,7 +747,7 @@ hipError_t deep_rows(const wtconv_shape& s, const float* Px, const float* Pdy, f
         const size_t lds = deep_bww_lds(s);
         if ((e = set_lds(fn, lds)) != hipSuccess) return e;
         void* args[] = {&Px, &Pdy, &part, &B, &C, &H, &W, &L, &LTv, &row0, &npart};
-        e = hipLaunchKernel(fn, dim3(unsigned(B) * unsigned(C)), dim3(256), args, lds, stream);
+        e = hipLaunchKernel(fn, dim3(unsigned(B) * unsigned(C)), dim3(kDeepNT), args, lds, stream);
         if (e != hipSuccess) return e;
         return hipGetLastError();
     }
