@@ -1086,8 +1086,9 @@ constexpr size_t bww_lds_bytes() {
 // allows, at most 3.  Shapes that fit 128 VGPRs keep four waves anyway; the
 // ones that do not (the 56 x 56 stage shape among them) would spill at four,
 // and each spilled register is a scratch store per thread of every
-// workgroup, HBM writes beside the output, for no speed (the forward is
-// bound by its instruction count, not by its occupancy).
+// workgroup, HBM writes beside the output, for no speed (at 127 VGPRs and
+// four waves the stage-1 forward ran no faster than at three: its time is
+// the latency of its per-group phase chain, not a lack of waves).
 template <int K, int L, int H, int W, int P, int NT, typename T>
 constexpr int apply_waves() {
     const int w = waves_for_lds(apply_lds_bytes<Geo<K, L, H, W, P, NT>>(), NT);
