@@ -87,6 +87,25 @@ bool backward_aliases(const wtconv_shape* s, const void* x, const void* dy,
     return false;
 }
 
+// The workspace [workspace, workspace + need) against every other buffer of
+// a call: the kernels write it while they read the inputs and write the
+// outputs.
+bool workspace_aliases(const wtconv_shape* s, const void* workspace, size_t need,
+                       const void* const* acts, int nacts, const void* const (&params)[5],
+                       const void* const* grads) {
+    if (need == 0 || !workspace) return false;
+    const size_t e = elem_size(s->dtype), KK = size_t(s->k) * s->k, C = size_t(s->C),
+                 L = size_t(s->L);
+    const size_t pn[5] = {C * KK * e, C * e, C * e, L * C * 4 * KK * e, L * C * 4 * e};
+    for (int i = 0; i < nacts; ++i)
+        if (overlap2(workspace, need, acts[i], act_bytes(s))) return true;
+    for (int i = 0; i < 5; ++i) {
+        if (overlap2(workspace, need, params[i], pn[i])) return true;
+        if (grads && overlap2(workspace, need, grads[i], pn[i])) return true;
+    }
+    return false;
+}
+
 int check_params(const wtconv_shape* s, const void* w_base, const void* b_base,
                  const void* s_base, const void* w_wav, const void* s_wav) {
     if (s->C == 0) return WTCONV_OK;
@@ -221,8 +240,15 @@ int apply(const wtconv_shape* s, const void* in, const void* w_base, const void*
     if (overlap(in, out, act_bytes(s))) return WTCONV_ERR_ALIAS;
     const Plan pl = plan_for(s);
     if (!pl.ok) return WTCONV_ERR_UNSUPPORTED;
-    rc = check_workspace(apply_workspace_bytes(s), workspace, ws_bytes);
+    const size_t need = apply_workspace_bytes(s);
+    rc = check_workspace(need, workspace, ws_bytes);
     if (rc) return rc;
+    {
+        const void* const acts[2] = {in, out};
+        const void* const params[5] = {w_base, b_base, s_base, w_wav, s_wav};
+        if (workspace_aliases(s, workspace, need, acts, 2, params, nullptr))
+            return WTCONV_ERR_ALIAS;
+    }
     Params p{w_base, b_base, s_base, w_wav, s_wav};
     hipStream_t st = static_cast<hipStream_t>(stream);
     if (!pl.padded) return hip_status(run_apply(pl, in, p, out, flip, workspace, st));
@@ -290,6 +316,14 @@ int backward(const wtconv_shape* s, const void* x, const void* dy, const void* w
     }
     rc = check_workspace(workspace_bytes(s), workspace, ws_bytes);
     if (rc) return rc;
+    if (!noalloc) {
+        const void* const acts[3] = {x, dy, dx};
+        const void* const params[5] = {w_base, b_base, s_base, w_wav, s_wav};
+        const void* const grads[5] = {dw_base, db_base, ds_base, dw_wav, ds_wav};
+        if (workspace_aliases(s, workspace, workspace_bytes(s), acts, fused ? 3 : 2, params,
+                              grads))
+            return WTCONV_ERR_ALIAS;
+    }
     const wtconv_shape& r = pl.run;
     hipError_t err = hipSuccess;
     const void* xr = x;

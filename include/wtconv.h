@@ -44,11 +44,14 @@
  * its shape implies, on the current HIP device; a shorter buffer, or host
  * memory, is read or written out of bounds on the GPU.
  *
- * Arithmetic: loads are widened to fp32, every sum is accumulated in fp32 and
- * each output is rounded once (round-to-nearest-even) to `dtype`.
+ * Arithmetic: loads are widened to fp32, every sum is accumulated in fp32
+ * (the parameter gradients' partial rows are then summed, and put through
+ * the chain rule of the scale folding, in fp64) and each output is rounded
+ * once (round-to-nearest-even) to `dtype`.
  *
  * Ownership and threading: the caller owns every buffer, the workspace
- * included.  The library never allocates, frees or synchronises; every call
+ * included; the workspace may not overlap any other buffer of the call
+ * (WTCONV_ERR_ALIAS).  The library never allocates, frees or synchronises; every call
  * only enqueues kernels on `stream` (a hipStream_t, NULL for the default
  * stream) and returns.  The library keeps no state between calls, apart
  * from the static scratch of wtconv_bwd_noalloc (see there).
@@ -88,7 +91,8 @@ typedef struct {
 #define WTCONV_ERR_WORKSPACE (-7)   /* ws_bytes below wtconv_workspace_size() */
 #define WTCONV_ERR_UNSUPPORTED (-8) /* valid shape this build has no kernel for
                                        (a plane of 2^31 bytes or more) */
-#define WTCONV_ERR_ALIAS (-9)       /* an output overlaps an input or another output */
+#define WTCONV_ERR_ALIAS (-9)       /* an output overlaps an input or another output, or
+                                       the workspace overlaps any buffer of the call */
 #define WTCONV_ERR_SCRATCH (-10)    /* wtconv_bwd_noalloc: the shape needs more workspace
                                        than WTCONV_NOALLOC_SCRATCH_BYTES */
 #define WTCONV_ERR_HIP (-100)       /* a kernel launch failed */

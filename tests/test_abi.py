@@ -160,6 +160,34 @@ def test_gradient_buffers_must_not_alias(lb, fused):
                                     None) == -9
 
 
+@pytest.mark.parametrize("call", ["fwd", "bwd_input", "bwd_weight", "bwd"])
+def test_workspace_must_not_alias(lb, call):
+    """The kernels write the workspace while they read the inputs and write
+    the outputs: a workspace that shares a byte with any buffer of the call is
+    refused before anything runs."""
+    s = good(lb, H=55, W=55)  # zero-extended planes: every call uses the workspace
+    need = lb.wtconv_workspace_size(s)
+    assert need > 0
+
+    def run(ws):
+        if call == "fwd":
+            return lb.lib.wtconv_fwd(ctypes.byref(s), X, *PARAMS, DX, ws, need, None)
+        if call == "bwd_input":
+            p = [PARAMS[0], PARAMS[2], PARAMS[3], PARAMS[4]]
+            return lb.lib.wtconv_bwd_input(ctypes.byref(s), DY, *p, DX, ws, need, None)
+        if call == "bwd_weight":
+            return lb.lib.wtconv_bwd_weight(ctypes.byref(s), X, DY, *PARAMS, *GRADS, ws, need,
+                                            None)
+        return lb.lib.wtconv_bwd(ctypes.byref(s), X, DY, *PARAMS, DX, *GRADS, ws, need, None)
+
+    bufs = {"fwd": [X, DX] + PARAMS, "bwd_input": [DY, DX, PARAMS[0]] + PARAMS[2:],
+            "bwd_weight": [X, DY] + PARAMS + GRADS, "bwd": [X, DY, DX] + PARAMS + GRADS}[call]
+    for b in bufs:
+        assert run(b) == -9, b
+        # a workspace that ends inside the buffer
+        assert run(ctypes.c_void_p(b.value - need + 16)) == -9, b
+
+
 def test_workspace_size_queries(lb):
     n = ctypes.c_size_t(7)
     huge = good(lb, H=32768, W=32768, L=4)  # 4 GiB planes: beyond 32-bit plane offsets
