@@ -3,12 +3,14 @@
 
 namespace wtc {
 
-// The ConvNeXt-T stage shapes.
+// The ConvNeXt-T stage shapes (the 7 x 7 planes of stage 4 run zero-extended
+// to 8 x 8).
 const PlaneVariant* plane_table_0(int* n) {
     static const PlaneVariant table[] = {
         WTC_PLANE_ROW(5, 2, 56, 56, 1, 256)
         WTC_PLANE_ROW(5, 2, 28, 28, 2, 256)
         WTC_PLANE_ROW(5, 1, 14, 14, 8, 256)
+        WTC_PLANE_ROW(5, 1, 8, 8, 16, 256)
         WTC_PLANE_ROW(5, 2, 32, 32, 1, 256)
     };
     *n = int(sizeof(table) / sizeof(table[0]));

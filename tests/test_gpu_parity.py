@@ -42,6 +42,7 @@ SMALL = [  # k, L, H, W: every small variant the library carries
     (1, 1, 8, 8), (3, 1, 8, 8), (3, 2, 16, 16), (3, 3, 16, 16), (5, 3, 16, 16),
     (7, 2, 16, 16), (7, 1, 14, 14), (3, 2, 16, 32), (5, 4, 32, 32), (3, 5, 32, 32),
     (5, 6, 64, 64), (5, 2, 32, 32), (5, 2, 28, 28), (5, 1, 14, 14), (5, 2, 56, 56),
+    (5, 1, 8, 8),
 ]
 
 
@@ -150,6 +151,8 @@ ANY_SIZE = [  # k, L, H, W, dtype: sides the kernels do not take directly
     (5, 2, 55, 55, "f32"),    # zero-extended to 56 x 56 (whole planes)
     (5, 2, 27, 27, "f16"),    # to 28 x 28, fp16
     (5, 1, 13, 13, "f32"),    # to 14 x 14
+    (5, 1, 7, 7, "f32"),      # ConvNeXt stage 4: to 8 x 8 (whole planes)
+    (5, 1, 7, 7, "f16"),
     (3, 3, 30, 17, "f32"),    # to 32 x 24, tiles
     (7, 2, 6, 10, "f32"),     # to 8 x 12, tiles
     (5, 3, 56, 56, "f32"),    # L = 3 at 56: divisible, tiles directly
@@ -160,6 +163,21 @@ ANY_SIZE = [  # k, L, H, W, dtype: sides the kernels do not take directly
     (5, 2, 1, 7, "f16"),      # one row: every level's grid one row high
     (7, 3, 3, 2, "f32"),      # a plane smaller than the kernel at every level
 ]
+
+
+@pytest.mark.parametrize("H,dtype", [(7, "f32"), (8, "f32"), (7, "f16")])
+def test_stage4_planes(H, dtype):
+    """ConvNeXt stage-4 planes (7 x 7, zero-extended to 8 x 8, and 8 x 8
+    directly) with more images than a group holds (16 planes per group) and a
+    ragged last group."""
+    B, C, k, L = 20, 6, 5, 1
+    d = wi.make_inputs(B, C, H, H, L, k, dtype, seed=400 + H)
+    g = torch.Generator().manual_seed(19)
+    td = d["x"].dtype
+    d["s_base"] = (1 + 0.5 * torch.randn(C, generator=g)).to(td)
+    d["s_wav"] = (0.3 + 0.5 * torch.randn(L, C, 4, generator=g)).to(td)
+    d["b_base"] = (0.5 * torch.randn(C, generator=g)).to(td)
+    assert_parity(d, dtype, "stage4 %dx%d %s" % (H, H, dtype))
 
 
 @pytest.mark.parametrize("k,L,H,W,dtype", ANY_SIZE)
