@@ -10,7 +10,7 @@ using Variant = PlaneVariant;
 
 const Variant* find_variant(const wtconv_shape& s) {
     const PlaneVariant* (*parts[])(int*) = {plane_table_0, plane_table_1, plane_table_2,
-                                            plane_table_3};
+                                            plane_table_3, plane_table_4, plane_table_5};
     for (auto part : parts) {
         int n = 0;
         const Variant* t = part(&n);

@@ -75,5 +75,7 @@ const PlaneVariant* plane_table_0(int* n);
 const PlaneVariant* plane_table_1(int* n);
 const PlaneVariant* plane_table_2(int* n);
 const PlaneVariant* plane_table_3(int* n);
+const PlaneVariant* plane_table_4(int* n);
+const PlaneVariant* plane_table_5(int* n);
 
 }  // namespace wtc

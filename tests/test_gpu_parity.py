@@ -42,7 +42,8 @@ SMALL = [  # k, L, H, W: every small variant the library carries
     (1, 1, 8, 8), (3, 1, 8, 8), (3, 2, 16, 16), (3, 3, 16, 16), (5, 3, 16, 16),
     (7, 2, 16, 16), (7, 1, 14, 14), (3, 2, 16, 32), (5, 4, 32, 32), (3, 5, 32, 32),
     (5, 6, 64, 64), (5, 2, 32, 32), (5, 2, 28, 28), (5, 1, 14, 14), (5, 2, 56, 56),
-    (5, 1, 8, 8),
+    (5, 1, 8, 8), (5, 1, 56, 56), (5, 3, 56, 56), (5, 1, 28, 28), (5, 3, 32, 32),
+    (5, 2, 16, 16), (5, 2, 8, 8), (5, 3, 8, 8),
 ]
 
 
