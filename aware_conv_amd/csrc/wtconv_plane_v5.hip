@@ -9,8 +9,8 @@ const PlaneVariant* plane_table_5(int* n) {
     static const PlaneVariant table[] = {
         WTC_PLANE_ROW(5, 3, 32, 32, 1, 256)
         WTC_PLANE_ROW(5, 2, 16, 16, 4, 256)
-        WTC_PLANE_ROW(5, 2, 8, 8, 16, 256)
-        WTC_PLANE_ROW(5, 3, 8, 8, 16, 256)
+        WTC_PLANE_ROW(5, 2, 8, 8, 8, 256)
+        WTC_PLANE_ROW(5, 3, 8, 8, 8, 256)
     };
     *n = int(sizeof(table) / sizeof(table[0]));
     return table;
