@@ -82,7 +82,8 @@ int dwconv_fwd(const dwconv_shape* d, const void* x, const void* w, const void* 
     if (overlap(x, y, act_bytes(s))) return WTCONV_ERR_ALIAS;
     if (!wtc::plane_supported(s)) return WTCONV_ERR_UNSUPPORTED;
     Params p{w, bias, nullptr, nullptr, nullptr};
-    return hip_status(wtc::plane_apply(s, x, p, y, false, static_cast<hipStream_t>(stream)));
+    return hip_status(wtc::plane_apply(s, x, p, y, false, static_cast<hipStream_t>(stream),
+                                       wtc::Rag{s.H, s.W}));
 }
 
 int dwconv_bwd(const dwconv_shape* d, const void* x, const void* dy, const void* w, void* dx,
@@ -107,7 +108,7 @@ int dwconv_bwd(const dwconv_shape* d, const void* x, const void* dy, const void*
     if (ws_bytes < need) return WTCONV_ERR_WORKSPACE;
     if (need > 0 && !workspace) return WTCONV_ERR_NULL;
     if (need > 0 && !aligned(workspace, 16)) return WTCONV_ERR_ALIGN;
-    return hip_status(wtc::plane_bwd(s, x, dy, p, dx, g, workspace, st));
+    return hip_status(wtc::plane_bwd(s, x, dy, p, dx, g, workspace, st, wtc::Rag{s.H, s.W}));
 }
 
 }  // extern "C"

@@ -120,12 +120,16 @@ int check_params(const wtconv_shape* s, const void* w_base, const void* b_base,
 
 // How a shape runs.  Two kernel families take a shape directly: whole planes
 // staged in LDS (the shapes this build instantiates), else output tiles of
-// large planes plus per-plane deep levels.  Any other shape runs on planes
-// zero-extended at their end (into the workspace), and its results are
-// cropped back.
+// large planes plus per-plane deep levels.  A shape whose sides, rounded up
+// to a multiple of 2^L, have whole-plane kernels runs on those kernels with
+// its planes read as corners of the larger ones (zero beyond) and its
+// results stored as corners (`rag`).  Any other shape runs on planes
+// zero-extended at their end in the workspace, and its results are cropped
+// back (`padded`).
 struct Plan {
     bool ok;
     bool padded;
+    bool rag;            // whole-plane kernels on corners of their planes
     bool plane;          // whole-plane kernels (else tiles)
     wtconv_shape run;    // the shape the kernels see
     size_t inner;        // workspace bytes of the kernels on `run`
@@ -169,13 +173,14 @@ Plan plan_for(const wtconv_shape* s) {
         if (wtc::plane_supported(a)) {
             pl.run = a;
             pl.plane = true;
+            pl.rag = true;
             pl.ok = true;
         } else if (direct(b, &plane)) {
             pl.run = b;
             pl.plane = plane;
+            pl.padded = true;
             pl.ok = true;
         }
-        pl.padded = pl.ok;
     }
     if (!pl.ok) return pl;
     pl.inner = pl.plane ? wtc::plane_workspace_bytes(pl.run) : wtc::tile_workspace_bytes(pl.run);
@@ -220,9 +225,14 @@ long planes_of(const wtconv_shape* s) { return long(s->B) * s->C; }
 
 int hip_status(hipError_t e) { return e == hipSuccess ? WTCONV_OK : WTCONV_ERR_HIP; }
 
-hipError_t run_apply(const Plan& pl, const void* in, const Params& p, void* out, bool flip,
-                     void* workspace, hipStream_t st) {
-    if (pl.plane) return wtc::plane_apply(pl.run, in, p, out, flip, st);
+// The stored planes of a call (the user's shape on `rag` plans).
+wtc::Rag stored(const Plan& pl, const wtconv_shape* s) {
+    return pl.rag ? wtc::Rag{s->H, s->W} : wtc::Rag{pl.run.H, pl.run.W};
+}
+
+hipError_t run_apply(const Plan& pl, const wtconv_shape* s, const void* in, const Params& p,
+                     void* out, bool flip, void* workspace, hipStream_t st) {
+    if (pl.plane) return wtc::plane_apply(pl.run, in, p, out, flip, st, stored(pl, s));
     return wtc::tile_apply(pl.run, in, p, out, flip, workspace, st);
 }
 
@@ -251,12 +261,12 @@ int apply(const wtconv_shape* s, const void* in, const void* w_base, const void*
     }
     Params p{w_base, b_base, s_base, w_wav, s_wav};
     hipStream_t st = static_cast<hipStream_t>(stream);
-    if (!pl.padded) return hip_status(run_apply(pl, in, p, out, flip, workspace, st));
+    if (!pl.padded) return hip_status(run_apply(pl, s, in, p, out, flip, workspace, st));
     const wtconv_shape& r = pl.run;
     void* xin = ext_buf(pl, workspace, 0);
     void* xout = ext_buf(pl, workspace, 1);
     hipError_t e = wtc::copy_planes(in, xin, planes_of(s), s->H, s->W, r.H, r.W, s->dtype, st);
-    if (e == hipSuccess) e = run_apply(pl, xin, p, xout, flip, workspace, st);
+    if (e == hipSuccess) e = run_apply(pl, s, xin, p, xout, flip, workspace, st);
     if (e == hipSuccess)
         e = wtc::copy_planes(xout, out, planes_of(s), r.H, r.W, s->H, s->W, s->dtype, st);
     return hip_status(e);
@@ -341,8 +351,8 @@ int backward(const wtconv_shape* s, const void* x, const void* dy, const void* w
         dxr = ext_buf(pl, workspace, 2);
     }
     if (pl.plane) {
-        err = fused ? wtc::plane_bwd(r, xr, dyr, p, dxr, g, workspace, st)
-                    : wtc::plane_bwd_weight(r, xr, dyr, p, g, workspace, st);
+        err = fused ? wtc::plane_bwd(r, xr, dyr, p, dxr, g, workspace, st, stored(pl, s))
+                    : wtc::plane_bwd_weight(r, xr, dyr, p, g, workspace, st, stored(pl, s));
     } else {
         // tiles of large planes: one pass over x and dy for both gradients,
         // or the weight taps alone

@@ -26,6 +26,15 @@ struct Grads {
     void* ds_wav;
 };
 
+// The planes as stored in device memory, when they are smaller than the
+// planes a whole-plane kernel computes on (Hs <= H, Ws <= W): the kernel
+// reads them as the top-left corner of its planes, zero elsewhere (each
+// plane zero-extended at its end), and stores only that corner of its
+// results.  Hs = H and Ws = W: the planes as they are.
+struct Rag {
+    int Hs, Ws;
+};
+
 // Whole-plane path: every (b, c) plane is staged in LDS in one piece.
 // Returns true if this build holds kernels for the shape.
 bool plane_supported(const wtconv_shape& s);
@@ -33,15 +42,17 @@ bool plane_supported(const wtconv_shape& s);
 size_t plane_workspace_bytes(const wtconv_shape& s);
 // flip = false: forward (y = op(x)); flip = true: input gradient
 // (dx = op^T(dy): 180-degree rotated kernels, no bias).
+// `rg`: the stored planes (see Rag; {s.H, s.W} for planes of the kernel's
+// own size).
 hipError_t plane_apply(const wtconv_shape& s, const void* in,
                        const Params& p, void* out, bool flip,
-                       hipStream_t stream);
+                       hipStream_t stream, Rag rg);
 hipError_t plane_bwd_weight(const wtconv_shape& s, const void* x,
                             const void* dy, const Params& p, const Grads& g,
-                            void* workspace, hipStream_t stream);
+                            void* workspace, hipStream_t stream, Rag rg);
 // Input gradient and parameter gradients in one pass over x and dy.
 hipError_t plane_bwd(const wtconv_shape& s, const void* x, const void* dy, const Params& p,
-                     void* dx, const Grads& g, void* workspace, hipStream_t stream);
+                     void* dx, const Grads& g, void* workspace, hipStream_t stream, Rag rg);
 // Zero parameter gradients (empty batch or empty planes).
 hipError_t zero_grads(const wtconv_shape& s, const Params& p, const Grads& g,
                       hipStream_t stream);

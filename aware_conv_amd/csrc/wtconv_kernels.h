@@ -459,18 +459,35 @@ __device__ __forceinline__ rsrc_t make_rsrc(const void* base, int bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, kBufFlags);
 }
 
-// Planes b0 .. b0+P-1 of channel c (those below B): base pointer and size.
+// Planes b0 .. b0+P-1 of channel c (those below B) of a tensor of HW-element
+// planes: base pointer and size.
 template <class G, typename T>
 struct GroupSpan {
     const T* base;
     int bytes;
-    __device__ GroupSpan(const T* src, int b0, int B, int C, int c) {
-        constexpr int HW = G::H * G::W;
+    __device__ GroupSpan(const T* src, int b0, int B, int C, int c, int HW = G::H * G::W) {
         const int nvalid = min(G::P, B - b0);
         base = src + (size_t(b0) * C + c) * HW;
         bytes = nvalid > 0 ? ((nvalid - 1) * C * HW + HW) * int(sizeof(T)) : 0;
     }
 };
+
+// One element through a buffer resource (offset past the resource: reads
+// zero, writes nothing).
+template <typename T>
+__device__ __forceinline__ T buf_load_elem(rsrc_t r, int off) {
+    if constexpr (std::is_same<T, float>::value)
+        return __int_as_float(int(__builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0)));
+    else
+        return __ushort_as_half(__builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0));
+}
+template <typename T>
+__device__ __forceinline__ void buf_store_elem(T v, rsrc_t r, int off) {
+    if constexpr (std::is_same<T, float>::value)
+        __builtin_amdgcn_raw_buffer_store_b32(unsigned(__float_as_int(v)), r, off, 0, 0);
+    else
+        __builtin_amdgcn_raw_buffer_store_b16(__half_as_ushort(v), r, off, 0, 0);
+}
 
 template <int BYTES>
 __device__ __forceinline__ typename std::conditional<
@@ -530,10 +547,16 @@ struct Fetch {
 
     // Whole planes: the loads of planes b0..b0+P-1 through a buffer
     // resource, with no branch (items past ITEMS and planes past B read
-    // zeros).
+    // zeros).  RAG: planes stored as Hs x Ws corners (Rag), read one element
+    // at a time, zero past the corner.
+    template <bool RAG = false>
     __device__ __forceinline__ void issue_buf(const T* __restrict__ src, int b0, int B, int C,
-                                              int c, int tid) {
+                                              int c, int tid, Rag rg = Rag{G::H, G::W}) {
         static_assert(G::HT == 0, "whole planes only");
+        if constexpr (RAG) {
+            issue_rag(src, b0, B, C, c, tid, rg);
+            return;
+        }
         const GroupSpan<G, T> g(src, b0, B, C, c);
         const rsrc_t rs = make_rsrc(g.base, g.bytes);
 #pragma unroll
@@ -548,6 +571,37 @@ struct Fetch {
 #pragma unroll
             for (int k = 0; k < ROWS; ++k)
                 r[it][k] = buf_load<V * int(sizeof(T))>(rs, off + (in ? k * G::W * int(sizeof(T)) : 0));
+        }
+    }
+
+    __device__ __forceinline__ void issue_rag(const T* __restrict__ src, int b0, int B, int C,
+                                              int c, int tid, Rag rg) {
+        const GroupSpan<G, T> g(src, b0, B, C, c, rg.Hs * rg.Ws);
+        const rsrc_t rs = make_rsrc(g.base, g.bytes);
+        constexpr int ES = int(sizeof(T));
+#pragma unroll
+        for (int it = 0; it < IT; ++it) {
+            const int item = tid + it * G::NT;
+            const int cv = item % NV;
+            const int rb = (item / NV) % RB;
+            const int pl = item / (NV * RB);
+            const bool in = ITEMS % G::NT == 0 || item < ITEMS;
+#pragma unroll
+            for (int k = 0; k < ROWS; ++k) {
+                const int rr = ROWS * rb + k;
+                union {
+                    raw_t raw;
+                    T e[V];
+                } u;
+#pragma unroll
+                for (int e = 0; e < V; ++e) {
+                    const int col = cv * V + e;
+                    const bool ok = in && rr < rg.Hs && col < rg.Ws;
+                    const int off = ok ? ((pl * C * rg.Hs + rr) * rg.Ws + col) * ES : kOutOfRange;
+                    u.e[e] = buf_load_elem<T>(rs, off);
+                }
+                r[it][k] = u.raw;
+            }
         }
     }
 
@@ -1027,6 +1081,45 @@ __device__ __forceinline__ void final_store(const float* lds, T* __restrict__ ou
     }
 }
 
+// final_store for whole planes stored as Hs x Ws corners (Rag): the same
+// synthesis, then one element at a time, only inside the corner.
+template <class G, typename T>
+__device__ __forceinline__ void final_store_rag(const float* lds, T* __restrict__ out, int b0,
+                                                int B, int C, int c, int tid, Rag rg) {
+    static_assert(G::HT == 0, "whole planes only");
+    constexpr int V = vec_elems<T>(G::W);
+    constexpr int NV = G::W / V, RP = G::H / 2, ITEMS = G::P * RP * NV;
+    constexpr int CW = V < 4 ? V : 4, NCH = V / CW;
+    constexpr int ES = int(sizeof(T));
+    const GroupSpan<G, T> g(out, b0, B, C, c, rg.Hs * rg.Ws);
+    const rsrc_t rs = make_rsrc(g.base, g.bytes);
+#pragma unroll
+    for (int it = 0; it < cdiv(ITEMS, G::NT); ++it) {
+        const int raw_item = tid + it * G::NT;
+        const bool in = ITEMS % G::NT == 0 || raw_item < ITEMS;
+        const int item = in ? raw_item : ITEMS - 1;
+        const int cv = item % NV;
+        const int i = (item / NV) % RP;
+        const int pl = item / (NV * RP);
+#pragma unroll
+        for (int ch = 0; ch < NCH; ++ch) {
+            float r0[CW], r1[CW];
+            synth_rows<G, CW>(lds, pl, i, cv * V + ch * CW, r0, r1);
+#pragma unroll
+            for (int e = 0; e < CW; ++e) {
+                const int col = cv * V + ch * CW + e;
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const int rr = 2 * i + h;
+                    const bool ok = in && rr < rg.Hs && col < rg.Ws;
+                    const int off = ok ? ((pl * C * rg.Hs + rr) * rg.Ws + col) * ES : kOutOfRange;
+                    buf_store_elem<T>(from_f<T>(h ? r1[e] : r0[e]), rs, off);
+                }
+            }
+        }
+    }
+}
+
 // Folded filters into LDS: [0, KK) base, then (l, s) blocks, then the bias.
 template <class G, typename T, bool FLIP>
 __device__ __forceinline__ void fold_weights(float* wf, const T* __restrict__ wb,
@@ -1096,12 +1189,12 @@ constexpr int apply_waves() {
     return w < cap ? w : cap;
 }
 
-template <int K, int L, int H, int W, int P, int NT, typename T, bool FLIP>
+template <int K, int L, int H, int W, int P, int NT, typename T, bool FLIP, bool RAG = false>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(
     apply_waves<K, L, H, W, P, NT, T>(), 8))) void k_plane_apply(
     const T* __restrict__ in, const T* __restrict__ wb, const T* __restrict__ bb,
     const T* __restrict__ sb, const T* __restrict__ ww, const T* __restrict__ sw,
-    T* __restrict__ out, int B, int C) {
+    T* __restrict__ out, int B, int C, Rag rg) {
     using G = Geo<K, L, H, W, P, NT>;
     using F = Fetch<G, T>;
     constexpr int KK = G::KK, Q = G::Q, R = G::R;
@@ -1113,7 +1206,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(
     const int q0 = int(total * blockIdx.x / gridDim.x);
     const int q1 = int(total * (blockIdx.x + 1) / gridDim.x);
     F fx;
-    if (q0 < q1) fx.issue_buf(in, (q0 % ngroups) * P, B, C, q0 / ngroups, tid);
+    if (q0 < q1) fx.template issue_buf<RAG>(in, (q0 % ngroups) * P, B, C, q0 / ngroups, tid, rg);
     for (int i = tid; i < G::side; i += NT) lds[i] = 0.f;
 
     const Job job = decode_job<G>(tid);
@@ -1150,7 +1243,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(
         float acc[Q][R];
         if (job.on) conv_tile<K, Q, R>(lds + win, pitch, w, init, acc);
         // the next group's loads fly during write-back, synthesis and store
-        if (q + 1 < q1) fx.issue_buf(in, ((q + 1) % ngroups) * P, B, C, (q + 1) / ngroups, tid);
+        if (q + 1 < q1) fx.template issue_buf<RAG>(in, ((q + 1) % ngroups) * P, B, C, (q + 1) / ngroups, tid, rg);
         __syncthreads();
         if (job.on) {
             if (full) {
@@ -1173,7 +1266,10 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(
             cascade_level<G, L - decltype(lc)::value>(lds, tid);
             __syncthreads();
         });
-        final_store<G, T>(lds, out, b0, B, C, c, tid);
+        if constexpr (RAG)
+            final_store_rag<G, T>(lds, out, b0, B, C, c, tid, rg);
+        else
+            final_store<G, T>(lds, out, b0, B, C, c, tid);
         __syncthreads();
     }
 }
@@ -1241,12 +1337,12 @@ __device__ __forceinline__ void reduce_row(float* lds, const float (&acc)[G::KK]
 // Weight-gradient partial sums of channel blockIdx.x % C over the groups of
 // chunk blockIdx.x / C: one row of G::NPART floats per workgroup,
 // [G_b (KK), sum dy, G[l][s] (4 L KK)].
-template <int K, int L, int H, int W, int P, int NT, typename T>
+template <int K, int L, int H, int W, int P, int NT, typename T, bool RAG = false>
 __global__ __launch_bounds__(NT) void k_plane_bww(
     const T* __restrict__ x,
                                                   const T* __restrict__ dy,
                                                   float* __restrict__ part, int B, int C,
-                                                  int gpw) {
+                                                  int gpw, Rag rg) {
     using G = GeoGrad<K, L, H, W, P, NT>;
     constexpr int KK = G::KK, Q = G::Q, R = G::R;
     extern __shared__ float lds[];
@@ -1258,8 +1354,8 @@ __global__ __launch_bounds__(NT) void k_plane_bww(
     const int g1 = min(g0 + gpw, ngroups);
     Fetch<G, T> fx, fd;
     if (g0 < g1) {
-        fx.issue_buf(x, g0 * P, B, C, c, tid);
-        fd.issue_buf(dy, g0 * P, B, C, c, tid);
+        fx.template issue_buf<RAG>(x, g0 * P, B, C, c, tid, rg);
+        fd.template issue_buf<RAG>(dy, g0 * P, B, C, c, tid, rg);
     }
     for (int i = tid; i < G::side + G::vside; i += NT) lds[i] = 0.f;
     __syncthreads();
@@ -1292,8 +1388,8 @@ __global__ __launch_bounds__(NT) void k_plane_bww(
         fx.template commit<true, false>(lds, tid);
         fd.template commit<false, true>(lds, tid);
         if (g + 1 < g1) {
-            fx.issue_buf(x, b0 + P, B, C, c, tid);
-            fd.issue_buf(dy, b0 + P, B, C, c, tid);
+            fx.template issue_buf<RAG>(x, b0 + P, B, C, c, tid, rg);
+            fd.template issue_buf<RAG>(dy, b0 + P, B, C, c, tid, rg);
         }
         __syncthreads();
         static_for<Fetch<G, T>::LEVELS + 1, L + 1>([&](auto lc) {
@@ -1305,17 +1401,20 @@ __global__ __launch_bounds__(NT) void k_plane_bww(
             float d[Q][R];
             if (job.lvl == 0) {
                 // base taps: dy straight from HBM (the tile's own pixels)
-                // addresses are clamped into the tensor; padding reads as 0
+                // addresses are clamped into the tensor; padding, and with
+                // RAG the part of the plane beyond the stored corner, reads as 0
+                const int Hs = RAG ? rg.Hs : H, Ws = RAG ? rg.Ws : W;
                 const int b = b0 + job.pl;
-                const T* dp = dy + (size_t(min(b, B - 1)) * C + c) * H * W;
+                const T* dp = dy + (size_t(min(b, B - 1)) * C + c) * Hs * Ws;
 #pragma unroll
                 for (int q = 0; q < Q; ++q)
 #pragma unroll
                     for (int j = 0; j < R; ++j) {
-                        const bool ok = b < B && q < nrows && j < ncols;
-                        const int yy = min(job.grp * Q + q, H - 1);
-                        const int xx = min(job.strip * R + j, W - 1);
-                        const float v = to_f(dp[yy * W + xx]);
+                        const int row = job.grp * Q + q, col = job.strip * R + j;
+                        const bool ok = b < B && q < nrows && j < ncols && row < Hs && col < Ws;
+                        const int yy = min(row, Hs - 1);
+                        const int xx = min(col, Ws - 1);
+                        const float v = to_f(dp[yy * Ws + xx]);
                         d[q][j] = ok ? v : 0.f;
                     }
                 sdy += tile_sum<Q, R>(d);
@@ -1375,11 +1474,11 @@ struct LinearRows {
 // loop carries none of that.
 // Two workgroups per compute unit fit its LDS at the stage shapes: the
 // register budget is held to that occupancy.
-template <int K, int L, int H, int W, int P, int NT, typename T, bool CROSS>
+template <int K, int L, int H, int W, int P, int NT, typename T, bool CROSS, bool RAG = false>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void k_plane_bwd(
     const T* __restrict__ x, const T* __restrict__ dy, const T* __restrict__ wb,
     const T* __restrict__ sb, const T* __restrict__ ww, const T* __restrict__ sw,
-    T* __restrict__ dx, float* __restrict__ part, int B, int C, LinearRows rows) {
+    T* __restrict__ dx, float* __restrict__ part, int B, int C, LinearRows rows, Rag rg) {
     using G = GeoGrad<K, L, H, W, P, NT>;
     using F = Fetch<G, T>;
     constexpr int KK = G::KK, Q = G::Q, R = G::R, DY = bwd_dy_base<G>();
@@ -1400,8 +1499,8 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void k_
     int c = int(q0 / ngroups), grp = int(q0 % ngroups);
     F fx, fd;
     if (nitems > 0) {
-        fx.issue_buf(x, grp * P, B, C, c, tid);
-        fd.issue_buf(dy, grp * P, B, C, c, tid);
+        fx.template issue_buf<RAG>(x, grp * P, B, C, c, tid, rg);
+        fd.template issue_buf<RAG>(dy, grp * P, B, C, c, tid, rg);
     }
     for (int i = tid; i < DY + G::side; i += NT) lds[i] = 0.f;
 
@@ -1483,8 +1582,8 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void k_
         const bool wrap = grp + 1 == ngroups;
         const int cn = wrap ? c + 1 : c, gn = wrap ? 0 : grp + 1;
         if (it + 1 < nitems) {
-            fx.issue_buf(x, gn * P, B, C, cn, tid);
-            fd.issue_buf(dy, gn * P, B, C, cn, tid);
+            fx.template issue_buf<RAG>(x, gn * P, B, C, cn, tid, rg);
+            fd.template issue_buf<RAG>(dy, gn * P, B, C, cn, tid, rg);
         }
         __syncthreads();
         if (job.on) {
@@ -1506,7 +1605,10 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void k_
             cascade_level<G, L - decltype(lc)::value>(ldy, tid);
             __syncthreads();
         });
-        final_store<G, T>(ldy, dx, b0, B, C, c, tid);
+        if constexpr (RAG)
+            final_store_rag<G, T>(ldy, dx, b0, B, C, c, tid, rg);
+        else
+            final_store<G, T>(ldy, dx, b0, B, C, c, tid);
         c = cn;
         grp = gn;
         __syncthreads();
@@ -1546,12 +1648,13 @@ constexpr int bwd1_waves() {
 // SIMD the LDS allows, at most three.  Without DX the kernel is the weight
 // gradient alone (wtconv_bwd_weight): no conv, no input gradient, `dx` and
 // the filters unread.
-template <int K, int L, int H, int W, int P, int NT, typename T, bool CROSS, bool DX = true>
+template <int K, int L, int H, int W, int P, int NT, typename T, bool CROSS, bool DX = true,
+          bool RAG = false>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(
     bwd1_waves<Geo<K, L, H, W, P, NT>>()))) void k_plane_bwd1(
     const T* __restrict__ x, const T* __restrict__ dy, const T* __restrict__ wb,
     const T* __restrict__ sb, const T* __restrict__ ww, const T* __restrict__ sw,
-    T* __restrict__ dx, float* __restrict__ part, int B, int C, LinearRows rows) {
+    T* __restrict__ dx, float* __restrict__ part, int B, int C, LinearRows rows, Rag rg) {
     using G = Geo<K, L, H, W, P, NT>;
     using F = Fetch<G, T>;
     constexpr int KK = G::KK, Q = G::Q, R = G::R;
@@ -1564,8 +1667,8 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(
     int c = int(q0 / ngroups), grp = int(q0 % ngroups);
     F fx, fd;
     if (nitems > 0) {
-        fx.issue_buf(x, grp * P, B, C, c, tid);
-        fd.issue_buf(dy, grp * P, B, C, c, tid);
+        fx.template issue_buf<RAG>(x, grp * P, B, C, c, tid, rg);
+        fd.template issue_buf<RAG>(dy, grp * P, B, C, c, tid, rg);
     }
     for (int i = tid; i < G::side; i += NT) lds[i] = 0.f;
 
@@ -1665,8 +1768,8 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(
         asm volatile("" : "+v"(t));
         {
             const bool more = it + 1 < nitems;
-            fx.issue_buf(x, more ? gn * P : B, B, C, more ? cn : c, t);
-            fd.issue_buf(dy, more ? gn * P : B, B, C, more ? cn : c, t);
+            fx.template issue_buf<RAG>(x, more ? gn * P : B, B, C, more ? cn : c, t, rg);
+            fd.template issue_buf<RAG>(dy, more ? gn * P : B, B, C, more ? cn : c, t, rg);
         }
         __syncthreads();
         if constexpr (DX) {
@@ -1689,7 +1792,10 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(
                 cascade_level<G, L - decltype(lc)::value>(lds, t);
                 __syncthreads();
             });
-            final_store<G, T>(lds, dx, b0, B, C, c, t);
+            if constexpr (RAG)
+                final_store_rag<G, T>(lds, dx, b0, B, C, c, t, rg);
+            else
+                final_store<G, T>(lds, dx, b0, B, C, c, t);
             __syncthreads();
         }
         c = cn;

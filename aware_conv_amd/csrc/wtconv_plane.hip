@@ -38,6 +38,11 @@ int bww_chunks(const wtconv_shape& s, int P, int slots) {
     return cdiv(ngroups, gpw);
 }
 
+// The kernel set for planes stored as `rg`.
+const PlaneKernels& kernels_for(const Variant* v, Rag rg) {
+    return (rg.Hs == v->H && rg.Ws == v->W) ? v->full : v->rag;
+}
+
 }  // namespace
 
 bool plane_supported(const wtconv_shape& s) {
@@ -76,10 +81,11 @@ size_t plane_workspace_bytes(const wtconv_shape& s) {
 }
 
 hipError_t plane_apply(const wtconv_shape& s, const void* in, const Params& p, void* out,
-                       bool flip, hipStream_t stream) {
+                       bool flip, hipStream_t stream, Rag rg) {
     const Variant* v = find_variant(s);
     if (!v) return hipErrorInvalidValue;
-    const void* fn = flip ? v->bwi : v->fwd;
+    const PlaneKernels& ks = kernels_for(v, rg);
+    const void* fn = flip ? ks.bwi : ks.fwd;
     hipError_t e = prepare(fn, v->lds_apply);
     if (e != hipSuccess) return e;
     int B = s.B, C = s.C;
@@ -91,7 +97,7 @@ hipError_t plane_apply(const wtconv_shape& s, const void* in, const Params& p, v
     const void* sb = p.s_base;
     const void* ww = p.w_wav;
     const void* sw = p.s_wav;
-    void* args[] = {&in, &wb, &bb, &sb, &ww, &sw, &out, &B, &C};
+    void* args[] = {&in, &wb, &bb, &sb, &ww, &sw, &out, &B, &C, &rg};
     e = hipLaunchKernel(fn, dim3(unsigned(nwg)), dim3(v->NT), args, v->lds_apply, stream);
     if (e != hipSuccess) return e;
     return hipGetLastError();
@@ -126,7 +132,8 @@ namespace {
 // (channel, group) items, then the finalize over each channel's rows.
 hipError_t launch_linear(const wtconv_shape& s, const Variant* v, const void* fn_one,
                          const void* fn_cross, const void* x, const void* dy, const Params& p,
-                         void* dx, const Grads& g, void* workspace, hipStream_t stream) {
+                         void* dx, const Grads& g, void* workspace, hipStream_t stream,
+                         Rag rg) {
     hipError_t e = prepare(fn_one, v->lds_bwd);
     if (e != hipSuccess) return e;
     const int ngroups = cdiv(s.B, v->P);
@@ -156,7 +163,7 @@ hipError_t launch_linear(const wtconv_shape& s, const Variant* v, const void* fn
     const void* sb = p.s_base;
     const void* ww = p.w_wav;
     const void* sw = p.s_wav;
-    void* args[] = {&x, &dy, &wb, &sb, &ww, &sw, &dx, &part, &B, &C, &rows};
+    void* args[] = {&x, &dy, &wb, &sb, &ww, &sw, &dx, &part, &B, &C, &rows, &rg};
     const void* fn = cross ? fn_cross : fn_one;
     if (cross && (e = prepare(fn, v->lds_bwd)) != hipSuccess) return e;
     e = hipLaunchKernel(fn, dim3(unsigned(nwg)), dim3(v->NT), args, v->lds_bwd, stream);
@@ -169,20 +176,21 @@ hipError_t launch_linear(const wtconv_shape& s, const Variant* v, const void* fn
 
 hipError_t plane_bwd_weight(const wtconv_shape& s, const void* x, const void* dy,
                             const Params& p, const Grads& g, void* workspace,
-                            hipStream_t stream) {
+                            hipStream_t stream, Rag rg) {
     const Variant* v = find_variant(s);
     if (!v) return hipErrorInvalidValue;
+    const PlaneKernels& ks = kernels_for(v, rg);
     // shapes with the one-side fused backward take its weight-only form
-    if (v->bww1)
-        return launch_linear(s, v, v->bww1, v->bww1_cross, x, dy, p, nullptr, g, workspace,
-                             stream);
-    hipError_t e = prepare(v->bww, v->lds_bww);
+    if (ks.bww1)
+        return launch_linear(s, v, ks.bww1, ks.bww1_cross, x, dy, p, nullptr, g, workspace,
+                             stream, rg);
+    hipError_t e = prepare(ks.bww, v->lds_bww);
     if (e != hipSuccess) return e;
-    const int nchunk = bww_chunks(s, v->P, resident_wgs(v->bww, v->NT, v->lds_bww));
+    const int nchunk = bww_chunks(s, v->P, resident_wgs(ks.bww, v->NT, v->lds_bww));
     int gpw = cdiv(cdiv(s.B, v->P), nchunk), B = s.B, C = s.C;
     float* part = static_cast<float*>(workspace);
-    void* args[] = {&x, &dy, &part, &B, &C, &gpw};
-    e = hipLaunchKernel(v->bww, dim3(unsigned(nchunk) * unsigned(s.C)), dim3(v->NT), args,
+    void* args[] = {&x, &dy, &part, &B, &C, &gpw, &rg};
+    e = hipLaunchKernel(ks.bww, dim3(unsigned(nchunk) * unsigned(s.C)), dim3(v->NT), args,
                         v->lds_bww, stream);
     if (e == hipSuccess) e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -190,15 +198,16 @@ hipError_t plane_bwd_weight(const wtconv_shape& s, const void* x, const void* dy
 }
 
 hipError_t plane_bwd(const wtconv_shape& s, const void* x, const void* dy, const Params& p,
-                     void* dx, const Grads& g, void* workspace, hipStream_t stream) {
+                     void* dx, const Grads& g, void* workspace, hipStream_t stream, Rag rg) {
     const Variant* v = find_variant(s);
     if (!v) return hipErrorInvalidValue;
-    if (!v->bwd) {
-        hipError_t e = plane_apply(s, dy, p, dx, true, stream);
+    const PlaneKernels& ks = kernels_for(v, rg);
+    if (!ks.bwd) {
+        hipError_t e = plane_apply(s, dy, p, dx, true, stream, rg);
         if (e != hipSuccess) return e;
-        return plane_bwd_weight(s, x, dy, p, g, workspace, stream);
+        return plane_bwd_weight(s, x, dy, p, g, workspace, stream, rg);
     }
-    return launch_linear(s, v, v->bwd, v->bwd_cross, x, dy, p, dx, g, workspace, stream);
+    return launch_linear(s, v, ks.bwd, ks.bwd_cross, x, dy, p, dx, g, workspace, stream, rg);
 }
 
 hipError_t zero_grads(const wtconv_shape& s, const Params& p, const Grads& g,

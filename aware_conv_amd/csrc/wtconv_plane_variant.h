@@ -7,8 +7,9 @@
 
 namespace wtc {
 
-struct PlaneVariant {
-    int K, L, H, W, dtype, P, NT;
+// The kernels of one shape, for planes stored at that shape or (`rag`) as
+// smaller corners of it (Rag).
+struct PlaneKernels {
     const void* fwd;
     const void* bwi;
     const void* bww;
@@ -16,6 +17,11 @@ struct PlaneVariant {
     const void* bwd_cross;  // the same, for ranges that span channels
     const void* bww1;       // weight gradient alone on the one-side kernel, or NULL
     const void* bww1_cross;
+};
+
+struct PlaneVariant {
+    int K, L, H, W, dtype, P, NT;
+    PlaneKernels full, rag;
     size_t lds_apply, lds_bww, lds_bwd;
 };
 
@@ -37,33 +43,41 @@ constexpr bool bwd_one_side() {
     return (L == 0 || G::Q * G::R >= 20) && dev::bwd1_lds_bytes<G>() <= kPlaneMaxLds;
 }
 
+template <int K, int L, int H, int W, int P, int NT, typename T, bool RAG>
+PlaneKernels make_plane_kernels() {
+    using namespace dev;
+    using G = Geo<K, L, H, W, P, NT>;
+    using GG = GeoGrad<K, L, H, W, P, NT>;
+    constexpr bool one_side = bwd_one_side<K, L, H, W, P, NT>();
+    constexpr size_t ld = one_side ? bwd1_lds_bytes<G>() : bwd_lds_bytes<GG>();
+    auto fn = [](auto f) { return reinterpret_cast<const void*>(f); };
+    PlaneKernels k{fn(&k_plane_apply<K, L, H, W, P, NT, T, false, RAG>),
+                   fn(&k_plane_apply<K, L, H, W, P, NT, T, true, RAG>),
+                   fn(&k_plane_bww<K, L, H, W, P, NT, T, RAG>),
+                   nullptr, nullptr, nullptr, nullptr};
+    if constexpr (one_side) {
+        k.bwd = fn(&k_plane_bwd1<K, L, H, W, P, NT, T, false, true, RAG>);
+        k.bwd_cross = fn(&k_plane_bwd1<K, L, H, W, P, NT, T, true, true, RAG>);
+        k.bww1 = fn(&k_plane_bwd1<K, L, H, W, P, NT, T, false, false, RAG>);
+        k.bww1_cross = fn(&k_plane_bwd1<K, L, H, W, P, NT, T, true, false, RAG>);
+    } else if constexpr (ld <= kPlaneMaxLds) {
+        k.bwd = fn(&k_plane_bwd<K, L, H, W, P, NT, T, false, RAG>);
+        k.bwd_cross = fn(&k_plane_bwd<K, L, H, W, P, NT, T, true, RAG>);
+    }
+    return k;
+}
+
 template <int K, int L, int H, int W, int P, int NT, typename T>
 PlaneVariant make_plane_variant(int dtype) {
     using namespace dev;
     using G = Geo<K, L, H, W, P, NT>;
     using GG = GeoGrad<K, L, H, W, P, NT>;
-    const size_t la = apply_lds_bytes<G>();
-    const size_t lb = bww_lds_bytes<GG>();
     constexpr bool one_side = bwd_one_side<K, L, H, W, P, NT>();
     constexpr size_t ld = one_side ? bwd1_lds_bytes<G>() : bwd_lds_bytes<GG>();
-    const void* fused = nullptr;
-    const void* fused_cross = nullptr;
-    const void* wonly = nullptr;
-    const void* wonly_cross = nullptr;
-    if constexpr (one_side) {
-        fused = reinterpret_cast<const void*>(&k_plane_bwd1<K, L, H, W, P, NT, T, false>);
-        fused_cross = reinterpret_cast<const void*>(&k_plane_bwd1<K, L, H, W, P, NT, T, true>);
-        wonly = reinterpret_cast<const void*>(&k_plane_bwd1<K, L, H, W, P, NT, T, false, false>);
-        wonly_cross = reinterpret_cast<const void*>(&k_plane_bwd1<K, L, H, W, P, NT, T, true, false>);
-    } else if constexpr (ld <= kPlaneMaxLds) {
-        fused = reinterpret_cast<const void*>(&k_plane_bwd<K, L, H, W, P, NT, T, false>);
-        fused_cross = reinterpret_cast<const void*>(&k_plane_bwd<K, L, H, W, P, NT, T, true>);
-    }
     return PlaneVariant{K, L, H, W, dtype, P, NT,
-                        reinterpret_cast<const void*>(&k_plane_apply<K, L, H, W, P, NT, T, false>),
-                        reinterpret_cast<const void*>(&k_plane_apply<K, L, H, W, P, NT, T, true>),
-                        reinterpret_cast<const void*>(&k_plane_bww<K, L, H, W, P, NT, T>),
-                        fused, fused_cross, wonly, wonly_cross, la, lb, ld};
+                        make_plane_kernels<K, L, H, W, P, NT, T, false>(),
+                        make_plane_kernels<K, L, H, W, P, NT, T, true>(),
+                        apply_lds_bytes<G>(), bww_lds_bytes<GG>(), ld};
 }
 
 // Rows (K, L, H, W, planes per group, threads), both dtypes each.

@@ -31,8 +31,11 @@
  * appended at its end before its analysis, as the stride-2 'SAME' Haar
  * convolutions of the cybasar.com tutorial (section 3) do, and the synthesis
  * crops back to that grid.  The library runs such shapes on planes
- * zero-extended at their end to a multiple of 2^L (in the workspace) and
- * crops the results, which is the same operator.
+ * zero-extended at their end to a multiple of 2^L and crops the results,
+ * which is the same operator: the whole-plane kernels read each stored plane
+ * as the corner of the extended one (zeros beyond it) and write only that
+ * corner back; the tile kernels run on zero-extended copies in the
+ * workspace.
  *
  * Tensors (all contiguous, row-major, device memory, element type `dtype`):
  *   x, y, dy, dx : [B][C][H][W]
@@ -111,7 +114,7 @@ int wtconv_workspace_size(const wtconv_shape* s, size_t* bytes);
  * with more than three levels use the workspace for the deeper levels (the
  * 8 x 8 box sums of the input, their contribution, and for the largest
  * planes their Haar levels: a few 1/64 of the input), and shapes run on
- * zero-extended planes keep those planes there; pass wtconv_workspace_size()
+ * zero-extended tiled planes keep those planes there; pass wtconv_workspace_size()
  * bytes, or NULL when it reported 0.
  */
 int wtconv_fwd(const wtconv_shape* s, const void* x, const void* w_base,

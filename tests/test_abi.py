@@ -66,18 +66,24 @@ def good(lb, **kw):
     (dict(B=-1), -2), (dict(H=-56), -2), (dict(H=1 << 25), -2),
     (dict(L=0), -4), (dict(L=7), -4), (dict(k=4), -3), (dict(k=9), -3), (dict(k=0), -3),
     (dict(dtype=2), -5),
-    # sides that are not multiples of 2^L run on zero-extended planes in the
-    # workspace: without one the call is refused
-    (dict(H=54), -7), (dict(W=58), -7), (dict(H=55, W=55), -7),
+    # sides that round up (to a multiple of 2^L) to no whole-plane shape run
+    # on zero-extended planes in the workspace: without one the call is
+    # refused
+    (dict(H=58), -7), (dict(W=58), -7), (dict(H=59, W=59), -7),
 ])
 def test_shape_errors(lb, kw, code):
     assert fwd(lb, good(lb, **kw)) == code
 
 
 def test_odd_sides_need_room_for_extended_planes(lb):
-    # 55 x 55 at L = 2 runs on 56 x 56 planes: three of them plus the partials
+    # 55 x 55 at L = 2 runs on the 56 x 56 whole-plane kernels, reading and
+    # writing its planes as corners: the partial rows of 56 x 56, nothing more
     s55, s56 = good(lb, H=55, W=55), good(lb, H=56, W=56)
-    assert lb.wtconv_workspace_size(s55) >= 3 * 2 * 8 * 56 * 56 * 4 + lb.wtconv_workspace_size(s56)
+    assert lb.wtconv_workspace_size(s55) == lb.wtconv_workspace_size(s56)
+    # 58 x 58 rounds up to 60 x 60, which only the tiles take: three extended
+    # planes and the tiles' partial rows
+    s58, s60 = good(lb, H=58, W=58), good(lb, H=60, W=60)
+    assert lb.wtconv_workspace_size(s58) >= 3 * 2 * 8 * 60 * 60 * 4 + lb.wtconv_workspace_size(s60)
 
 
 def test_null_and_alignment_errors(lb):
@@ -165,7 +171,7 @@ def test_workspace_must_not_alias(lb, call):
     """The kernels write the workspace while they read the inputs and write
     the outputs: a workspace that shares a byte with any buffer of the call is
     refused before anything runs."""
-    s = good(lb, H=55, W=55)  # zero-extended planes: every call uses the workspace
+    s = good(lb, H=58, W=58)  # zero-extended planes: every call uses the workspace
     need = lb.wtconv_workspace_size(s)
     assert need > 0
 

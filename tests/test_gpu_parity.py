@@ -149,10 +149,10 @@ def test_deep_levels_through_device_memory(B, C, k, L, H, W, dtype):
 
 
 ANY_SIZE = [  # k, L, H, W, dtype: sides the kernels do not take directly
-    (5, 2, 55, 55, "f32"),    # zero-extended to 56 x 56 (whole planes)
-    (5, 2, 27, 27, "f16"),    # to 28 x 28, fp16
-    (5, 1, 13, 13, "f32"),    # to 14 x 14
-    (5, 1, 7, 7, "f32"),      # ConvNeXt stage 4: to 8 x 8 (whole planes)
+    (5, 2, 55, 55, "f32"),    # corners of 56 x 56 whole planes
+    (5, 2, 27, 27, "f16"),    # of 28 x 28, fp16
+    (5, 1, 13, 13, "f32"),    # of 14 x 14
+    (5, 1, 7, 7, "f32"),      # ConvNeXt stage 4: of 8 x 8
     (5, 1, 7, 7, "f16"),
     (3, 3, 30, 17, "f32"),    # to 32 x 24, tiles
     (7, 2, 6, 10, "f32"),     # to 8 x 12, tiles
@@ -168,8 +168,8 @@ ANY_SIZE = [  # k, L, H, W, dtype: sides the kernels do not take directly
 
 @pytest.mark.parametrize("H,dtype", [(7, "f32"), (8, "f32"), (7, "f16")])
 def test_stage4_planes(H, dtype):
-    """ConvNeXt stage-4 planes (7 x 7, zero-extended to 8 x 8, and 8 x 8
-    directly) with more images than a group holds (16 planes per group) and a
+    """ConvNeXt stage-4 planes (7 x 7, read and written as corners of 8 x 8
+    planes, and 8 x 8 directly) with more images than a group holds (16 planes per group) and a
     ragged last group."""
     B, C, k, L = 20, 6, 5, 1
     d = wi.make_inputs(B, C, H, H, L, k, dtype, seed=400 + H)
@@ -184,7 +184,8 @@ def test_stage4_planes(H, dtype):
 @pytest.mark.parametrize("k,L,H,W,dtype", ANY_SIZE)
 def test_any_size(k, L, H, W, dtype):
     """Odd grids at some level: the oracle pads every level's grid on its own;
-    the library zero-extends the planes once and crops."""
+    the library runs zero-extended planes and crops (whole-plane kernels
+    read and write the stored corners; tiles run on extended copies)."""
     B, C = 3, 4
     d = wi.make_inputs(B, C, H, W, L, k, dtype, seed=k * 31 + L * 7 + H * 3 + W)
     g = torch.Generator().manual_seed(13)

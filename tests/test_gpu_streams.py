@@ -28,7 +28,8 @@ def run(d):
     (4, 16, 56, 56, 2, 5),      # whole planes
     (2, 3, 128, 192, 4, 5),     # tiles and per-plane deep levels
     (1, 2, 768, 768, 6, 3),     # tiles and deep levels through device memory
-    (3, 4, 55, 41, 2, 3),       # zero-extended planes
+    (3, 4, 55, 41, 2, 3),       # zero-extended tiled planes in the workspace
+    (4, 16, 55, 55, 2, 5),      # corners of whole planes
 ])
 def test_two_streams_match_sequential_calls(B, C, H, W, L, k):
     dev = torch.device("cuda")

@@ -47,9 +47,9 @@ def noalloc_matches_bwd(case):
     # tiles with deep levels (box sums, deep contribution, partial rows in the
     # scratch), then a smaller tile shape, fp16
     [(2, 6, 512, 512, 5, 5, "f32"), (1, 3, 128, 96, 4, 3, "f16")],
-    # zero-extended planes (the extended tensors in the scratch), then a
-    # smaller whole-plane shape
-    [(4, 8, 55, 55, 2, 5, "f32"), (2, 4, 14, 14, 1, 5, "f16")],
+    # zero-extended tiled planes (the extended tensors in the scratch), then
+    # a smaller shape read as corners of whole planes
+    [(4, 8, 58, 58, 2, 5, "f32"), (2, 4, 13, 13, 1, 5, "f16")],
 ])
 def test_noalloc_twice_second_smaller(cases):
     for case in cases:
@@ -58,9 +58,9 @@ def test_noalloc_twice_second_smaller(cases):
 
 def test_noalloc_refuses_shapes_beyond_its_scratch():
     L = lib()
-    # 55 x 55 planes run zero-extended to 56 x 56: three extended tensors of
-    # 32 x 96 x 56 x 56 floats (37 MiB each) in the workspace
-    d = inputs(32, 96, 55, 55, 2, 5, "f32", seed=3)
+    # 58 x 58 planes run on tiles, zero-extended to 60 x 60: three extended
+    # tensors of 32 x 96 x 60 x 60 floats (42 MiB each) in the workspace
+    d = inputs(32, 96, 58, 58, 2, 5, "f32", seed=3)
     assert L.wtconv_workspace_size(L.shape_of(d["x"], d["w_wav"])) > 64 << 20
     p = [d[n] for n in PARAMS]
     dx = torch.empty_like(d["x"])
