@@ -96,22 +96,42 @@ def source_hash():
     return h.hexdigest()[:16]
 
 
+def template_args(kernel_name):
+    """The template arguments of a demangled kernel name, as strings."""
+    head = kernel_name.split("(")[0]
+    if "<" not in head:
+        return []
+    inner = head[head.index("<") + 1:head.rindex(">")]
+    return [a.strip() for a in inner.split(",")]
+
+
+# Position of the FLIP argument (input gradient) of the apply kernels:
+# k_plane_apply<K, L, H, W, P, NT, T, FLIP, RAG>, k_tile_apply<K, LT, TH, TW,
+# NT, T, FLIP>, k_deep_apply<T, K, FLIP>; and of DX (input gradient computed)
+# of k_plane_bwd1<K, L, H, W, P, NT, T, CROSS, DX, RAG>.
+_FLIP_ARG = {"k_plane_apply": 7, "k_tile_apply": 6, "k_deep_apply": 2}
+_BWD1_DX_ARG = 8
+
+
+def _kernel(kernel_name):
+    head = kernel_name.split("(")[0].split("<")[0]
+    return head.split("::")[-1].split(" ")[-1]
+
+
 def call_of(kernel_name, fused):
     """Entry point a profiled kernel belongs to, or None."""
-    n = kernel_name
+    k = _kernel(kernel_name)
+    args = template_args(kernel_name)
     c = None
-    if "k_plane_apply" in n or "k_tile_apply" in n or "k_deep_apply" in n:
-        # template argument FLIP: ..., false> forward, ..., true> input gradient
-        head = n.split("(")[0]
-        c = "wtconv_bwd_input" if head.rstrip("> ").endswith("true") else "wtconv_fwd"
-    elif "k_plane_bww" in n or "k_tile_bww" in n or "k_deep_bww" in n or "k_bww_final" in n:
+    if k in _FLIP_ARG:
+        flip = args[_FLIP_ARG[k]] == "true"
+        c = "wtconv_bwd_input" if flip else "wtconv_fwd"
+    elif k in ("k_plane_bww", "k_tile_bww", "k_deep_bww", "k_bww_final"):
         c = "wtconv_bwd_weight"
-    elif "k_plane_bwd1" in n and n.split("(")[0].rstrip("> ").endswith("false") and \
-            n.split("(")[0].count(",") == 8:
-        # the one-side backward's last template argument DX: false is the
-        # weight gradient alone
-        c = "wtconv_bwd_weight"
-    elif "k_plane_bwd" in n or "k_tile_bwd" in n:
+    elif k == "k_plane_bwd1":
+        # DX false: the weight gradient alone
+        c = "wtconv_bwd" if args[_BWD1_DX_ARG] == "true" else "wtconv_bwd_weight"
+    elif k.startswith("k_plane_bwd") or k.startswith("k_tile_bwd"):
         c = "wtconv_bwd"
     if fused and c in ("wtconv_bwd_input", "wtconv_bwd_weight"):
         c = "wtconv_bwd"
@@ -120,9 +140,9 @@ def call_of(kernel_name, fused):
 
 def is_step_marker(kernel_name):
     """The forward's main kernel: launched exactly once per step."""
-    head = kernel_name.split("(")[0]
-    return (("k_plane_apply" in head or "k_tile_apply" in head) and
-            head.rstrip("> ").endswith("false"))
+    k = _kernel(kernel_name)
+    return k in ("k_plane_apply", "k_tile_apply") and \
+        template_args(kernel_name)[_FLIP_ARG[k]] == "false"
 
 
 def summarize_traffic(fetch_dir, write_dir, wl, act_bytes, fused):

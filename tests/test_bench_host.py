@@ -13,18 +13,23 @@ import bench  # noqa: E402
 
 
 @pytest.mark.parametrize("name,fused,call", [
-    ("void wtc::dev::k_plane_apply<5, 2, 56, 56, 1, 256, float, false>(...)", True, "wtconv_fwd"),
-    ("void wtc::dev::k_plane_apply<5, 2, 56, 56, 1, 256, float, true>(...)", False, "wtconv_bwd_input"),
+    ("void wtc::dev::k_plane_apply<5, 2, 56, 56, 1, 256, float, false, false>(...)", True, "wtconv_fwd"),
+    ("void wtc::dev::k_plane_apply<5, 2, 56, 56, 1, 256, float, true, false>(...)", False, "wtconv_bwd_input"),
+    ("void wtc::dev::k_plane_apply<5, 2, 56, 56, 1, 256, float, false, true>(...)", False, "wtconv_fwd"),
+    ("void wtc::dev::k_plane_apply<5, 2, 56, 56, 1, 256, __half, true, true>(...)", False, "wtconv_bwd_input"),
     ("void wtc::dev::k_tile_apply<5, 3, 32, 64, 256, float, true>(...)", True, "wtconv_bwd"),
+    ("void wtc::dev::k_tile_apply<5, 3, 32, 64, 256, float, true>(...)", False, "wtconv_bwd_input"),
     ("void wtc::dev::k_deep_apply<float, 5, false>(...)", True, "wtconv_fwd"),
-    ("void wtc::dev::k_plane_bww<5, 2, 56, 56, 1, 256, float>(...)", False, "wtconv_bwd_weight"),
+    ("void wtc::dev::k_deep_apply<float, 5, true>(...)", False, "wtconv_bwd_input"),
+    ("void wtc::dev::k_plane_bww<5, 2, 56, 56, 1, 256, float, false>(...)", False, "wtconv_bwd_weight"),
     ("void wtc::dev::k_deep_bww<5>(...)", True, "wtconv_bwd"),
     ("void wtc::dev::k_bww_final<float>(...)", False, "wtconv_bwd_weight"),
-    ("void wtc::dev::k_plane_bwd<5, 2, 56, 56, 1, 256, float, false>(...)", True, "wtconv_bwd"),
-    ("void wtc::dev::k_plane_bwd1<5, 2, 56, 56, 1, 256, float, false, true>(...)", True, "wtconv_bwd"),
-    ("void wtc::dev::k_plane_bwd1<5, 2, 56, 56, 1, 256, float, true, true>(...)", False, "wtconv_bwd"),
-    ("void wtc::dev::k_plane_bwd1<5, 2, 56, 56, 1, 256, float, true, false>(...)", False, "wtconv_bwd_weight"),
-    ("void wtc::dev::k_plane_bwd1<5, 2, 56, 56, 1, 256, float, false, false>(...)", True, "wtconv_bwd"),
+    ("void wtc::dev::k_plane_bwd<5, 2, 56, 56, 1, 256, float, false, false>(...)", True, "wtconv_bwd"),
+    ("void wtc::dev::k_plane_bwd1<5, 2, 56, 56, 1, 256, float, false, true, false>(...)", True, "wtconv_bwd"),
+    ("void wtc::dev::k_plane_bwd1<5, 2, 56, 56, 1, 256, float, true, true, true>(...)", False, "wtconv_bwd"),
+    ("void wtc::dev::k_plane_bwd1<5, 2, 56, 56, 1, 256, float, true, false, false>(...)", False, "wtconv_bwd_weight"),
+    ("void wtc::dev::k_plane_bwd1<5, 2, 56, 56, 1, 256, float, false, false, true>(...)", False, "wtconv_bwd_weight"),
+    ("void wtc::dev::k_plane_bwd1<5, 2, 56, 56, 1, 256, float, false, false, false>(...)", True, "wtconv_bwd"),
     ("void wtc::dev::k_tile_bwd1<5, 3, 32, 32, 256, float>(...)", True, "wtconv_bwd"),
     ("__amd_rocclr_copyBuffer", True, None),
     ("void at::native::roll_cuda_kernel<float>(...)", True, None),
@@ -34,9 +39,11 @@ def test_kernels_map_to_their_entry_point(name, fused, call):
 
 
 def test_step_marker_is_the_forward_main_kernel():
-    assert bench.is_step_marker("void wtc::dev::k_plane_apply<5, 2, 56, 56, 1, 256, float, false>(x)")
+    assert bench.is_step_marker("void wtc::dev::k_plane_apply<5, 2, 56, 56, 1, 256, float, false, false>(x)")
+    assert bench.is_step_marker("void wtc::dev::k_plane_apply<5, 2, 56, 56, 1, 256, float, false, true>(x)")
     assert bench.is_step_marker("void wtc::dev::k_tile_apply<5, 3, 32, 64, 256, float, false>(x)")
-    assert not bench.is_step_marker("void wtc::dev::k_plane_apply<5, 2, 56, 56, 1, 256, float, true>(x)")
+    assert not bench.is_step_marker("void wtc::dev::k_plane_apply<5, 2, 56, 56, 1, 256, float, true, false>(x)")
+    assert not bench.is_step_marker("void wtc::dev::k_tile_apply<5, 3, 32, 64, 256, float, true>(x)")
     assert not bench.is_step_marker("void wtc::dev::k_deep_apply<float, 5, false>(x)")
 
 
