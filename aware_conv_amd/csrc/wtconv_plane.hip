@@ -92,6 +92,13 @@ hipError_t plane_apply(const wtconv_shape& s, const void* in, const Params& p, v
     const long total = long(cdiv(s.B, v->P)) * s.C;
     long nwg = resident_wgs(fn, v->NT, v->lds_apply);
     if (nwg > total) nwg = total;
+    // as few workgroups as take the same most groups each: with 3072 groups
+    // on 1280 slots, 1024 workgroups of three instead of 512 of three and
+    // 768 of two (the last round then runs on every workgroup, not 40%)
+    if (nwg > 0) {
+        const long per = (total + nwg - 1) / nwg;
+        nwg = (total + per - 1) / per;
+    }
     const void* bb = flip ? p.w_base : p.b_base;  // unread when flipped
     const void* wb = p.w_base;
     const void* sb = p.s_base;
