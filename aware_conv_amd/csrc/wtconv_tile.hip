@@ -28,32 +28,40 @@ constexpr int kDeepRS = 8, kDeepNCH = 12;
 // more).
 constexpr int kDeepNT = 512;
 
-// LDS plan of a deep workgroup (floats): folded filters, then per level m of
-// P (m = 0: P itself) a bordered x-side array set, then unbordered results.
+// LDS plan of a deep workgroup (floats): folded filters, then per level
+// m = 1..LD of P a bordered x-side array set (P itself, level 0, is read
+// from device memory straight into level 1's butterflies and never stored),
+// then unbordered results.
 // Rows are padded to whole kDeepRS segments so that a segment's window stays
-// in its row.
+// in its row.  Both pitches are odd: the lanes of a half-wavefront take
+// consecutive rows (and segments of kDeepRS columns), which an odd pitch
+// puts on distinct banks; an even one folds them onto a few (with pitch 36,
+// eight rows on eight banks: every window read 8-way conflicted).
 struct DeepLayout {
     int hp, wp, p, LD, KK;
     __host__ __device__ int h(int m) const { return hp >> m; }
     __host__ __device__ int w(int m) const { return wp >> m; }
     __host__ __device__ int bp(int m) const {  // bordered pitch
-        return (w(m) + kDeepRS - 1) / kDeepRS * kDeepRS + 2 * p;
+        return ((w(m) + kDeepRS - 1) / kDeepRS * kDeepRS + 2 * p) | 1;
     }
+    __host__ __device__ int rp(int m) const { return w(m) | 1; }  // result pitch
     __host__ __device__ int barr(int m) const { return (h(m) + 2 * p) * bp(m); }
     __host__ __device__ int nsub(int m) const { return m ? 4 : 1; }
     __host__ __device__ int wf() const { return 0; }
-    __host__ __device__ int uoff(int m) const {  // bordered arrays, m = 0..LD
+    __host__ __device__ int uoff(int m) const {  // bordered arrays, m = 1..LD
         int o = LD * 4 * KK;
-        for (int k = 0; k < m; ++k) o += nsub(k) * barr(k);
+        for (int k = 1; k < m; ++k) o += nsub(k) * barr(k);
         return o;
     }
     __host__ __device__ int coff(int m) const {  // results, m = 1..LD
         int o = uoff(LD + 1);
-        for (int k = 1; k < m; ++k) o += 4 * h(k) * w(k);
+        for (int k = 1; k < m; ++k) o += 4 * h(k) * rp(k);
         return o;
     }
     __host__ __device__ int end_apply() const { return coff(LD + 1); }
     __host__ __device__ int end_bww() const { return uoff(LD + 1) * 2 - LD * 4 * KK; }
+    // the dy side of the weight-gradient kernel follows the x side
+    __host__ __device__ int dy_shift() const { return uoff(LD + 1) - uoff(1); }
     // correlation partials after the two array sets: [item][K]
     __host__ __device__ int end_bww_red(int K) const {
         return end_bww() + LD * 4 * K * kDeepNCH * K;
@@ -94,31 +102,42 @@ __global__ __launch_bounds__(128) void k_box_sums(const T* __restrict__ src,
     }
 }
 
-// P of one plane -> bordered array m = 0.  Eight loads are issued before
-// their stores: one element per iteration would wait a device-memory round
-// trip per element.
-__device__ void load_p(const float* __restrict__ Pp, const DeepLayout& D, float* lds, int base,
-                       int tid, int nt) {
-    constexpr int U = 8;
-    const int n = D.hp * D.wp;
+// Level 1 of one plane from its box sums P in device memory: each item
+// loads a 2 x 2 block of P (two 8-byte loads; P's width is even) and writes
+// its four unnormalised Haar coefficients.  Four items' loads are issued
+// before their butterflies, so a lane waits on one device-memory round trip
+// per four items, not per item.
+__device__ void load_level1(const float* __restrict__ Pp, const DeepLayout& D, float* lds,
+                            int shift, int tid, int nt) {
+    constexpr int U = 4;
+    const int h = D.h(1), w = D.w(1), n = h * w, A = D.barr(1);
     for (int e0 = tid; e0 < n; e0 += U * nt) {
-        float v[U];
+        float2 top[U], bot[U];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            const int e = e0 + u * nt;
-            v[u] = e < n ? Pp[e] : 0.f;
+            const int e = min(e0 + u * nt, n - 1);
+            const float* q = Pp + size_t(2 * (e / w)) * D.wp + 2 * (e % w);
+            top[u] = *reinterpret_cast<const float2*>(q);
+            bot[u] = *reinterpret_cast<const float2*>(q + D.wp);
         }
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int e = e0 + u * nt;
-            if (e < n) lds[base + (e / D.wp + D.p) * D.bp(0) + D.p + e % D.wp] = v[u];
+            if (e >= n) break;
+            const float s0 = top[u].x + top[u].y, d0 = top[u].x - top[u].y;
+            const float s1 = bot[u].x + bot[u].y, d1 = bot[u].x - bot[u].y;
+            const int o = D.u(1, 0, e / w, e % w) + shift;
+            lds[o] = s0 + s1;
+            lds[o + A] = d0 + d1;
+            lds[o + 2 * A] = s0 - s1;
+            lds[o + 3 * A] = d0 - d1;
         }
     }
 }
 
-// Levels m = 1..LD of P: unnormalised Haar butterflies of the LL above.
+// Levels m = 2..LD of P: unnormalised Haar butterflies of the LL above.
 __device__ void deep_analysis(const DeepLayout& D, float* lds, int shift, int tid, int nt) {
-    for (int m = 1; m <= D.LD; ++m) {
+    for (int m = 2; m <= D.LD; ++m) {
         const int h = D.h(m), w = D.w(m);
         for (int e = tid; e < h * w; e += nt) {
             const int i = e / w, j = e % w;
@@ -158,7 +177,7 @@ __global__ __launch_bounds__(kDeepNT) void k_deep_apply(
         const int tt = FLIP ? KK - 1 - t : t;
         lds[i] = to_f(sw[gi]) * ldexpf(1.f, -2 * la) * to_f(ww[gi * KK + tt]);
     }
-    load_p(P + (size_t(b) * C + c) * D.hp * D.wp, D, lds, D.uoff(0), tid, nt);
+    load_level1(P + (size_t(b) * C + c) * D.hp * D.wp, D, lds, 0, tid, nt);
     __syncthreads();
     deep_analysis(D, lds, 0, tid, nt);
     // subband convs
@@ -183,7 +202,7 @@ __global__ __launch_bounds__(kDeepNT) void k_deep_apply(
                     for (int r = 0; r < RS; ++r) acc[r] = fmaf(wv, row[r + vv], acc[r]);
                 }
             }
-            float* o = lds + D.coff(m) + (s * h + i) * w + j0;
+            float* o = lds + D.coff(m) + (s * h + i) * D.rp(m) + j0;
 #pragma unroll
             for (int r = 0; r < RS; ++r)
                 if (j0 + r < w) o[r] = acc[r];
@@ -192,24 +211,24 @@ __global__ __launch_bounds__(kDeepNT) void k_deep_apply(
     __syncthreads();
     // fold level m into the LL of level m-1, deepest first
     for (int m = D.LD; m >= 2; --m) {
-        const int h = D.h(m - 1), w = D.w(m - 1), hc = D.h(m), wc = D.w(m);
+        const int h = D.h(m - 1), w = D.w(m - 1), hc = D.h(m), rc = D.rp(m);
         for (int e = tid; e < h * w; e += nt) {
             const int i = e / w, j = e % w;
-            const float* cs = lds + D.coff(m) + (i >> 1) * wc + (j >> 1);
-            const int A = hc * wc;
+            const float* cs = lds + D.coff(m) + (i >> 1) * rc + (j >> 1);
+            const int A = hc * rc;
             const float sy = (i & 1) ? -1.f : 1.f, sx = (j & 1) ? -1.f : 1.f;
             const float e0 = fmaf(sy, cs[2 * A], cs[0]), f0 = fmaf(sy, cs[3 * A], cs[A]);
-            lds[D.coff(m - 1) + i * w + j] += fmaf(sx, f0, e0);
+            lds[D.coff(m - 1) + i * D.rp(m - 1) + j] += fmaf(sx, f0, e0);
         }
         __syncthreads();
     }
     // expand level 1 over P's grid
     {
-        const int hc = D.h(1), wc = D.w(1), A = hc * wc;
+        const int hc = D.h(1), rc = D.rp(1), A = hc * rc;
         float* o = deep + (size_t(b) * C + c) * D.hp * D.wp;
         for (int e = tid; e < D.hp * D.wp; e += nt) {
             const int i = e / D.wp, j = e % D.wp;
-            const float* cs = lds + D.coff(1) + (i >> 1) * wc + (j >> 1);
+            const float* cs = lds + D.coff(1) + (i >> 1) * rc + (j >> 1);
             const float sy = (i & 1) ? -1.f : 1.f, sx = (j & 1) ? -1.f : 1.f;
             const float e0 = fmaf(sy, cs[2 * A], cs[0]), f0 = fmaf(sy, cs[3 * A], cs[A]);
             o[e] = fmaf(sx, f0, e0);
@@ -232,12 +251,12 @@ __global__ __launch_bounds__(kDeepNT) void k_deep_bww(const float* __restrict__ 
     const int b = blockIdx.x / C, c = blockIdx.x % C;
     constexpr int KK = K * K, NCH = kDeepNCH;
     const DeepLayout D{Hp >> LT, Wp >> LT, K / 2, L - LT, KK};
-    const int shift = D.uoff(D.LD + 1) - D.uoff(0);  // dy side follows the x side
+    const int shift = D.dy_shift();
     for (int i = tid; i < D.end_bww(); i += nt) lds[i] = 0.f;
     __syncthreads();
     const size_t po = (size_t(b) * C + c) * D.hp * D.wp;
-    load_p(px + po, D, lds, D.uoff(0), tid, nt);
-    load_p(pdy + po, D, lds, D.uoff(0) + shift, tid, nt);
+    load_level1(px + po, D, lds, 0, tid, nt);
+    load_level1(pdy + po, D, lds, shift, tid, nt);
     __syncthreads();
     deep_analysis(D, lds, 0, tid, nt);
     deep_analysis(D, lds, shift, tid, nt);

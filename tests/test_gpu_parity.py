@@ -133,8 +133,8 @@ def test_fused_backward_ranges_span_channels(B, C, k, L, H, W, dtype):
 @pytest.mark.parametrize("B,C,k,L,H,W,dtype", [
     (2, 3, 5, 5, 1024, 1024, "f32"),
     (1, 2, 7, 6, 768, 768, "f16"),
-    (3, 2, 3, 4, 512, 1536, "f32"),
-    (2, 2, 1, 4, 832, 832, "f32"),
+    (2, 2, 3, 4, 1024, 1280, "f32"),
+    (1, 2, 1, 4, 1152, 1152, "f32"),
 ])
 def test_deep_levels_through_device_memory(B, C, k, L, H, W, dtype):
     # box sums too large for one workgroup's LDS: the deep levels run level by
@@ -146,6 +146,24 @@ def test_deep_levels_through_device_memory(B, C, k, L, H, W, dtype):
     d["s_wav"] = (0.3 + 0.5 * torch.randn(L, C, 4, generator=g)).to(td)
     d["b_base"] = (0.5 * torch.randn(C, generator=g)).to(td)
     assert_parity(d, dtype, "deep in memory B%d C%d k%d L%d %dx%d %s" % (B, C, k, L, H, W, dtype))
+
+
+@pytest.mark.parametrize("B,C,k,L,H,W,dtype", [
+    (3, 2, 3, 4, 512, 1536, "f32"),
+    (2, 2, 1, 4, 832, 832, "f32"),
+    (2, 3, 5, 5, 512, 512, "f16"),
+])
+def test_deep_levels_of_large_planes_in_lds(B, C, k, L, H, W, dtype):
+    # the largest box sums whose deep levels still fit one workgroup's LDS
+    # (one or two workgroups per compute unit): level 1 is computed from the
+    # box sums in device memory, levels 2.. in LDS
+    d = wi.make_inputs(B, C, H, W, L, k, dtype, seed=H + W + L + 1)
+    g = torch.Generator().manual_seed(23)
+    td = d["x"].dtype
+    d["s_base"] = (1 + 0.5 * torch.randn(C, generator=g)).to(td)
+    d["s_wav"] = (0.3 + 0.5 * torch.randn(L, C, 4, generator=g)).to(td)
+    d["b_base"] = (0.5 * torch.randn(C, generator=g)).to(td)
+    assert_parity(d, dtype, "deep in LDS B%d C%d k%d L%d %dx%d %s" % (B, C, k, L, H, W, dtype))
 
 
 ANY_SIZE = [  # k, L, H, W, dtype: sides the kernels do not take directly
