@@ -88,7 +88,15 @@ __global__ __launch_bounds__(128) void k_box_sums(const T* __restrict__ src,
     for (int q0 = 0; q0 < nq; q0 += blockDim.x) {
         const int q = q0 + threadIdx.x;
         float acc = 0.f;
-        if (q < nq) {
+        if (q < nq && n == 8) {
+            // the blocks of three tile levels: all eight row loads in flight
+            // at once, then the sums in the same order as below
+            float v[8][4];
+#pragma unroll
+            for (int r = 0; r < 8; ++r) load_vec<T, 4>(s0 + size_t(r) * Wp + 4 * q, v[r]);
+#pragma unroll
+            for (int r = 0; r < 8; ++r) acc += (v[r][0] + v[r][1]) + (v[r][2] + v[r][3]);
+        } else if (q < nq) {
             for (int r = 0; r < n; ++r) {
                 float v[4];
                 load_vec<T, 4>(s0 + size_t(r) * Wp + 4 * q, v);
