@@ -236,15 +236,37 @@ __device__ __forceinline__ void lds_get(const float* src, float* v) {
 // values (the receptive footprint of the coarser levels) around its core.
 // AMAX_ caps the row alignment (floats): 4 lets the row phases use 16-byte
 // LDS accesses, 2 leaves the pitch free to spread the conv windows of a
-// wavefront over every bank.
-template <int K_, int L_, int H_, int W_, int P_, int NT_, int HT_ = 0, int AMAX_ = 4>
+// wavefront over every bank.  TRIM_ (tiles): store less halo on the levels
+// the fetch analyses in registers (sh below).
+template <int K_, int L_, int H_, int W_, int P_, int NT_, int HT_ = 0, int AMAX_ = 4,
+          bool TRIM_ = false>
 struct Geo {
     static constexpr int K = K_, L = L_, H = H_, W = W_, P = P_, NT = NT_, HT = HT_;
     static constexpr int p = K / 2, KK = K * K;
     static_assert(HT == 0 || (HT == L && P == 1), "tiles hold one plane, all their levels");
-    // stored halo and the part of it filled with data
+    // receptive halo and the part of it filled with data
     __host__ __device__ static constexpr int h(int l) { return HT ? (p << (HT - l)) : p; }
     __host__ __device__ static constexpr int ah(int l) { return HT ? h(l) : 0; }
+    // Levels the halo fetch of a tile analyses in registers (Fetch: four-row
+    // items give levels 1 and 2, two-row items level 1).
+    __host__ __device__ static constexpr int fetch_levels() {
+        return (L >= 2 && ah(0) % 4 == 0 && W % 4 == 0) ? 2 : (L >= 1 ? 1 : 0);
+    }
+    // Stored halo of level l.  Whole planes: the zero border p.  Tiles: h(l),
+    // the footprint of the coarser levels; with TRIM_ only on the levels
+    // analysed in LDS (from fetch_levels() on): below those a level is only
+    // read by its own conv, so it keeps p, rounded up to the unit the fetch
+    // writes it in (8 >> l: four rows by four or eight columns at level 0).
+    // The 32 x 64 forward tile at k = 5 then needs 42.6 KB of LDS instead of
+    // 61.6 KB, three workgroups per unit instead of two (512^2 forward
+    // 619 -> 550 us).  The tile backward keeps the full halos: it holds 191
+    // VGPRs, two waves per SIMD, so the smaller footprint buys it nothing
+    // (it ran 2% slower on the trimmed layout; at three waves it spills).
+    __host__ __device__ static constexpr int sh(int l) {
+        if (!HT || !TRIM_ || l >= fetch_levels()) return h(l);
+        const int u = 8 >> l, s = (p + u - 1) / u * u;
+        return s < h(l) ? s : h(l);
+    }
     static constexpr Tile TL = plan_tile(K, L, H, W, P, NT, 32);
     static constexpr int R = TL.R, Q = TL.Q, NJ = TL.jobs;
     static_assert(R > 0 && NJ <= NT, "no tile fits one job per lane");
@@ -263,10 +285,10 @@ struct Geo {
     // rows: halo, then the padded core (its last tile's window) or the core
     // plus the far halo, whichever reaches further
     __host__ __device__ static constexpr int rows(int l) {
-        return h(l) + maxi(NG(l) * Q + p, hl(l) + h(l));
+        return sh(l) + maxi(NG(l) * Q + p, hl(l) + sh(l));
     }
     __host__ __device__ static constexpr int minpitch(int l) {
-        return h(l) + maxi(NS(l) * R + p, wl(l) + h(l));
+        return sh(l) + maxi(NS(l) * R + p, wl(l) + sh(l));
     }
     // alignment (floats) of the core rows of level l: the widest LDS access
     // the fp32 item width of the plane (and of the halo) allows, halved per
@@ -289,7 +311,7 @@ struct Geo {
         int base = 0;
         for (int l = 0; l <= L; ++l) {
             t.lv[l] = plan_layout(jstart(l), jobs(l), S(l), NS(l), NG(l), R, Q, rows(l),
-                                  minpitch(l), base, h(l), al(l));
+                                  minpitch(l), base, sh(l), al(l));
             base = t.lv[l].off + P * S(l) * t.lv[l].astride;
         }
         t.end = base;
@@ -299,7 +321,7 @@ struct Geo {
     static constexpr bool aligned_table() {
         for (int l = 0; l <= L; ++l) {
             const int a = al(l), pt = TB.lv[l].pitch, o = TB.lv[l].off;
-            if (pt % a || TB.lv[l].astride % a || (o + h(l) * pt + h(l)) % a) return false;
+            if (pt % a || TB.lv[l].astride % a || (o + sh(l) * pt + sh(l)) % a) return false;
         }
         return true;
     }
@@ -322,7 +344,7 @@ struct Geo {
     // element (i, j) of x-side array (level l, plane pl, subband s); i and j
     // may reach into the border
     __host__ __device__ static constexpr int uidx(int l, int pl, int s, int i, int j) {
-        return off(l) + (pl * S(l) + s) * arr(l) + (i + h(l)) * pitch(l) + h(l) + j;
+        return off(l) + (pl * S(l) + s) * arr(l) + (i + sh(l)) * pitch(l) + sh(l) + j;
     }
     __host__ __device__ static constexpr int vidx(int l, int pl, int s, int i, int j) {
         return voff(l) + (pl * 4 + s) * varr(l) + i * vpitch(l) + j;
@@ -335,6 +357,10 @@ struct Geo {
 // per tile (dy and x), so window reads outweigh the row phases.
 template <int K, int L, int H, int W, int P, int NT>
 using GeoGrad = Geo<K, L, H, W, P, NT, 0, 2>;
+
+// Layout of the tile forward: trimmed halos below the LDS-analysed levels.
+template <int K, int LT, int TH, int TW, int NT>
+using GeoTileApply = Geo<K, LT, TH, TW, 1, NT, LT, 4, true>;
 
 // One lane's tile: array level, plane, subband, tile row group and column
 // strip.  Decoded once; the lane keeps it on every group of planes.
@@ -542,8 +568,31 @@ struct Fetch {
     static_assert(FW % V == 0 && FH % ROWS == 0, "footprint in whole items");
     static constexpr int ITEMS = G::P * RB * NV, IT = cdiv(ITEMS, G::NT);
     static constexpr int LEVELS = ROWS == 4 ? 2 : (G::L >= 1 ? 1 : 0);  // levels computed here
+    static_assert(!HALO || LEVELS == G::fetch_levels(), "the layout's view of the fetch");
+    // a level-l item (ROWS >> l rows, V >> l columns, placed at -A0 >> l plus
+    // whole items) lies entirely inside or entirely outside the stored halo
+    static constexpr bool whole_items() {
+        for (int l = 0; l < LEVELS && l < 2; ++l) {
+            const int d = (A0 >> l) - G::sh(l), nr = ROWS >> l, nc = V >> l;
+            if (d < 0 || (nr && d % nr) || (nc && d % nc)) return false;
+        }
+        return true;
+    }
+    static_assert(!HALO || whole_items(), "fetch items straddle the stored halo");
     using raw_t = typename RawVec<V * int(sizeof(T))>::type;
     raw_t r[IT][ROWS];
+
+    // Is the level-l block of nr x nc values at (i, j) stored?  (Tiles keep
+    // less halo than they load below the levels analysed in LDS.)
+    template <int l>
+    static __device__ __forceinline__ bool stored(int i, int j, int nr, int nc) {
+        if constexpr (!HALO || (A0 >> l) == G::sh(l)) {
+            return true;
+        } else {
+            constexpr int a = G::sh(l);
+            return i >= -a && i + nr <= G::hl(l) + a && j >= -a && j + nc <= G::wl(l) + a;
+        }
+    }
 
     // Whole planes: the loads of planes b0..b0+P-1 through a buffer
     // resource, with no branch (items past ITEMS and planes past B read
@@ -682,9 +731,12 @@ struct Fetch {
                 for (int k = 0; k < ROWS; ++k) unpack(r[it][k], x[k]);
                 const int fy = ROWS * rb - A0, fx = cv * V - A0;
                 if constexpr (WRITE_X) {
-                    float* o = lds + G::uidx(0, pl, 0, fy, fx);
+                    if (stored<0>(fy, fx, ROWS, V)) {
+                        float* o = lds + G::uidx(0, pl, 0, fy, fx);
 #pragma unroll
-                    for (int k = 0; k < ROWS; ++k) lds_put<V, G::al(0)>(o + k * G::pitch(0), x[k]);
+                        for (int k = 0; k < ROWS; ++k)
+                            lds_put<V, G::al(0)>(o + k * G::pitch(0), x[k]);
+                    }
                 }
                 if constexpr (G::L >= 1) {  // (L = 0: plain depthwise conv)
                     float ll[ROWS / 2][V / 2];
@@ -700,7 +752,8 @@ struct Fetch {
 #pragma unroll
                             for (int sb = 0; sb < 4; ++sb) sub[sb][m] = o[sb];
                         }
-                        put_row<VSIDE, 1, V / 2>(lds, pl, fy / 2 + rr, fx / 2, sub);
+                        if (VSIDE || stored<1>(fy / 2, fx / 2, ROWS / 2, V / 2))
+                            put_row<VSIDE, 1, V / 2>(lds, pl, fy / 2 + rr, fx / 2, sub);
                     }
                     if constexpr (ROWS == 4) {
                         float sub[4][V / 4];
@@ -711,7 +764,8 @@ struct Fetch {
 #pragma unroll
                             for (int sb = 0; sb < 4; ++sb) sub[sb][m] = o[sb];
                         }
-                        put_row<VSIDE, 2, V / 4>(lds, pl, fy / 4, fx / 4, sub);
+                        if (VSIDE || stored<2>(fy / 4, fx / 4, 1, V / 4))
+                            put_row<VSIDE, 2, V / 4>(lds, pl, fy / 4, fx / 4, sub);
                     }
                 }
             }
@@ -1970,7 +2024,7 @@ __global__ __launch_bounds__(NT) void k_tile_apply(
     const T* __restrict__ in, const T* __restrict__ wb, const T* __restrict__ bb,
     const T* __restrict__ sb, const T* __restrict__ ww, const T* __restrict__ sw,
     const float* __restrict__ deep, T* __restrict__ out, int B, int C, int Hp, int Wp) {
-    using G = Geo<K, LT, TH, TW, 1, NT, LT>;
+    using G = GeoTileApply<K, LT, TH, TW, NT>;
     using F = Fetch<G, T>;
     constexpr int KK = G::KK, Q = G::Q, R = G::R;
     extern __shared__ float lds[];

@@ -36,7 +36,7 @@ template <int K, int LT, typename T>
 TileVariant make_tile_variant(int dtype) {
     constexpr int ATW = apply_tile_w(K), BTW = bwd_tile_w(K);
     using G = dev::Geo<K, LT, kTileH, kTileW, 1, kTileNT, LT>;
-    using GA = dev::Geo<K, LT, kTileH, ATW, 1, kTileNT, LT>;
+    using GA = dev::GeoTileApply<K, LT, kTileH, ATW, kTileNT>;
     using GB = dev::Geo<K, LT, kTileH, BTW, 1, kTileNT, LT>;
     return TileVariant{
         K, LT, dtype, kTileH, kTileW, kTileH, ATW, BTW, kTileNT,
