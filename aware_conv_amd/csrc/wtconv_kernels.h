@@ -257,11 +257,9 @@ struct Geo {
     // analysed in LDS (from fetch_levels() on): below those a level is only
     // read by its own conv, so it keeps p, rounded up to the unit the fetch
     // writes it in (8 >> l: four rows by four or eight columns at level 0).
-    // The 32 x 64 forward tile at k = 5 then needs 42.6 KB of LDS instead of
-    // 61.6 KB, three workgroups per unit instead of two (512^2 forward
-    // 619 -> 550 us).  The tile backward keeps the full halos: it holds 191
-    // VGPRs, two waves per SIMD, so the smaller footprint buys it nothing
-    // (it ran 2% slower on the trimmed layout; at three waves it spills).
+    // The 32 x 64 tile at k = 5 then needs 42.6 KB of LDS instead of 61.6 KB
+    // for the forward (41.3 + 1.3 KB for the fused backward), three
+    // workgroups per unit instead of two (512^2 forward 619 -> 550 us).
     __host__ __device__ static constexpr int sh(int l) {
         if (!HT || !TRIM_ || l >= fetch_levels()) return h(l);
         const int u = 8 >> l, s = (p + u - 1) / u * u;
@@ -940,6 +938,64 @@ __device__ __forceinline__ void conv_corr_tile(const float* src, int pitch,
         if (ir >= p && ir < p + Q)
 #pragma unroll
             for (int j = 0; j < R; ++j) ctr[ir - p][j] = cur[j + p];
+#pragma unroll
+        for (int q = 0; q < Q; ++q) {
+            const int u = ir - q;
+            if (u >= 0 && u < K) {
+#pragma unroll
+                for (int v = 0; v < K; ++v)
+#pragma unroll
+                    for (int j = 0; j < R; ++j) {
+                        acc[q][j] = fmaf(w[u * K + v], cur[j + v], acc[q][j]);
+                        g[u * K + v] = fmaf(a[q][j], cur[j + v], g[u * K + v]);
+                    }
+            }
+        }
+#pragma unroll
+        for (int q = 0; q < Q; ++q) {
+            const int u = ir - q;
+            if (u >= 0 && u < K) {
+#pragma unroll
+                for (int j = 0; j < R; ++j) asm volatile("" : "+v"(acc[q][j]));
+#pragma unroll
+                for (int v = 0; v < K; ++v) asm volatile("" : "+v"(g[u * K + v]));
+            }
+        }
+        asm volatile("" : "+v"(nxt));
+    }
+}
+
+// conv_corr_tile with the window's centre summed on the way (rows below
+// nrows, columns below ncols) instead of kept: one register for the Q x R
+// of the centre.
+template <int K, int Q, int R>
+__device__ __forceinline__ void conv_corr_tile_csum(const float* src, int pitch,
+                                               const float (&w)[K * K], const float (&a)[Q][R],
+                                               float (&acc)[Q][R], float (&g)[K * K],
+                                               float& csum, int nrows, int ncols) {
+    constexpr int p = K / 2, NR = Q + K - 1, NC = R + K - 1;
+#pragma unroll
+    for (int q = 0; q < Q; ++q)
+#pragma unroll
+        for (int j = 0; j < R; ++j) acc[q][j] = 0.f;
+    float in[2][NC];
+#pragma unroll
+    for (int m = 0; m < NC; ++m) in[0][m] = src[m];
+    int nxt = pitch;  // element offset of the next row
+#pragma unroll
+    for (int ir = 0; ir < NR; ++ir) {
+        const float* cur = in[ir & 1];
+        if (ir + 1 < NR) {
+#pragma unroll
+            for (int m = 0; m < NC; ++m) in[(ir + 1) & 1][m] = src[nxt + m];
+            nxt += pitch;
+        }
+        if (ir >= p && ir < p + Q) {
+            float rs = 0.f;
+#pragma unroll
+            for (int j = 0; j < R; ++j) rs += (ir - p < nrows && j < ncols) ? cur[j + p] : 0.f;
+            csum += rs;
+        }
 #pragma unroll
         for (int q = 0; q < Q; ++q) {
             const int u = ir - q;
@@ -2204,14 +2260,13 @@ namespace wtc {
 namespace dev {
 
 // LDS of the one-side tile backward: one array layout (x's core, then dy with
-// its halos), the reduction rows, or the folded filters on their way to
-// registers, whichever is largest.
+// its halos) with the folded filters after it, or the reduction rows,
+// whichever is larger.
 template <class G>
 constexpr size_t tile_bwd1_lds_bytes() {
-    const size_t a = sizeof(float) * G::side;
+    const size_t a = sizeof(float) * (G::side + G::NWF);
     const size_t b = sizeof(float) * G::NT * (G::KK + 1);
-    const size_t f = sizeof(float) * G::NWF;
-    return a > b ? (a > f ? a : f) : (b > f ? b : f);
+    return a > b ? a : b;
 }
 // Waves per SIMD for the register budget: what the LDS allows, at most 3,
 // and 2 for 7 x 7 filters (their 49 taps and wider windows need the 256
@@ -2236,15 +2291,21 @@ constexpr int tile_bwd1_waves() {
 // one window per tile feeds the input-gradient conv and the taps.  Levels
 // beyond the fetch's are analysed over their halos for x too, from stale
 // values there: only core coefficients, which depend on core values alone,
-// are read.  Registers for up to three waves per SIMD where the LDS allows.
+// are read.  Registers for up to three waves per SIMD where the LDS allows
+// (the trimmed layout of the forward): at k = 5 that holds without spills
+// because nothing long-lived shares the peaks -- the filters are reloaded
+// from LDS per tile, the window's centre is summed as it passes, and the
+// next tile's dy is loaded after the store (x's commit and analysis cover
+// its latency); at three waves with the filters in registers it spilled and
+// ran twice as long.
 template <int K, int LT, int TH, int TW, int NT, typename T>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(
-    tile_bwd1_waves<Geo<K, LT, TH, TW, 1, NT, LT>>()))) void k_tile_bwd1(
+    tile_bwd1_waves<GeoTileApply<K, LT, TH, TW, NT>>()))) void k_tile_bwd1(
     const T* __restrict__ x, const T* __restrict__ dy, const T* __restrict__ wb,
     const T* __restrict__ sb, const T* __restrict__ ww, const T* __restrict__ sw,
     const float* __restrict__ deep, T* __restrict__ dx, float* __restrict__ part,
     float* __restrict__ px, int B, int C, int Hp, int Wp, int upw, int npart) {
-    using G = Geo<K, LT, TH, TW, 1, NT, LT>;
+    using G = GeoTileApply<K, LT, TH, TW, NT>;
     using FX = Fetch<G, T, false>;  // x: the tile's core
     using FD = Fetch<G, T, true>;   // dy: the core and its halos
     constexpr int KK = G::KK, Q = G::Q, R = G::R;
@@ -2273,14 +2334,11 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(
     const int ncols = min(R, wcols - job.strip * R);
     const bool full = nrows == Q && ncols == R;
     const int dst = win + G::p * pitch + G::p;
-    // the folded filters pass through the head of the arrays on their way
-    // to registers (one channel per workgroup)
-    float w[KK];
-    fold_weights<G, T, true>(lds, wb, wb, sb, ww, sw, C, c, tid);
-    __syncthreads();
-#pragma unroll
-    for (int t = 0; t < KK; ++t) w[t] = lds[wsrc + t];
-    __syncthreads();
+    // the folded filters (one channel per workgroup) stay after the arrays;
+    // a lane reloads its K x K into registers for each tile's conv, so that
+    // they are not live through the store phase beside the next tile's loads
+    float* const wl = lds + G::side + wsrc;
+    fold_weights<G, T, true>(lds + G::side, wb, wb, sb, ww, sw, C, c, tid);
     for (int i = tid; i < G::side; i += NT) lds[i] = 0.f;
     __syncthreads();
     float gacc[KK];  // rotated: gacc[KK - 1 - t] accumulates tap t
@@ -2333,26 +2391,19 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(
         if (job.on) {
             // the window's centre past the job's part of the core is halo
             // (real neighbours): masked out of the dy sum
-            float d[Q][R];
-            conv_corr_tile<K, Q, R>(lds + win, pitch, w, ux, acc, gacc, d);
-            if (job.lvl == 0) {
-                float m[Q][R];
+            float csum = 0.f;
+            float w[KK];
 #pragma unroll
-                for (int qq = 0; qq < Q; ++qq)
-#pragma unroll
-                    for (int j = 0; j < R; ++j)
-                        m[qq][j] = (full || (qq < nrows && j < ncols)) ? d[qq][j] : 0.f;
-                sdy += tile_sum<Q, R>(m);
-            }
+            for (int tt = 0; tt < KK; ++tt) w[tt] = wl[tt];
+            conv_corr_tile_csum<K, Q, R>(lds + win, pitch, w, ux, acc, gacc, csum, nrows, ncols);
+            if (job.lvl == 0) sdy += csum;
         }
-        // the next tile's loads after the FMAs, unconditional (past the range
-        // they cover an empty buffer range: b = B)
+        // the next tile's x after the FMAs, its dy after the store; both
+        // unconditional (past the range they cover an empty buffer range:
+        // b = B)
         asm volatile("" : "+v"(t));
-        {
-            const bool more = u + 1 < u1;
-            fx.issue_tile_buf(x, more ? nx.b : B, B, C, c, t, nx.ty * TH, nx.tx * TW, Hp, Wp);
-            fd.issue_tile_buf(dy, more ? nx.b : B, B, C, c, t, nx.ty * TH, nx.tx * TW, Hp, Wp);
-        }
+        const bool more = u + 1 < u1;
+        fx.issue_tile_buf(x, more ? nx.b : B, B, C, c, t, nx.ty * TH, nx.tx * TW, Hp, Wp);
         __syncthreads();
         if (job.on) {
 #pragma unroll
@@ -2371,6 +2422,8 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(
             __syncthreads();
         });
         final_store<G, T>(lds, dx, b, B, C, c, t, y0, x0, Hp, Wp);
+        asm volatile("" : "+v"(t));
+        fd.issue_tile_buf(dy, more ? nx.b : B, B, C, c, t, nx.ty * TH, nx.tx * TW, Hp, Wp);
         cu = nx;
         __syncthreads();
     }
