@@ -1261,6 +1261,39 @@ __device__ __forceinline__ void fold_weights(float* wf, const T* __restrict__ wb
 // Kernels
 // ---------------------------------------------------------------------------
 
+// Wave priority from here on (s_setprio, 0..3).  A SIMD issues from its ready
+// waves in priority order, oldest first among equals; with three workgroups
+// of one kernel per compute unit, each in its own phase of the per-group
+// chain, the order decides whether a workgroup's short latency-bound phases
+// (commits, write-back, synthesis and stores between barriers) wait behind
+// another workgroup's FMAs.  The fences keep the compiler from moving
+// instructions across the change.
+template <int N>
+__device__ __forceinline__ void wave_prio() {
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_setprio(N);
+    __builtin_amdgcn_sched_barrier(0);
+}
+
+// Phase priorities (commit and analysis, conv, write-back to store) of the
+// kernels that gain from them, chosen among 12 settings per kernel (stage 1
+// unless named, gated per-call times, one box):
+// - whole-plane forward: 3, 1, 0 -- the stores lowest (fp32 48.1 -> 44.8
+//   us, fp16 92 -> 86 us, 28^2 30.4 -> 29.4 us); with the stores above the
+//   conv it ran 46-49 us;
+// - one-side whole-plane backward: fp32 0, 1, 3 (93.0 -> 84.6 us), fp16 3, 0,
+//   3 (168 -> 151.5 us) -- the store phase highest;
+// - tile forward: 0, 1, 3 (512^2: 552 -> 520 us).
+// The tile backward is left at one priority: no setting beat it, and a conv
+// above the other phases slowed it by up to 20%.
+struct PrioPlaneApply { static constexpr int commit = 3, conv = 1, store = 0; };
+template <typename T>
+struct PrioPlaneBwd1 {
+    static constexpr bool f32 = std::is_same<T, float>::value;
+    static constexpr int commit = f32 ? 0 : 3, conv = f32 ? 1 : 0, store = 3;
+};
+struct PrioTileApply { static constexpr int commit = 0, conv = 1, store = 3; };
+
 // Waves per SIMD the LDS footprint allows (NT/64 waves per workgroup spread
 // over 4 SIMDs); the register budget is sized to match.
 constexpr int waves_for_lds(size_t lds_bytes, int nt) {
@@ -1344,6 +1377,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(
             init = job.lvl == 0 ? wf[G::NWF - 1] : 0.f;
             cur = c;
         }
+        wave_prio<PrioPlaneApply::commit>();
         fx.template commit<true, false>(lds, tid);
         __syncthreads();
         static_for<F::LEVELS + 1, L + 1>([&](auto lc) {
@@ -1351,7 +1385,9 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(
             __syncthreads();
         });
         float acc[Q][R];
+        wave_prio<PrioPlaneApply::conv>();
         if (job.on) conv_tile<K, Q, R>(lds + win, pitch, w, init, acc);
+        wave_prio<PrioPlaneApply::store>();
         // the next group's loads fly during write-back, synthesis and store
         if (q + 1 < q1) fx.template issue_buf<RAG>(in, ((q + 1) % ngroups) * P, B, C, (q + 1) / ngroups, tid, rg);
         __syncthreads();
@@ -1834,6 +1870,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(
         }
         // x through the arrays: the lane keeps U at its tile (zeros outside
         // the level's core, so a partial tile needs no mask)
+        wave_prio<PrioPlaneBwd1<T>::commit>();
         fx.template commit<true, false>(lds, t);
         __syncthreads();
         static_for<F::LEVELS + 1, L + 1>([&](auto lc) {
@@ -1861,7 +1898,9 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(
                 float w[KK];
 #pragma unroll
                 for (int t = 0; t < KK; ++t) w[t] = wf[wsrc + t];
+                wave_prio<PrioPlaneBwd1<T>::conv>();
                 conv_corr_tile<K, Q, R>(lds + win, pitch, w, u, acc, gacc, d);
+                wave_prio<PrioPlaneBwd1<T>::store>();
             } else {
                 corr_window_tile<K, Q, R>(lds + win, pitch, u, gacc, d);
             }
@@ -2121,6 +2160,7 @@ __global__ __launch_bounds__(NT) void k_tile_apply(
             init = job.lvl == 0 ? wf[G::NWF - 1] : 0.f;
             cur = c;
         }
+        wave_prio<PrioTileApply::commit>();
         fx.template commit<true, false>(lds, tid);
         __syncthreads();
         static_for<F::LEVELS + 1, LT + 1>([&](auto lc) {
@@ -2130,7 +2170,9 @@ __global__ __launch_bounds__(NT) void k_tile_apply(
         DeepRegs<G> dr;
         if (deep) fetch_deep<G>(dr, deep, b, C, c, y0, x0, Hp, Wp, tid);
         float acc[Q][R];
+        wave_prio<PrioTileApply::conv>();
         if (job.on) conv_tile<K, Q, R>(lds + win, pitch, w, init, acc);
+        wave_prio<PrioTileApply::store>();
         if (q + 1 < q1) fx.issue_tile_buf(in, nx.b, B, C, nx.c, tid, nx.ty * TH, nx.tx * TW, Hp, Wp);
         __syncthreads();
         if (job.on) {
