@@ -1283,16 +1283,20 @@ __device__ __forceinline__ void wave_prio() {
 //   conv it ran 46-49 us;
 // - one-side whole-plane backward: fp32 0, 1, 3 (93.0 -> 84.6 us), fp16 3, 0,
 //   3 (168 -> 151.5 us) -- the store phase highest;
-// - tile forward: 0, 1, 3 (512^2: 552 -> 520 us).
-// The tile backward is left at one priority: no setting beat it, and a conv
-// above the other phases slowed it by up to 20%.
+// - two-side whole-plane backward: 0, 1, 3 (28^2: 56.3 -> 53.9 us, 14^2
+//   40.7 -> 40.0 us);
+// - tile forward: 0, 1, 3 (512^2: 552 -> 520 us);
+// - tile backward: x's commit 2, dy's commit 3, conv 0, store 3 (512^2:
+//   960 -> 944 us); a conv above the other phases slowed it by up to 20%.
 struct PrioPlaneApply { static constexpr int commit = 3, conv = 1, store = 0; };
 template <typename T>
 struct PrioPlaneBwd1 {
     static constexpr bool f32 = std::is_same<T, float>::value;
     static constexpr int commit = f32 ? 0 : 3, conv = f32 ? 1 : 0, store = 3;
 };
+struct PrioPlaneBwd { static constexpr int commit = 0, conv = 1, store = 3; };
 struct PrioTileApply { static constexpr int commit = 0, conv = 1, store = 3; };
+struct PrioTileBwd1 { static constexpr int commit_x = 2, commit_dy = 3, conv = 0, store = 3; };
 
 // Waves per SIMD the LDS footprint allows (NT/64 waves per workgroup spread
 // over 4 SIMDs); the register budget is sized to match.
@@ -1693,6 +1697,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void k_
             sdy = 0.f;
             cur = c;
         }
+        wave_prio<PrioPlaneBwd::commit>();
         fx.template commit<true, false>(lds, tid);
         fd.template commit<true, false>(ldy, tid);
         __syncthreads();
@@ -1702,6 +1707,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void k_
             __syncthreads();
         });
         float acc[Q][R];
+        wave_prio<PrioPlaneBwd::conv>();
         if (job.on) {
             // The tile's own dy values (V^l_s at level l), read from the
             // core of its array: outside a level's core the arrays hold
@@ -1725,6 +1731,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void k_
             for (int t = 0; t < KK; ++t) w[t] = wf[wo + t];
             conv_tile<K, Q, R>(ldy + yw, pitch, w, 0.f, acc);
         }
+        wave_prio<PrioPlaneBwd::store>();
         const bool wrap = grp + 1 == ngroups;
         const int cn = wrap ? c + 1 : c, gn = wrap ? 0 : grp + 1;
         if (it + 1 < nitems) {
@@ -2392,6 +2399,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(
         int t = tid;
         const int b = cu.b, y0 = cu.ty * TH, x0 = cu.tx * TW;
         const TileCursor nx = cu.next(B, nty, ntx);
+        wave_prio<PrioTileBwd1::commit_x>();
         fx.template commit<true, false>(lds, t);
         __syncthreads();
         static_for<FX::LEVELS + 1, LT + 1>([&](auto lc) {
@@ -2421,6 +2429,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(
             }
         }
         __syncthreads();
+        wave_prio<PrioTileBwd1::commit_dy>();
         fd.template commit<true, false>(lds, t);
         __syncthreads();
         static_for<FD::LEVELS + 1, LT + 1>([&](auto lc) {
@@ -2437,7 +2446,9 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(
             float w[KK];
 #pragma unroll
             for (int tt = 0; tt < KK; ++tt) w[tt] = wl[tt];
+            wave_prio<PrioTileBwd1::conv>();
             conv_corr_tile_csum<K, Q, R>(lds + win, pitch, w, ux, acc, gacc, csum, nrows, ncols);
+            wave_prio<PrioTileBwd1::store>();
             if (job.lvl == 0) sdy += csum;
         }
         // the next tile's x after the FMAs, its dy after the store; both
