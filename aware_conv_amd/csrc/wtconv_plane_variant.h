@@ -34,13 +34,21 @@ constexpr size_t kPlaneMaxLds = 163840;  // LDS of one gfx950 compute unit
 // shapes, it wins where a lane's tile holds at least 20 outputs (56 x 56:
 // 28 outputs, 97.6 -> 89.2 us per backward) or where there are no wavelet
 // levels (the plain depthwise conv: x's pass is a copy), and loses on the
-// 14-output tiles of the 28 x 28 and 14 x 14 shapes (56.0 -> 58.5 and
-// 40.6 -> 46.2 us), whose two-side LDS already lets three workgroups share a
-// compute unit.
+// 14-output tiles of the 28 x 28 shape (56.0 -> 58.5 us; fp16 55.5 -> 56.9
+// us with the wave priorities of both kernels), whose two-side LDS already
+// lets three workgroups share a compute unit.
+// Two small shapes are measured exceptions (B = 64, per fused backward):
+// 14 x 14 at k = 5, L = 1 (four planes per group on 128 threads: 40.1 ->
+// 36.7 us, fp16 41.0 -> 37.9 us; its 14-output tiles notwithstanding) and
+// 8 x 8 at L = 3 (57.6 -> 47.0 us) take the one-side kernel; 8 x 8 at L = 1
+// and 2 keep the two-side one (the one-side took 53.6 and 92.5 us against
+// 39.7 and 46.3).
 template <int K, int L, int H, int W, int P, int NT>
 constexpr bool bwd_one_side() {
     using G = dev::Geo<K, L, H, W, P, NT>;
-    return (L == 0 || G::Q * G::R >= 20) && dev::bwd1_lds_bytes<G>() <= kPlaneMaxLds;
+    constexpr bool measured = (K == 5 && L == 1 && H == 14 && W == 14) ||
+                              (K == 5 && L == 3 && H == 8 && W == 8);
+    return (L == 0 || G::Q * G::R >= 20 || measured) && dev::bwd1_lds_bytes<G>() <= kPlaneMaxLds;
 }
 
 template <int K, int L, int H, int W, int P, int NT, typename T, bool RAG>
