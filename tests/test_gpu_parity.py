@@ -172,6 +172,9 @@ ANY_SIZE = [  # k, L, H, W, dtype: sides the kernels do not take directly
     (5, 1, 13, 13, "f32"),    # of 14 x 14
     (5, 1, 7, 7, "f32"),      # ConvNeXt stage 4: of 8 x 8
     (5, 1, 7, 7, "f16"),
+    (5, 3, 7, 7, "f32"),      # of the 8 x 8 three-level variant (one-side backward)
+    (5, 2, 7, 7, "f16"),      # of the 8 x 8 two-level variant (two-side backward)
+    (5, 1, 13, 13, "f16"),    # of 14 x 14, four planes per group, one-side backward
     (3, 3, 30, 17, "f32"),    # to 32 x 24, tiles
     (7, 2, 6, 10, "f32"),     # to 8 x 12, tiles
     (5, 3, 56, 56, "f32"),    # L = 3 at 56: divisible, tiles directly
