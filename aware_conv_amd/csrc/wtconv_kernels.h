@@ -356,9 +356,10 @@ struct Geo {
 template <int K, int L, int H, int W, int P, int NT>
 using GeoGrad = Geo<K, L, H, W, P, NT, 0, 2>;
 
-// Layout of the tile forward: trimmed halos below the LDS-analysed levels.
+// Layout of the tile forward and fused backward: trimmed halos below the
+// LDS-analysed levels.
 template <int K, int LT, int TH, int TW, int NT>
-using GeoTileApply = Geo<K, LT, TH, TW, 1, NT, LT, 4, true>;
+using GeoTileTrim = Geo<K, LT, TH, TW, 1, NT, LT, 4, true>;
 
 // One lane's tile: array level, plane, subband, tile row group and column
 // strip.  Decoded once; the lane keeps it on every group of planes.
@@ -2126,7 +2127,7 @@ __global__ __launch_bounds__(NT) void k_tile_apply(
     const T* __restrict__ in, const T* __restrict__ wb, const T* __restrict__ bb,
     const T* __restrict__ sb, const T* __restrict__ ww, const T* __restrict__ sw,
     const float* __restrict__ deep, T* __restrict__ out, int B, int C, int Hp, int Wp) {
-    using G = GeoTileApply<K, LT, TH, TW, NT>;
+    using G = GeoTileTrim<K, LT, TH, TW, NT>;
     using F = Fetch<G, T>;
     constexpr int KK = G::KK, Q = G::Q, R = G::R;
     extern __shared__ float lds[];
@@ -2349,12 +2350,12 @@ constexpr int tile_bwd1_waves() {
 // ran twice as long.
 template <int K, int LT, int TH, int TW, int NT, typename T>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(
-    tile_bwd1_waves<GeoTileApply<K, LT, TH, TW, NT>>()))) void k_tile_bwd1(
+    tile_bwd1_waves<GeoTileTrim<K, LT, TH, TW, NT>>()))) void k_tile_bwd1(
     const T* __restrict__ x, const T* __restrict__ dy, const T* __restrict__ wb,
     const T* __restrict__ sb, const T* __restrict__ ww, const T* __restrict__ sw,
     const float* __restrict__ deep, T* __restrict__ dx, float* __restrict__ part,
     float* __restrict__ px, int B, int C, int Hp, int Wp, int upw, int npart) {
-    using G = GeoTileApply<K, LT, TH, TW, NT>;
+    using G = GeoTileTrim<K, LT, TH, TW, NT>;
     using FX = Fetch<G, T, false>;  // x: the tile's core
     using FD = Fetch<G, T, true>;   // dy: the core and its halos
     constexpr int KK = G::KK, Q = G::Q, R = G::R;

@@ -36,8 +36,8 @@ template <int K, int LT, typename T>
 TileVariant make_tile_variant(int dtype) {
     constexpr int ATW = apply_tile_w(K), BTW = bwd_tile_w(K);
     using G = dev::Geo<K, LT, kTileH, kTileW, 1, kTileNT, LT>;
-    using GA = dev::GeoTileApply<K, LT, kTileH, ATW, kTileNT>;
-    using GB = dev::GeoTileApply<K, LT, kTileH, BTW, kTileNT>;
+    using GA = dev::GeoTileTrim<K, LT, kTileH, ATW, kTileNT>;
+    using GB = dev::GeoTileTrim<K, LT, kTileH, BTW, kTileNT>;
     return TileVariant{
         K, LT, dtype, kTileH, kTileW, kTileH, ATW, BTW, kTileNT,
         reinterpret_cast<const void*>(&dev::k_tile_apply<K, LT, kTileH, ATW, kTileNT, T, false>),
