@@ -1368,6 +1368,13 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(
     const bool full = nrows == Q && ncols == R;
     const int dst = win + G::p * pitch + G::p;  // tile's first output element
 
+    // fp16: the filters are reloaded from LDS before each group's conv
+    // instead of living in registers across groups, which takes the fp16
+    // forward from 152 to 127 VGPRs (no spills in its ragged form, which
+    // spilled 148 bytes per lane: 55 x 55 forward 102 -> 64.5 us; stage 1
+    // fp16 85.6 -> 84.0 us).  fp32 keeps them: on small planes the reload is
+    // per-group work for few FMAs (28 x 28: 29.6 -> 30.9 us).
+    constexpr bool kReload = std::is_same<T, __half>::value;
     float w[KK];
     float init = 0.f;
     int cur = -1;
@@ -1377,8 +1384,10 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(
         if (c != cur) {
             fold_weights<G, T, FLIP>(wf, wb, bb, sb, ww, sw, C, c, tid);
             __syncthreads();
+            if constexpr (!kReload) {
 #pragma unroll
-            for (int t = 0; t < KK; ++t) w[t] = wf[wsrc + t];
+                for (int t = 0; t < KK; ++t) w[t] = wf[wsrc + t];
+            }
             init = job.lvl == 0 ? wf[G::NWF - 1] : 0.f;
             cur = c;
         }
@@ -1391,7 +1400,13 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(
         });
         float acc[Q][R];
         wave_prio<PrioPlaneApply::conv>();
-        if (job.on) conv_tile<K, Q, R>(lds + win, pitch, w, init, acc);
+        if (job.on) {
+            if constexpr (kReload) {
+#pragma unroll
+                for (int t = 0; t < KK; ++t) w[t] = wf[wsrc + t];
+            }
+            conv_tile<K, Q, R>(lds + win, pitch, w, init, acc);
+        }
         wave_prio<PrioPlaneApply::store>();
         // the next group's loads fly during write-back, synthesis and store
         if (q + 1 < q1) fx.template issue_buf<RAG>(in, ((q + 1) % ngroups) * P, B, C, (q + 1) / ngroups, tid, rg);
