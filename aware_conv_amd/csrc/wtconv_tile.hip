@@ -71,6 +71,37 @@ struct DeepLayout {
     }
 };
 
+// e / d and e % d for 0 <= e < 2^22 and d >= 1, from d's fp32 reciprocal.
+// The two roundings (reciprocal, product) are each within 2^-23 relative,
+// so on a quotient below 2^22 the truncated product is off by at most one,
+// which the remainder's sign corrects.  The deep phases index an element
+// per item; the integer division this replaces cost them more VALU issue
+// than the arithmetic on the element.
+struct DivMod {
+    int d;
+    float r;
+    __device__ explicit DivMod(int d_) : d(d_), r(1.f / float(d_)) {}
+    __device__ int2 operator()(int e) const {
+        int q = int(float(e) * r), m = e - q * d;
+        if (m < 0) {
+            --q;
+            m += d;
+        } else if (m >= d) {
+            ++q;
+            m -= d;
+        }
+        return make_int2(q, m);
+    }
+};
+
+// n floats from a (16-byte aligned) set to zero, 16 bytes per store.
+__device__ void zero_lds(float* a, int n, int tid, int nt) {
+    const int n4 = n >> 2;
+    float4* a4 = reinterpret_cast<float4*>(a);
+    for (int i = tid; i < n4; i += nt) a4[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int i = 4 * n4 + tid; i < n; i += nt) a[i] = 0.f;
+}
+
 // P = U^LT_LL of every plane: P[i][j] is the sum of the plane's 2^LT x 2^LT
 // block (i, j).  One workgroup per row of P; each lane sums a 4-column strip
 // of the block rows with one vector load per row, then the n/4 lanes of a
@@ -118,23 +149,25 @@ __global__ __launch_bounds__(128) void k_box_sums(const T* __restrict__ src,
 __device__ void load_level1(const float* __restrict__ Pp, const DeepLayout& D, float* lds,
                             int shift, int tid, int nt) {
     constexpr int U = 4;
-    const int h = D.h(1), w = D.w(1), n = h * w, A = D.barr(1);
+    const int h = D.h(1), w = D.w(1), n = h * w, A = D.barr(1), wp = D.wp;
+    const int base = D.u(1, 0, 0, 0) + shift, bp = D.bp(1);
+    const DivMod by_w(w);
     for (int e0 = tid; e0 < n; e0 += U * nt) {
         float2 top[U], bot[U];
+        int2 ij[U];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            const int e = min(e0 + u * nt, n - 1);
-            const float* q = Pp + size_t(2 * (e / w)) * D.wp + 2 * (e % w);
+            ij[u] = by_w(min(e0 + u * nt, n - 1));
+            const float* q = Pp + size_t(2 * ij[u].x) * wp + 2 * ij[u].y;
             top[u] = *reinterpret_cast<const float2*>(q);
-            bot[u] = *reinterpret_cast<const float2*>(q + D.wp);
+            bot[u] = *reinterpret_cast<const float2*>(q + wp);
         }
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            const int e = e0 + u * nt;
-            if (e >= n) break;
+            if (e0 + u * nt >= n) break;
             const float s0 = top[u].x + top[u].y, d0 = top[u].x - top[u].y;
             const float s1 = bot[u].x + bot[u].y, d1 = bot[u].x - bot[u].y;
-            const int o = D.u(1, 0, e / w, e % w) + shift;
+            const int o = base + ij[u].x * bp + ij[u].y;
             lds[o] = s0 + s1;
             lds[o + A] = d0 + d1;
             lds[o + 2 * A] = s0 - s1;
@@ -146,13 +179,15 @@ __device__ void load_level1(const float* __restrict__ Pp, const DeepLayout& D, f
 // Levels m = 2..LD of P: unnormalised Haar butterflies of the LL above.
 __device__ void deep_analysis(const DeepLayout& D, float* lds, int shift, int tid, int nt) {
     for (int m = 2; m <= D.LD; ++m) {
-        const int h = D.h(m), w = D.w(m);
+        const int h = D.h(m), w = D.w(m), sp = D.bp(m - 1), dp = D.bp(m), A = D.barr(m);
+        const int sb = D.u(m - 1, 0, 0, 0) + shift, db = D.u(m, 0, 0, 0) + shift;
+        const DivMod by_w(w);
         for (int e = tid; e < h * w; e += nt) {
-            const int i = e / w, j = e % w;
-            const int src = D.u(m - 1, 0, 2 * i, 2 * j) + shift, sp = D.bp(m - 1);
+            const int2 ij = by_w(e);
+            const int src = sb + 2 * ij.x * sp + 2 * ij.y;
             const float a = lds[src], b = lds[src + 1], c = lds[src + sp], d = lds[src + sp + 1];
             const float s0 = a + b, d0 = a - b, s1 = c + d, d1 = c - d;
-            const int o = D.u(m, 0, i, j) + shift, A = D.barr(m);
+            const int o = db + ij.x * dp + ij.y;
             lds[o] = s0 + s1;
             lds[o + A] = d0 + d1;
             lds[o + 2 * A] = s0 - s1;
@@ -174,10 +209,12 @@ __global__ __launch_bounds__(kDeepNT) void k_deep_apply(
     const int b = blockIdx.x / C, c = blockIdx.x % C;
     constexpr int KK = K * K, RS = kDeepRS;
     const DeepLayout D{Hp >> LT, Wp >> LT, K / 2, L - LT, KK};
-    for (int i = tid; i < D.end_apply(); i += nt) lds[i] = 0.f;
-    __syncthreads();
-    // folded filters of absolute levels LT+1..L: gamma * 4^-l * K (rotated
-    // for the input gradient)
+    // the bordered arrays start at zero: their borders and the row padding
+    // past a level's width are the convs' zero padding (the interiors, and
+    // every result read later, are written below)
+    zero_lds(lds + D.uoff(1), D.uoff(D.LD + 1) - D.uoff(1), tid, nt);
+    // folded filters of absolute levels LT+1..L, below the bordered arrays:
+    // gamma * 4^-l * K (rotated for the input gradient)
     for (int i = tid; i < D.LD * 4 * KK; i += nt) {
         const int ms = i / KK, t = i % KK, m = ms / 4, s = ms % 4;
         const int la = LT + m + 1;
@@ -185,21 +222,26 @@ __global__ __launch_bounds__(kDeepNT) void k_deep_apply(
         const int tt = FLIP ? KK - 1 - t : t;
         lds[i] = to_f(sw[gi]) * ldexpf(1.f, -2 * la) * to_f(ww[gi * KK + tt]);
     }
+    __syncthreads();
     load_level1(P + (size_t(b) * C + c) * D.hp * D.wp, D, lds, 0, tid, nt);
     __syncthreads();
     deep_analysis(D, lds, 0, tid, nt);
     // subband convs
     for (int m = 1; m <= D.LD; ++m) {
         const int h = D.h(m), w = D.w(m), nseg = (w + RS - 1) / RS;
+        const int bpm = D.bp(m), A = D.barr(m), um = D.uoff(m), rpm = D.rp(m), cm = D.coff(m);
+        const DivMod by_seg(nseg), by_h(h);
         for (int e = tid; e < 4 * h * nseg; e += nt) {
-            const int s = e / (h * nseg), i = (e / nseg) % h, j0 = (e % nseg) * RS;
+            const int2 rs = by_seg(e), si = by_h(rs.x);  // rs.x = s * h + i
+            const int s = si.x, i = si.y, j0 = rs.y * RS;
             const float* wk = lds + (m - 1) * 4 * KK + s * KK;
             float acc[RS];
 #pragma unroll
             for (int r = 0; r < RS; ++r) acc[r] = 0.f;
 #pragma unroll
             for (int uu = 0; uu < K; ++uu) {
-                const float* src = lds + D.u(m, s, i + uu - D.p, j0 - D.p);
+                // row i + uu - p from column j0 - p of the bordered array
+                const float* src = lds + um + s * A + (i + uu) * bpm + j0;
                 float row[RS + K - 1];
 #pragma unroll
                 for (int t = 0; t < RS + K - 1; ++t) row[t] = src[t];
@@ -210,7 +252,7 @@ __global__ __launch_bounds__(kDeepNT) void k_deep_apply(
                     for (int r = 0; r < RS; ++r) acc[r] = fmaf(wv, row[r + vv], acc[r]);
                 }
             }
-            float* o = lds + D.coff(m) + (s * h + i) * D.rp(m) + j0;
+            float* o = lds + cm + rs.x * rpm + j0;
 #pragma unroll
             for (int r = 0; r < RS; ++r)
                 if (j0 + r < w) o[r] = acc[r];
@@ -218,28 +260,42 @@ __global__ __launch_bounds__(kDeepNT) void k_deep_apply(
     }
     __syncthreads();
     // fold level m into the LL of level m-1, deepest first
+    // (one item per coarse position: its four subbands give the 2 x 2 fine
+    // block, (LL + sy HL) + sx (LH + sy HH) with sy, sx = -1 on odd rows,
+    // columns; levels halve exactly, the plane being a multiple of 2^L)
     for (int m = D.LD; m >= 2; --m) {
-        const int h = D.h(m - 1), w = D.w(m - 1), hc = D.h(m), rc = D.rp(m);
-        for (int e = tid; e < h * w; e += nt) {
-            const int i = e / w, j = e % w;
-            const float* cs = lds + D.coff(m) + (i >> 1) * rc + (j >> 1);
-            const int A = hc * rc;
-            const float sy = (i & 1) ? -1.f : 1.f, sx = (j & 1) ? -1.f : 1.f;
-            const float e0 = fmaf(sy, cs[2 * A], cs[0]), f0 = fmaf(sy, cs[3 * A], cs[A]);
-            lds[D.coff(m - 1) + i * D.rp(m - 1) + j] += fmaf(sx, f0, e0);
+        const int hc = D.h(m), wc = D.w(m), rc = D.rp(m), A = hc * rc, rf = D.rp(m - 1);
+        const float* cm = lds + D.coff(m);
+        float* fm = lds + D.coff(m - 1);
+        const DivMod by_w(wc);
+        for (int e = tid; e < hc * wc; e += nt) {
+            const int2 ij = by_w(e);
+            const float* cs = cm + ij.x * rc + ij.y;
+            const float ll = cs[0], lh = cs[A], hl = cs[2 * A], hh = cs[3 * A];
+            const float e0 = ll + hl, f0 = lh + hh, e1 = ll - hl, f1 = lh - hh;
+            float* f = fm + 2 * ij.x * rf + 2 * ij.y;
+            f[0] += e0 + f0;
+            f[1] += e0 - f0;
+            f[rf] += e1 + f1;
+            f[rf + 1] += e1 - f1;
         }
         __syncthreads();
     }
     // expand level 1 over P's grid
+    // (the same 2 x 2 blocks, two 8-byte stores each: P's width is even)
     {
-        const int hc = D.h(1), rc = D.rp(1), A = hc * rc;
-        float* o = deep + (size_t(b) * C + c) * D.hp * D.wp;
-        for (int e = tid; e < D.hp * D.wp; e += nt) {
-            const int i = e / D.wp, j = e % D.wp;
-            const float* cs = lds + D.coff(1) + (i >> 1) * rc + (j >> 1);
-            const float sy = (i & 1) ? -1.f : 1.f, sx = (j & 1) ? -1.f : 1.f;
-            const float e0 = fmaf(sy, cs[2 * A], cs[0]), f0 = fmaf(sy, cs[3 * A], cs[A]);
-            o[e] = fmaf(sx, f0, e0);
+        const int hc = D.h(1), wc = D.w(1), rc = D.rp(1), A = hc * rc, wp = D.wp;
+        const float* cm = lds + D.coff(1);
+        float* o = deep + (size_t(b) * C + c) * D.hp * wp;
+        const DivMod by_w(wc);
+        for (int e = tid; e < hc * wc; e += nt) {
+            const int2 ij = by_w(e);
+            const float* cs = cm + ij.x * rc + ij.y;
+            const float ll = cs[0], lh = cs[A], hl = cs[2 * A], hh = cs[3 * A];
+            const float e0 = ll + hl, f0 = lh + hh, e1 = ll - hl, f1 = lh - hh;
+            float* q = o + size_t(2 * ij.x) * wp + 2 * ij.y;
+            *reinterpret_cast<float2*>(q) = make_float2(e0 + f0, e0 - f0);
+            *reinterpret_cast<float2*>(q + wp) = make_float2(e1 + f1, e1 - f1);
         }
     }
 }
@@ -260,7 +316,8 @@ __global__ __launch_bounds__(kDeepNT) void k_deep_bww(const float* __restrict__ 
     constexpr int KK = K * K, NCH = kDeepNCH;
     const DeepLayout D{Hp >> LT, Wp >> LT, K / 2, L - LT, KK};
     const int shift = D.dy_shift();
-    for (int i = tid; i < D.end_bww(); i += nt) lds[i] = 0.f;
+    // both bordered array sets (x's, then dy's) start at zero
+    zero_lds(lds + D.uoff(1), D.end_bww() - D.uoff(1), tid, nt);
     __syncthreads();
     const size_t po = (size_t(b) * C + c) * D.hp * D.wp;
     load_level1(px + po, D, lds, 0, tid, nt);
