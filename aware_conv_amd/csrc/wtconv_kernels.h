@@ -1983,81 +1983,120 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(
 // rows.nwg = 0, `nchunk` rows at (chunk * C + c); otherwise the LinearRows
 // rows of c.  nchunk = 0 (and rows.nwg = 0) gives zero gradients.  The row
 // sums and the products are taken in fp64 and rounded once to the output
-// type.  Every device-memory read (scales, bias, filters, rows) is issued
-// before the workgroup's one barrier, so the kernel waits on one round trip
-// to memory, not one per dependent step.
-template <typename T>
-__global__ __launch_bounds__(256) void k_bww_final(
-    const float* __restrict__ part, int nchunk, LinearRows rows, int C, int K, int L,
+// type.
+// The workgroup is a chain of memory round trips, so it is laid out to
+// have few: every device-memory read (rows, filters, scales, beta, bias) is
+// issued by the lanes in one pass before the one barrier (beta and the bias
+// by two lanes with the scales: read as branch-guarded scalars each was a
+// round trip of its own ahead of the rows), and after it each thread
+// computes one output and stores it once, last (stores count in vmcnt: a
+// thread that stored and then went on to another output waited at its next
+// vmcnt wait for the store's write acknowledgement, one round trip per
+// output group).  The kernel size is a template argument so that the dot
+// products unroll.  Up to kFinalNT threads: one per column of the rows and
+// one per output (547 outputs at 512², L = 5, k = 5, in one pass).
+constexpr int kFinalNT = 1024, kFinalRows = 16;
+
+// Threads of k_bww_final for kernel size k and L levels: one per row column
+// and one per output, in whole wavefronts.
+__host__ __device__ constexpr int bww_final_threads(int k, int L) {
+    const int KK = k * k, n = KK + 2 + 4 * L * KK + 4 * L;  // >= the row columns
+    return n < kFinalNT ? (n + 63) / 64 * 64 : kFinalNT;
+}
+
+template <typename T, int K>
+__global__ __launch_bounds__(kFinalNT) void k_bww_final(
+    const float* __restrict__ part, int nchunk, LinearRows rows, int C, int L,
     const T* __restrict__ wb, const T* __restrict__ bb, const T* __restrict__ sb,
     const T* __restrict__ ww, const T* __restrict__ sw, T* __restrict__ dwb,
     T* __restrict__ dbb, T* __restrict__ dsb, T* __restrict__ dww, T* __restrict__ dsw) {
-    // [NPART] row sums (fp64), then the filters Kb [KK], K [4 L KK] and the
-    // scales gamma [4 L] (fp32)
+    // [NPART] row sums (fp64), then the filters Kb [KK], K [4 L KK], the
+    // scales gamma [4 L], beta and the bias (fp32)
     extern __shared__ double gsum[];
-    const int KK = K * K, NPART = KK + 1 + 4 * L * KK, NF = KK + 4 * L * KK, NS = 4 * L;
+    constexpr int KK = K * K;
+    const int NPART = KK + 1 + 4 * L * KK, NF = KK + 4 * L * KK, NS = 4 * L;
     const int c = blockIdx.x, tid = threadIdx.x, nt = blockDim.x;
     float* kf = reinterpret_cast<float*>(gsum + NPART);
     float* gam = kf + NF;
-    // sb == NULL: no base scale (the plain depthwise conv), no dsb
-    const float beta = sb ? to_f(sb[c]) : 1.f;
-    const float bias = dsb ? to_f(bb[c]) : 0.f;
     const bool lin = rows.nwg > 0;
     const int nrow = lin ? rows.count(c) : nchunk;
     const size_t base = lin ? size_t(c) * rows.rmax : size_t(c);
     const size_t step = lin ? 1 : size_t(C);
-    const int nmax = NF > NPART ? NF : NPART;
+    const int nmax = NF > NPART ? NF : NPART;  // >= NS + 2
     for (int i = tid; i < nmax; i += nt) {
-        float f = 0.f, sc = 0.f;
-        if (i < KK) {
-            f = to_f(wb[size_t(c) * KK + i]);
-        } else if (i < NF) {
-            const int j = i - KK, ls = j / KK, t = j % KK, l = ls >> 2, s = ls & 3;
-            f = to_f(ww[((size_t(l) * C + c) * 4 + s) * KK + t]);
-        }
-        if (i < NS) sc = to_f(sw[(size_t(i >> 2) * C + c) * 4 + (i & 3)]);
+        // every read below is unconditional, from an address chosen per lane
+        // (a valid stand-in where the lane has no value), and selected after:
+        // reads in the arms of branches were each waited for at the join,
+        // one round trip apiece, before the rows were even issued
+        const int fi = i < NF ? i : NF - 1;
+        const int j = fi < KK ? 0 : fi - KK, ls = j / KK, t = j - ls * KK;
+        const T* fsrc = fi < KK ? wb + size_t(c) * KK + fi
+                                : ww + ((size_t(ls >> 2) * C + c) * 4 + (ls & 3)) * KK + t;
+        // scales gamma, then beta (sb == NULL: no base scale, the plain
+        // depthwise conv, and no dsb) and the bias
+        const T* ssrc = i < NS                 ? sw + (size_t(i >> 2) * C + c) * 4 + (i & 3)
+                        : (i == NS && sb)      ? sb + c
+                        : (i == NS + 1 && dsb) ? bb + c
+                                               : wb + size_t(c) * KK;
+        const float f = to_f(*fsrc), sv = to_f(*ssrc);
         double acc = 0.0;
         if (i < NPART) {
-            // eight rows per round, loaded unconditionally (a row index past
-            // the last reads the last row again and is masked), so that the
-            // eight loads are in flight together
-            for (int ch0 = 0; ch0 < nrow; ch0 += 8) {
-                float v[8];
+            // kFinalRows rows per round, loaded unconditionally (a row index
+            // past the last reads the last row again and is masked), so that
+            // the round's loads are in flight together; added in row order
+            for (int ch0 = 0; ch0 < nrow; ch0 += kFinalRows) {
+                float v[kFinalRows];
 #pragma unroll
-                for (int u = 0; u < 8; ++u) {
+                for (int u = 0; u < kFinalRows; ++u) {
                     const int r = min(ch0 + u, nrow - 1);
                     v[u] = part[(base + size_t(r) * step) * NPART + i];
                 }
 #pragma unroll
-                for (int u = 0; u < 8; ++u) acc += ch0 + u < nrow ? double(v[u]) : 0.0;
+                for (int u = 0; u < kFinalRows; ++u) acc += ch0 + u < nrow ? double(v[u]) : 0.0;
             }
             gsum[i] = acc;
         }
+        // (selected only now: the compiler makes the selects branches, and
+        // a branch on a value waits for its read)
+        const float sc = i < NS ? sv : i == NS ? (sb ? sv : 1.f) : (dsb ? sv : 0.f);
         if (i < NF) kf[i] = f;
-        if (i < NS) gam[i] = sc;
+        if (i < NS + 2) gam[i] = sc;
     }
     __syncthreads();
-    for (int i = tid; i < KK; i += nt) dwb[size_t(c) * KK + i] = from_f<T>(float(beta * gsum[i]));
-    if (tid == 0) {
-        dbb[c] = from_f<T>(float(beta * gsum[KK]));
-        if (dsb) {
-            double dot = double(bias) * gsum[KK];
-            for (int t = 0; t < KK; ++t) dot += double(kf[t]) * gsum[t];
-            dsb[c] = from_f<T>(float(dot));
+    const float beta = gam[NS], bias = gam[NS + 1];
+    // outputs: dKb [KK], dbias, dbeta, dK [4 L KK], dgamma [4 L]
+    const int nwv = 4 * L * KK, nout = KK + 2 + nwv + NS;
+    for (int o = tid; o < nout; o += nt) {
+        T* dst = nullptr;
+        double v = 0.0;
+        if (o < KK) {
+            dst = dwb + size_t(c) * KK + o;
+            v = beta * gsum[o];
+        } else if (o == KK) {
+            dst = dbb + c;
+            v = beta * gsum[KK];
+        } else if (o == KK + 1) {
+            if (dsb) {
+                double dot = double(bias) * gsum[KK];
+#pragma unroll
+                for (int t = 0; t < KK; ++t) dot += double(kf[t]) * gsum[t];
+                dst = dsb + c;
+                v = dot;
+            }
+        } else if (o < KK + 2 + nwv) {
+            const int i = o - KK - 2, ls = i / KK, t = i % KK, l = ls >> 2, s = ls & 3;
+            dst = dww + ((size_t(l) * C + c) * 4 + s) * KK + t;
+            v = double(gam[ls]) * ldexp(1.0, -2 * (l + 1)) * gsum[KK + 1 + i];
+        } else {
+            const int i = o - KK - 2 - nwv, l = i >> 2, s = i & 3;
+            double dot = 0.0;
+#pragma unroll
+            for (int t = 0; t < KK; ++t)
+                dot += double(kf[KK + i * KK + t]) * gsum[KK + 1 + i * KK + t];
+            dst = dsw + (size_t(l) * C + c) * 4 + s;
+            v = ldexp(1.0, -2 * (l + 1)) * dot;
         }
-    }
-    for (int i = tid; i < 4 * L * KK; i += nt) {
-        const int ls = i / KK, t = i % KK, l = ls >> 2, s = ls & 3;
-        const size_t gi = (size_t(l) * C + c) * 4 + s;
-        dww[gi * KK + t] = from_f<T>(float(double(gam[ls]) * ldexp(1.0, -2 * (l + 1)) *
-                                           gsum[KK + 1 + i]));
-    }
-    for (int i = tid; i < NS; i += nt) {
-        const int l = i >> 2, s = i & 3;
-        const size_t gi = (size_t(l) * C + c) * 4 + s;
-        double dot = 0.0;
-        for (int t = 0; t < KK; ++t) dot += double(kf[KK + i * KK + t]) * gsum[KK + 1 + i * KK + t];
-        dsw[gi] = from_f<T>(float(ldexp(1.0, -2 * (l + 1)) * dot));
+        if (dst) *dst = from_f<T>(float(v));
     }
 }
 

@@ -111,18 +111,35 @@ hipError_t plane_apply(const wtconv_shape& s, const void* in, const Params& p, v
 }
 
 namespace {
+template <typename T, int K>
+hipError_t launch_final_k(const wtconv_shape& s, const float* part, int nchunk,
+                          const LinearRows& rows, const Params& p, const Grads& g,
+                          hipStream_t stream) {
+    // fp64 row sums [NPART], fp32 filters [KK + 4 L KK], scales [4 L],
+    // beta and the bias
+    const size_t KK = size_t(K) * K, L = size_t(s.L);
+    const size_t lds = sizeof(double) * (KK + 1 + 4 * L * KK) +
+                       sizeof(float) * (KK + 4 * L * KK + 4 * L + 2);
+    // idle waves would still cost their launch and the barrier
+    const unsigned nt = unsigned(bww_final_threads(K, s.L));
+    hipLaunchKernelGGL((k_bww_final<T, K>), dim3(s.C), dim3(nt), lds, stream, part, nchunk,
+                       rows, s.C, s.L, (const T*)p.w_base, (const T*)p.b_base,
+                       (const T*)p.s_base, (const T*)p.w_wav, (const T*)p.s_wav,
+                       (T*)g.dw_base, (T*)g.db_base, (T*)g.ds_base, (T*)g.dw_wav, (T*)g.ds_wav);
+    return hipGetLastError();
+}
+
 template <typename T>
 hipError_t launch_final(const wtconv_shape& s, const float* part, int nchunk,
                         const LinearRows& rows, const Params& p, const Grads& g,
                         hipStream_t stream) {
-    // fp64 row sums [NPART], fp32 filters [KK + 4 L KK] and scales [4 L]
-    const size_t KK = size_t(s.k) * s.k, L = size_t(s.L);
-    const size_t lds = sizeof(double) * (KK + 1 + 4 * L * KK) + sizeof(float) * (KK + 4 * L * KK + 4 * L);
-    hipLaunchKernelGGL(k_bww_final<T>, dim3(s.C), dim3(256), lds, stream, part, nchunk, rows, s.C,
-                       s.k, s.L, (const T*)p.w_base, (const T*)p.b_base, (const T*)p.s_base,
-                       (const T*)p.w_wav, (const T*)p.s_wav, (T*)g.dw_base, (T*)g.db_base,
-                       (T*)g.ds_base, (T*)g.dw_wav, (T*)g.ds_wav);
-    return hipGetLastError();
+    switch (s.k) {
+        case 1: return launch_final_k<T, 1>(s, part, nchunk, rows, p, g, stream);
+        case 3: return launch_final_k<T, 3>(s, part, nchunk, rows, p, g, stream);
+        case 5: return launch_final_k<T, 5>(s, part, nchunk, rows, p, g, stream);
+        case 7: return launch_final_k<T, 7>(s, part, nchunk, rows, p, g, stream);
+        default: return hipErrorInvalidValue;
+    }
 }
 }  // namespace
 

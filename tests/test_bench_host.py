@@ -23,7 +23,8 @@ import bench  # noqa: E402
     ("void wtc::dev::k_deep_apply<float, 5, true>(...)", False, "wtconv_bwd_input"),
     ("void wtc::dev::k_plane_bww<5, 2, 56, 56, 1, 256, float, false>(...)", False, "wtconv_bwd_weight"),
     ("void wtc::dev::k_deep_bww<5>(...)", True, "wtconv_bwd"),
-    ("void wtc::dev::k_bww_final<float>(...)", False, "wtconv_bwd_weight"),
+    ("void wtc::dev::k_bww_final<float, 5>(...)", False, "wtconv_bwd_weight"),
+    ("void wtc::dev::k_bww_final<__half, 7>(...)", True, "wtconv_bwd"),
     ("void wtc::dev::k_plane_bwd<5, 2, 56, 56, 1, 256, float, false, false>(...)", True, "wtconv_bwd"),
     ("void wtc::dev::k_plane_bwd1<5, 2, 56, 56, 1, 256, float, false, true, false>(...)", True, "wtconv_bwd"),
     ("void wtc::dev::k_plane_bwd1<5, 2, 56, 56, 1, 256, float, true, true, true>(...)", False, "wtconv_bwd"),
