@@ -1276,6 +1276,15 @@ __device__ __forceinline__ void wave_prio() {
     __builtin_amdgcn_sched_barrier(0);
 }
 
+// Wait until every vector-memory access of this wave has completed.  gfx9
+// counts loads and stores in one counter that drains in issue order, so the
+// wait for the next group's prefetched loads, placed after this group's
+// stores, also waits for those stores' write acknowledgements.  Called just
+// before the stores (the loads, issued a write-back and a synthesis earlier,
+// have arrived), it leaves no load outstanding behind them, and the next
+// commit does not wait at all.
+__device__ __forceinline__ void drain_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
 // Phase priorities (commit and analysis, conv, write-back to store) of the
 // kernels that gain from them, chosen among 12 settings per kernel (stage 1
 // unless named, gated per-call times, one box):
@@ -1378,6 +1387,9 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(
     float w[KK];
     float init = 0.f;
     int cur = -1;
+    // the first group's loads, so that no path into the loop carries loads
+    // whose wait would fall behind stores (drain_vmem)
+    drain_vmem();
     for (int q = q0; q < q1; ++q) {
         const int c = q / ngroups;
         const int b0 = (q % ngroups) * P;
@@ -1432,6 +1444,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(
             cascade_level<G, L - decltype(lc)::value>(lds, tid);
             __syncthreads();
         });
+        drain_vmem();
         if constexpr (RAG)
             final_store_rag<G, T>(lds, out, b0, B, C, c, tid, rg);
         else
@@ -1692,6 +1705,9 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void k_
         cur = c;
     }
 
+    // the first loads, so that no path into the loop carries loads whose
+    // wait would fall behind stores (drain_vmem)
+    drain_vmem();
     for (int it = 0; it < nitems; ++it) {
         const int b0 = grp * P;
         if (CROSS && c != cur) {
@@ -1774,6 +1790,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void k_
             cascade_level<G, L - decltype(lc)::value>(ldy, tid);
             __syncthreads();
         });
+        drain_vmem();
         if constexpr (RAG)
             final_store_rag<G, T>(ldy, dx, b0, B, C, c, tid, rg);
         else
@@ -1872,6 +1889,9 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(
         cur = c;
     }
 
+    // the first group's loads, so that no path into the loop carries loads
+    // whose wait would fall behind stores (drain_vmem)
+    drain_vmem();
     for (int it = 0; it < nitems; ++it) {
         const int b0 = grp * P;
         int t = tid;
@@ -1964,6 +1984,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(
                 cascade_level<G, L - decltype(lc)::value>(lds, t);
                 __syncthreads();
             });
+            drain_vmem();
             if constexpr (RAG)
                 final_store_rag<G, T>(lds, dx, b0, B, C, c, t, rg);
             else
@@ -2211,6 +2232,9 @@ __global__ __launch_bounds__(NT) void k_tile_apply(
     float w[KK];
     float init = 0.f;
     int cur = -1;
+    // the first loads, so that no path into the loop carries loads whose
+    // wait would fall behind stores (drain_vmem)
+    drain_vmem();
     for (long q = q0; q < q1; ++q) {
         const int c = cu.c, b = cu.b, y0 = cu.ty * TH, x0 = cu.tx * TW;
         const TileCursor nx = cu.next(B, nty, ntx);
@@ -2253,6 +2277,7 @@ __global__ __launch_bounds__(NT) void k_tile_apply(
             cascade_level<G, LT - decltype(lc)::value>(lds, tid);
             __syncthreads();
         });
+        drain_vmem();
         final_store<G, T>(lds, out, b, B, C, c, tid, y0, x0, Hp, Wp);
         cu = nx;
         __syncthreads();
@@ -2450,6 +2475,9 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(
     for (int t = 0; t < KK; ++t) gacc[t] = 0.f;
     float sdy = 0.f;
 
+    // the first loads, so that no path into the loop carries loads whose
+    // wait would fall behind stores (drain_vmem)
+    drain_vmem();
     for (int u = u0; u < u1; ++u) {
         int t = tid;
         const int b = cu.b, y0 = cu.ty * TH, x0 = cu.tx * TW;
@@ -2529,6 +2557,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(
             cascade_level<G, LT - decltype(lc)::value>(lds, t);
             __syncthreads();
         });
+        drain_vmem();  // (the next dy is loaded after the store, by design)
         final_store<G, T>(lds, dx, b, B, C, c, t, y0, x0, Hp, Wp);
         asm volatile("" : "+v"(t));
         fd.issue_tile_buf(dy, more ? nx.b : B, B, C, c, t, nx.ty * TH, nx.tx * TW, Hp, Wp);
