@@ -2259,7 +2259,12 @@ __global__ __launch_bounds__(NT) void k_tile_apply(
         wave_prio<PrioTileApply::conv>();
         if (job.on) conv_tile<K, Q, R>(lds + win, pitch, w, init, acc);
         wave_prio<PrioTileApply::store>();
-        if (q + 1 < q1) fx.issue_tile_buf(in, nx.b, B, C, nx.c, tid, nx.ty * TH, nx.tx * TW, Hp, Wp);
+        // unconditional (past the range it covers an empty buffer range:
+        // b = B), so that every path carries the same loads: with the load
+        // on one path only, the wait for the deeper levels' value after it
+        // could only be vmcnt(0), a wait for this prefetch as well
+        const bool more = q + 1 < q1;
+        fx.issue_tile_buf(in, more ? nx.b : B, B, C, nx.c, tid, nx.ty * TH, nx.tx * TW, Hp, Wp);
         __syncthreads();
         if (job.on) {
 #pragma unroll
@@ -2484,6 +2489,11 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(
         const TileCursor nx = cu.next(B, nty, ntx);
         wave_prio<PrioTileBwd1::commit_x>();
         fx.template commit<true, false>(lds, t);
+        // the deeper levels' contribution, in flight through x's analysis
+        // (fetched after the dy analysis it was waited for at once, before
+        // the conv)
+        DeepRegs<G> dr;
+        if (deep) fetch_deep<G>(dr, deep, b, C, c, y0, x0, Hp, Wp, t);
         __syncthreads();
         static_for<FX::LEVELS + 1, LT + 1>([&](auto lc) {
             analysis_level<G, decltype(lc)::value, false>(lds, t);
@@ -2498,19 +2508,15 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(
                     const float v = lds[dst + qq * pitch + j];
                     ux[qq][j] = (full || (qq < nrows && j < ncols)) ? v : 0.f;
                 }
-        if (px) {
-            // the core of U^LT_LL(x): the tile's share of the box sums that
-            // the deeper levels' weight gradient starts from
-            constexpr int h = G::hl(LT), wl = G::wl(LT);
-            const int hd = Hp >> LT, wd = Wp >> LT;
-            if (t < h * wl) {
-                const int i = t / wl, j = t % wl;
-                const int gy = (y0 >> LT) + i, gx = (x0 >> LT) + j;
-                if (gy < hd && gx < wd)
-                    px[(size_t(b) * C + c) * hd * wd + size_t(gy) * wd + gx] =
-                        lds[G::uidx(LT, 0, 0, i, j)];
-            }
-        }
+        // the core of U^LT_LL(x): the tile's share of the box sums that the
+        // deeper levels' weight gradient starts from, held until the tile's
+        // stores (stored here, it left a store pending through dy's commit
+        // and the conv: their waits for loads then waited for it, and for
+        // the deeper levels' fetch right after its issue)
+        constexpr int pxh = G::hl(LT), pxw = G::wl(LT);
+        const bool pxon = px && t < pxh * pxw && (y0 >> LT) + t / pxw < (Hp >> LT) &&
+                          (x0 >> LT) + t % pxw < (Wp >> LT);
+        const float pxv = pxon ? lds[G::uidx(LT, 0, 0, t / pxw, t % pxw)] : 0.f;
         __syncthreads();
         wave_prio<PrioTileBwd1::commit_dy>();
         fd.template commit<true, false>(lds, t);
@@ -2519,8 +2525,6 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(
             analysis_level<G, decltype(lc)::value, false>(lds, t);
             __syncthreads();
         });
-        DeepRegs<G> dr;
-        if (deep) fetch_deep<G>(dr, deep, b, C, c, y0, x0, Hp, Wp, t);
         float acc[Q][R];
         if (job.on) {
             // the window's centre past the job's part of the core is halo
@@ -2558,6 +2562,11 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(
             __syncthreads();
         });
         drain_vmem();  // (the next dy is loaded after the store, by design)
+        if (pxon) {
+            const int hd = Hp >> LT, wd = Wp >> LT;
+            const int gy = (y0 >> LT) + t / pxw, gx = (x0 >> LT) + t % pxw;
+            px[(size_t(b) * C + c) * hd * wd + size_t(gy) * wd + gx] = pxv;
+        }
         final_store<G, T>(lds, dx, b, B, C, c, t, y0, x0, Hp, Wp);
         asm volatile("" : "+v"(t));
         fd.issue_tile_buf(dy, more ? nx.b : B, B, C, c, t, nx.ty * TH, nx.tx * TW, Hp, Wp);
