@@ -1232,6 +1232,10 @@ __device__ __forceinline__ void final_store_rag(const float* lds, T* __restrict_
 }
 
 // Folded filters into LDS: [0, KK) base, then (l, s) blocks, then the bias.
+// Each lane reads its two values (a tap and its scale, or the bias and
+// beta) unconditionally, from addresses chosen per lane, and computes after
+// both are issued: with beta read as a branch-guarded scalar and the taps
+// read in the lanes' branches, a fold waited on two memory round trips.
 template <class G, typename T, bool FLIP>
 __device__ __forceinline__ void fold_weights(float* wf, const T* __restrict__ wb,
                                              const T* __restrict__ bb, const T* __restrict__ sb,
@@ -1239,21 +1243,23 @@ __device__ __forceinline__ void fold_weights(float* wf, const T* __restrict__ wb
                                              int C, int c, int tid) {
     constexpr int KK = G::KK;
     for (int i = tid; i < G::NWF; i += G::NT) {
-        float v;
+        const bool base = i < KK, wav = !base && i < G::NWF - 1;
+        const int jj = wav ? i - KK : 0, ls = jj / KK, t = jj - ls * KK;
+        const int l = ls >> 2, s = ls & 3;
+        const size_t gi = (size_t(l) * C + c) * 4 + s;
+        const int tb = FLIP ? KK - 1 - i : i, tw = FLIP ? KK - 1 - t : t;
         // sb == NULL: no base scale (the plain depthwise conv)
-        const float beta = sb ? to_f(sb[c]) : 1.f;
-        if (i < KK) {
-            const int t = FLIP ? KK - 1 - i : i;
-            v = beta * to_f(wb[size_t(c) * KK + t]);
-        } else if (i < G::NWF - 1) {
-            const int jj = i - KK, ls = jj / KK, t = jj % KK;
-            const int l = ls >> 2, s = ls & 3;
-            const int tt = FLIP ? KK - 1 - t : t;
-            const size_t gi = (size_t(l) * C + c) * 4 + s;
-            v = to_f(sw[gi]) * ldexpf(1.f, -2 * (l + 1)) * to_f(ww[gi * KK + tt]);
-        } else {
-            v = FLIP ? 0.f : beta * to_f(bb[c]);
-        }
+        const T* a0 = base ? wb + size_t(c) * KK + tb : wav ? ww + gi * KK + tw : bb + c;
+        const T* a1 = wav ? sw + gi : sb ? sb + c : a0;
+        const float r0 = to_f(*a0), r1 = to_f(*a1);
+        const float beta = sb ? r1 : 1.f;
+        float v;
+        if (base)
+            v = beta * r0;
+        else if (wav)
+            v = r1 * ldexpf(1.f, -2 * (l + 1)) * r0;
+        else
+            v = FLIP ? 0.f : beta * r0;
         wf[i] = v;
     }
 }
