@@ -1232,7 +1232,9 @@ __device__ __forceinline__ void final_store_rag(const float* lds, T* __restrict_
 }
 
 // Folded filters into LDS: [0, KK) base, then (l, s) blocks, then the bias.
-// Each lane reads its two values (a tap and its scale, or the bias and
+// bb is read in either form (its value unused when FLIP), so it must point
+// at C readable elements then too: the callers pass wb.  Each lane reads
+// its two values (a tap and its scale, or the bias and
 // beta) unconditionally, from addresses chosen per lane, and computes after
 // both are issued: with beta read as a branch-guarded scalar and the taps
 // read in the lanes' branches, a fold waited on two memory round trips.

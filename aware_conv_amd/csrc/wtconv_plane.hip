@@ -99,7 +99,7 @@ hipError_t plane_apply(const wtconv_shape& s, const void* in, const Params& p, v
         const long per = (total + nwg - 1) / nwg;
         nwg = (total + per - 1) / per;
     }
-    const void* bb = flip ? p.w_base : p.b_base;  // unread when flipped
+    const void* bb = flip ? p.w_base : p.b_base;  // read but unused when flipped
     const void* wb = p.w_base;
     const void* sb = p.s_base;
     const void* ww = p.w_wav;

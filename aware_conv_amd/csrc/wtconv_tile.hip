@@ -855,7 +855,7 @@ hipError_t launch_tiles(const wtconv_shape& s, const TileVariant* v, const void*
     const long total = long(s.C) * units;
     long nwg = resident(fn, v->NT, v->lds_apply);
     if (nwg > total) nwg = total;
-    const void* bb = flip ? p.w_base : p.b_base;  // unread when flipped
+    const void* bb = flip ? p.w_base : p.b_base;  // read but unused when flipped
     const void* wb = p.w_base;
     const void* sb = p.s_base;
     const void* ww = p.w_wav;
