@@ -1140,15 +1140,16 @@ __device__ __forceinline__ void synth_rows(const float* lds, int pl, int i, int 
 // of range).  Whole planes (HT == 0): the group's planes.  Tiles: the core of
 // the tile at (y0, x0) of plane b of an Hp x Wp tensor; rows and columns
 // past the plane, and b >= B, store out of range.
-template <class G, typename T>
+template <class G, typename T, bool WIDE = false>
 __device__ __forceinline__ void final_store(const float* lds, T* __restrict__ out, int b0, int B,
                                             int C, int c, int tid, int y0 = 0, int x0 = 0,
                                             int Hp = G::H, int Wp = G::W) {
     constexpr int V = vec_elems<T>(G::W);
     constexpr int NV = G::W / V, RP = G::H / 2, ITEMS = G::P * RP * NV;
     // columns per pass: at most 4 floats, so that an 8-wide fp16 item keeps
-    // few values live (two 8-byte stores per row instead of one 16-byte)
-    constexpr int CW = V < 4 ? V : 4, NCH = V / CW;
+    // few values live (two 8-byte stores per row instead of one 16-byte);
+    // WIDE: the whole item per pass, for kernels with registers to spare
+    constexpr int CW = V < 4 || WIDE ? V : 4, NCH = V / CW;
     constexpr int BYTES = CW * int(sizeof(T));
     using raw_t = typename RawVec<BYTES>::type;
     rsrc_t rs;
@@ -1190,11 +1191,12 @@ __device__ __forceinline__ void final_store(const float* lds, T* __restrict__ ou
             store_vec<T, CW>(u0.e, r0);
             store_vec<T, CW>(u1.e, r1);
             const int o = off + (in ? ch * BYTES : 0);
-            // fp32 rows go out non-temporal: the layer's output is not
-            // read again by it, and streaming it past the caches took the
-            // stage-1 forward 43.1 -> 41.6 us, 14² 18.6 -> 17.6 us; fp16's
-            // 8-byte pieces were slower so (82.0 -> 82.5 us)
-            constexpr int kAux = sizeof(T) == 4 ? 2 : 0;
+            // fp32 rows and whole 16-byte fp16 pieces go out non-temporal:
+            // the layer's output is not read again by it, and streaming it
+            // past the caches took the stage-1 forward 43.1 -> 41.6 us, 14²
+            // 18.6 -> 17.6 us, the fp16 forward (whole items) 82.4 -> 80.5
+            // us; fp16's 8-byte pieces were slower so (82.0 -> 82.5 us)
+            constexpr int kAux = sizeof(T) == 4 || BYTES == 16 ? 2 : 0;
             buf_store<kAux>(u0.raw, rs, o);
             buf_store<kAux>(u1.raw, rs, o + (in ? row_elems * int(sizeof(T)) : 0));
         }
@@ -1465,7 +1467,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(
         if constexpr (RAG)
             final_store_rag<G, T>(lds, out, b0, B, C, c, tid, rg);
         else
-            final_store<G, T>(lds, out, b0, B, C, c, tid);
+            final_store<G, T, std::is_same<T, __half>::value>(lds, out, b0, B, C, c, tid);
         __syncthreads();
     }
 }
