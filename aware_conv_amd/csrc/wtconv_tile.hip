@@ -472,6 +472,68 @@ __global__ __launch_bounds__(256) void k_gdeep_conv(const float* __restrict__ U,
     }
 }
 
+// The same conv with the (plane, subband) staged in LDS first: a bordered
+// array (zero borders of p, rows padded to whole kDeepRS segments, odd
+// pitch), then kDeepRS outputs of a row per item from a register window, as
+// in k_deep_apply.  The taps and their order are k_gdeep_conv's (taps past
+// the level read the border's zeros instead of being skipped).  Device
+// memory is read once per element, coalesced, instead of once per tap with
+// a bounds test.  LDS: K^2 filters + (h + 2p) * pitch floats, for levels
+// where that fits 64 KB (gdeep_conv_lds_bytes).
+template <typename T, int K, bool FLIP>
+__global__ __launch_bounds__(256) void k_gdeep_conv_lds(const float* __restrict__ U,
+                                                        float* __restrict__ out,
+                                                        const T* __restrict__ ww,
+                                                        const T* __restrict__ sw, int C, int h,
+                                                        int w, int la) {
+    constexpr int KK = K * K, p = K / 2, RS = kDeepRS;
+    extern __shared__ float lds[];
+    const int ps = blockIdx.x, s = ps % 4, c = (ps / 4) % C;
+    const int tid = threadIdx.x, nt = blockDim.x;
+    const int nseg = (w + RS - 1) / RS, bp = (nseg * RS + 2 * p) | 1, rows = h + 2 * p;
+    float* wk = lds;
+    float* a = lds + KK;
+    if (tid < KK) {
+        const int tt = FLIP ? KK - 1 - tid : tid;
+        const size_t gi = (size_t(la - 1) * C + c) * 4 + s;
+        wk[tid] = to_f(sw[gi]) * ldexpf(1.f, -2 * la) * to_f(ww[gi * KK + tt]);
+    }
+    const float* u = U + size_t(ps) * h * w;
+    const DivMod by_bp(bp);
+    for (int e = tid; e < rows * bp; e += nt) {
+        const int2 rj = by_bp(e);
+        const int y = rj.x - p, x = rj.y - p;
+        a[e] = y >= 0 && y < h && x >= 0 && x < w ? u[y * w + x] : 0.f;
+    }
+    __syncthreads();
+    float* o = out + size_t(ps) * h * w;
+    const DivMod by_seg(nseg);
+    for (int e = tid; e < h * nseg; e += nt) {
+        const int2 is = by_seg(e);
+        const int i = is.x, j0 = is.y * RS;
+        float acc[RS];
+#pragma unroll
+        for (int r = 0; r < RS; ++r) acc[r] = 0.f;
+#pragma unroll
+        for (int uu = 0; uu < K; ++uu) {
+            // row i + uu - p of the level from column j0 - p, bordered
+            const float* src = a + (i + uu) * bp + j0;
+            float row[RS + K - 1];
+#pragma unroll
+            for (int t = 0; t < RS + K - 1; ++t) row[t] = src[t];
+#pragma unroll
+            for (int vv = 0; vv < K; ++vv) {
+                const float wv = wk[uu * K + vv];
+#pragma unroll
+                for (int r = 0; r < RS; ++r) acc[r] = fmaf(wv, row[r + vv], acc[r]);
+            }
+        }
+#pragma unroll
+        for (int r = 0; r < RS; ++r)
+            if (j0 + r < w) o[i * w + j0 + r] = acc[r];
+    }
+}
+
 // The conv outputs of one level synthesised one level down, with the signs
 // of k_deep_apply: added to the next finer LL (`accumulate`), or written as
 // the level-LT contribution D.
@@ -736,14 +798,27 @@ const void* gdeep_conv_fn_k(bool flip) {
     return flip ? reinterpret_cast<const void*>(&k_gdeep_conv<T, K, true>)
                 : reinterpret_cast<const void*>(&k_gdeep_conv<T, K, false>);
 }
+template <typename T, int K>
+const void* gdeep_conv_lds_fn_k(bool flip) {
+    return flip ? reinterpret_cast<const void*>(&k_gdeep_conv_lds<T, K, true>)
+                : reinterpret_cast<const void*>(&k_gdeep_conv_lds<T, K, false>);
+}
+// The staged form where its LDS fits (lds > 0), else the direct one.
 template <typename T>
-const void* gdeep_conv_fn(bool flip, int k) {
+const void* gdeep_conv_fn(bool flip, int k, size_t lds) {
     switch (k) {
-        case 1: return gdeep_conv_fn_k<T, 1>(flip);
-        case 3: return gdeep_conv_fn_k<T, 3>(flip);
-        case 5: return gdeep_conv_fn_k<T, 5>(flip);
-        default: return gdeep_conv_fn_k<T, 7>(flip);
+        case 1: return lds ? gdeep_conv_lds_fn_k<T, 1>(flip) : gdeep_conv_fn_k<T, 1>(flip);
+        case 3: return lds ? gdeep_conv_lds_fn_k<T, 3>(flip) : gdeep_conv_fn_k<T, 3>(flip);
+        case 5: return lds ? gdeep_conv_lds_fn_k<T, 5>(flip) : gdeep_conv_fn_k<T, 5>(flip);
+        default: return lds ? gdeep_conv_lds_fn_k<T, 7>(flip) : gdeep_conv_fn_k<T, 7>(flip);
     }
+}
+// Bytes of k_gdeep_conv_lds for an h x w level, or 0 past 64 KB.
+size_t gdeep_conv_lds_bytes(int k, int h, int w) {
+    const int p = k / 2, nseg = (w + kDeepRS - 1) / kDeepRS;
+    const size_t bp = size_t((nseg * kDeepRS + 2 * p) | 1);
+    const size_t b = sizeof(float) * (size_t(k) * k + (size_t(h) + 2 * p) * bp);
+    return b <= 65536 ? b : 0;
 }
 const void* gdeep_corr_fn(int k) {
     switch (k) {
@@ -760,8 +835,6 @@ hipError_t gdeep_apply(const wtconv_shape& s, const float* A, const Params& p, b
                        float* Cb, float* deep, hipStream_t stream) {
     const DeepGlobal G = deep_global(s);
     const int LT = tile_lt(s);
-    const void* fn = s.dtype == WTCONV_F32 ? gdeep_conv_fn<float>(flip, s.k)
-                                           : gdeep_conv_fn<__half>(flip, s.k);
     int C = s.C;
     const void* ww = p.w_wav;
     const void* sw = p.s_wav;
@@ -769,9 +842,12 @@ hipError_t gdeep_apply(const wtconv_shape& s, const float* A, const Params& p, b
         const float* u = A + G.level_off(m);
         float* o = Cb + G.level_off(m);
         int h = G.h(m), w = G.w(m), la = LT + m;
+        const size_t lds = gdeep_conv_lds_bytes(s.k, h, w);
+        const void* fn = s.dtype == WTCONV_F32 ? gdeep_conv_fn<float>(flip, s.k, lds)
+                                               : gdeep_conv_fn<__half>(flip, s.k, lds);
         void* args[] = {&u, &o, &ww, &sw, &C, &h, &w, &la};
-        hipError_t e = hipLaunchKernel(fn, dim3(unsigned(G.planes) * 4u), dim3(256), args, 0,
-                                       stream);
+        hipError_t e = hipLaunchKernel(fn, dim3(unsigned(G.planes) * 4u), dim3(256), args,
+                                       unsigned(lds), stream);
         if (e != hipSuccess) return e;
     }
     for (int m = G.LD; m >= 1; --m) {
