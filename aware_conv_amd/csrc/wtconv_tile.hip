@@ -621,6 +621,79 @@ __global__ __launch_bounds__(256) void k_gdeep_corr(const float* __restrict__ ux
         for (int o = tid; o < first; o += NT) row[o] = 0.f;
 }
 
+// The same taps with the (plane, level, subband) staged in LDS: U bordered
+// (zero borders of p, rows padded to whole kDeepRS segments, odd pitch), V
+// padded with zeros to whole segments.  A work item is one tap row over a
+// chunk of the rows (K accumulators, kDeepRS columns per step from register
+// windows, as in k_deep_bww); the chunks are summed in order.  Gathered
+// from device memory with a bounds test per element, and summed over the
+// 256 lanes one by one, the taps had cost ~250 us per 1024² step.  LDS:
+// gdeep_corr_lds_bytes, sized for level 1, the largest.
+template <int K>
+__global__ __launch_bounds__(256) void k_gdeep_corr_lds(const float* __restrict__ ux,
+                                                        const float* __restrict__ vdy,
+                                                        DeepGlobal G, float* __restrict__ part,
+                                                        int C, int LT, int row0, int npart) {
+    constexpr int KK = K * K, p = K / 2, RS = kDeepRS, NCH = 256 / K;
+    extern __shared__ float lds[];
+    const int tid = threadIdx.x, nt = blockDim.x;
+    const int ms = blockIdx.x % (G.LD * 4), pl = blockIdx.x / (G.LD * 4);
+    const int m = ms / 4 + 1, s = ms % 4, h = G.h(m), w = G.w(m);
+    const size_t off = G.level_off(m) + (size_t(pl) * 4 + s) * h * w;
+    const int nseg = (w + RS - 1) / RS, bpu = (nseg * RS + 2 * p) | 1, bpv = (nseg * RS) | 1;
+    const int nu = (h + 2 * p) * bpu, nv = h * bpv;
+    float* a = lds;       // U, bordered
+    float* v = a + nu;    // V, padded
+    float* red = v + nv;  // [item][K]
+    const DivMod by_bpu(bpu), by_bpv(bpv);
+    for (int e = tid; e < nu; e += nt) {
+        const int2 rj = by_bpu(e);
+        const int y = rj.x - p, x = rj.y - p;
+        a[e] = y >= 0 && y < h && x >= 0 && x < w ? ux[off + size_t(y) * w + x] : 0.f;
+    }
+    for (int e = tid; e < nv; e += nt) {
+        const int2 rj = by_bpv(e);
+        v[e] = rj.y < w ? vdy[off + size_t(rj.x) * w + rj.y] : 0.f;
+    }
+    __syncthreads();
+    if (tid < K * NCH) {
+        const int uu = tid / NCH, ch = tid % NCH;
+        const int i0 = ch * h / NCH, i1 = (ch + 1) * h / NCH;
+        float acc[K];
+#pragma unroll
+        for (int vv = 0; vv < K; ++vv) acc[vv] = 0.f;
+        for (int i = i0; i < i1; ++i)
+            for (int j0 = 0; j0 < nseg * RS; j0 += RS) {
+                const float* vr = v + i * bpv + j0;
+                // row i + uu - p of U from column j0 - p, bordered
+                const float* xr = a + (i + uu) * bpu + j0;
+                float dv[RS], xw[RS + K - 1];
+#pragma unroll
+                for (int r = 0; r < RS; ++r) dv[r] = vr[r];
+#pragma unroll
+                for (int r = 0; r < RS + K - 1; ++r) xw[r] = xr[r];
+#pragma unroll
+                for (int r = 0; r < RS; ++r)
+#pragma unroll
+                    for (int vv = 0; vv < K; ++vv) acc[vv] = fmaf(dv[r], xw[r + vv], acc[vv]);
+            }
+#pragma unroll
+        for (int vv = 0; vv < K; ++vv) red[tid * K + vv] = acc[vv];
+    }
+    __syncthreads();
+    const int b = pl / C, c = pl % C;
+    float* row = part + (size_t(row0 + b) * C + c) * npart;
+    const int first = KK + 1 + LT * 4 * KK;
+    for (int t = tid; t < KK; t += nt) {
+        const int uu = t / K, vv = t % K;
+        float sum = 0.f;
+        for (int ch = 0; ch < NCH; ++ch) sum += red[(uu * NCH + ch) * K + vv];
+        row[first + ms * KK + t] = sum;
+    }
+    if (ms == 0)
+        for (int o = tid; o < first; o += nt) row[o] = 0.f;
+}
+
 }  // namespace dev
 
 namespace {
@@ -820,13 +893,27 @@ size_t gdeep_conv_lds_bytes(int k, int h, int w) {
     const size_t b = sizeof(float) * (size_t(k) * k + (size_t(h) + 2 * p) * bp);
     return b <= 65536 ? b : 0;
 }
-const void* gdeep_corr_fn(int k) {
+// The staged form where its LDS fits (lds > 0), else the direct one.
+const void* gdeep_corr_fn(int k, size_t lds) {
     switch (k) {
-        case 1: return reinterpret_cast<const void*>(&k_gdeep_corr<1>);
-        case 3: return reinterpret_cast<const void*>(&k_gdeep_corr<3>);
-        case 5: return reinterpret_cast<const void*>(&k_gdeep_corr<5>);
-        default: return reinterpret_cast<const void*>(&k_gdeep_corr<7>);
+        case 1: return lds ? reinterpret_cast<const void*>(&k_gdeep_corr_lds<1>)
+                           : reinterpret_cast<const void*>(&k_gdeep_corr<1>);
+        case 3: return lds ? reinterpret_cast<const void*>(&k_gdeep_corr_lds<3>)
+                           : reinterpret_cast<const void*>(&k_gdeep_corr<3>);
+        case 5: return lds ? reinterpret_cast<const void*>(&k_gdeep_corr_lds<5>)
+                           : reinterpret_cast<const void*>(&k_gdeep_corr<5>);
+        default: return lds ? reinterpret_cast<const void*>(&k_gdeep_corr_lds<7>)
+                            : reinterpret_cast<const void*>(&k_gdeep_corr<7>);
     }
+}
+// Bytes of k_gdeep_corr_lds for levels of at most h x w (level 1), or 0
+// past 64 KB.
+size_t gdeep_corr_lds_bytes(int k, int h, int w) {
+    const int p = k / 2, nseg = (w + kDeepRS - 1) / kDeepRS;
+    const size_t bpu = size_t((nseg * kDeepRS + 2 * p) | 1), bpv = size_t((nseg * kDeepRS) | 1);
+    const size_t items = size_t(256 / k) * k;
+    const size_t b = sizeof(float) * ((size_t(h) + 2 * p) * bpu + size_t(h) * bpv + items * k);
+    return b <= 65536 ? b : 0;
 }
 
 // D from the levels A of the box sums: the convs of every level into Cb,
@@ -868,9 +955,10 @@ hipError_t gdeep_rows(const wtconv_shape& s, const float* Ax, const float* Ady, 
     DeepGlobal G = deep_global(s);
     int C = s.C, LT = tile_lt(s), npart = s.k * s.k * (1 + 4 * s.L) + 1;
     void* args[] = {&Ax, &Ady, &G, &part, &C, &LT, &row0, &npart};
-    const hipError_t e = hipLaunchKernel(gdeep_corr_fn(s.k),
+    const size_t lds = gdeep_corr_lds_bytes(s.k, G.h(1), G.w(1));
+    const hipError_t e = hipLaunchKernel(gdeep_corr_fn(s.k, lds),
                                          dim3(unsigned(G.planes) * unsigned(G.LD) * 4u),
-                                         dim3(256), args, 0, stream);
+                                         dim3(256), args, unsigned(lds), stream);
     if (e != hipSuccess) return e;
     return hipGetLastError();
 }
