@@ -55,6 +55,9 @@ DEEP_DEVICE = [  # deep levels through device memory
     (1, 2, 5, 4, 1024, 1024, "f32"),
     (1, 2, 7, 6, 768, 768, "f16"),
     (1, 2, 3, 5, 1024, 1024, "f16"),
+    # level 1 (128²) past both staged device-memory kernels' LDS: their
+    # direct forms
+    (1, 1, 5, 4, 2048, 2048, "f32"),
 ]
 
 
